@@ -330,13 +330,32 @@ def test_check_matmul_accepts_exact_and_rejects_perturbed():
     exact_bits = codecs.f32_to_bf16_bits(Y.astype(np.float32))
     assert ref.check_matmul(exact_bits, "bf16", Y, S)["ok"]
     tol = ref.matmul_tolerance(Y, S)
-    bad = Y.copy()
-    bad[1, 7] += 3 * tol[1, 7]
-    r = ref.check_matmul(codecs.f32_to_bf16_bits(bad.astype(np.float32)), "bf16", Y, S)
-    assert not r["ok"] and r["n_bad"] == 1
+    bad = exact_bits.copy()
+    # one BF16 step beyond the rounding of Y_ref + tol
+    hi_bits = codecs.f32_to_bf16_bits(np.float32(Y[1, 7] + tol[1, 7]))
+    bad[1, 7] = hi_bits + 1 if Y[1, 7] + tol[1, 7] > 0 else hi_bits - 1
+    r = ref.check_matmul(bad, "bf16", Y, S)
+    assert not r["ok"] and r["n_bad"] == 1 and r["first_bad"]["index"] == (1, 7)
     nan_bits = exact_bits.copy()
     nan_bits[0, 0] = 0x7FC0
     assert not ref.check_matmul(nan_bits, "bf16", Y, S)["ok"]
+
+
+def test_check_matmul_takes_output_rounding_outside_the_bound():
+    """Y_ref = 1 + 2^-8 + 2^-12 with S = |Y_ref|: tol = 3e-3 * Y_ref is less
+    than the BF16 rounding error of Y_ref itself (about 2^-8), yet
+    RNE_bf16(Y_ref) must pass; the next BF16 value above must fail, and so
+    must the next one below RNE_bf16(Y_ref - tol)."""
+    y = 1 + 2.0 ** -8 + 2.0 ** -12
+    Y = np.array([[y]])
+    S = np.array([[y]])
+    rounded = codecs.f32_to_bf16_bits(np.float32(y))            # 0x3F81 (1.0078125)
+    assert rounded[()] == 0x3F81
+    assert abs(1.0078125 - y) > ref.matmul_tolerance(Y, S)[0, 0]
+    assert ref.check_matmul(np.array([[0x3F81]], np.uint16), "bf16", Y, S)["ok"]
+    assert not ref.check_matmul(np.array([[0x3F82]], np.uint16), "bf16", Y, S)["ok"]
+    assert ref.check_matmul(np.array([[0x3F80]], np.uint16), "bf16", Y, S)["ok"]   # 1.0 = RNE(y - tol)
+    assert not ref.check_matmul(np.array([[0x3F7F]], np.uint16), "bf16", Y, S)["ok"]
 
 
 def test_tolerance_constants():
