@@ -1,0 +1,397 @@
+#!/usr/bin/env python3
+"""Benchmark of the weight-only FP4 / FP8 matmul library on one MI355X.
+
+Headline (one JSON line on stdout): the FP4 decode GEMV, M in {1, 2, 4, 8},
+N = K = 5120, block 16, BF16 activations N(0,1), bias.  One step = the four
+GEMV calls (one per M), each on its own copy of the weights; 73 copies
+(about 1 GiB) rotate so every call streams its weights from HBM rather than
+from the 256 MB last-level cache.  Each step is a captured HIP graph, so host
+launch overhead does not sit between the kernels.
+
+    value    = packed weight + scale bytes per step / step time  [GB/s]
+    roofline = the GEMV kernel: algorithmic bytes (weights, scales,
+               activations, bias, output) per launch / mean launch time,
+               against the 8 TB/s HBM3E peak
+    cpu_baseline = the CPU oracle on the same workload (GB/s of weights)
+
+"extra" reports the other workloads (small FP16 GEMV, FP4 prefill GEMM with
+the dequant + hipBLASLt baseline beside it, FP8 GEMV and prefill, wide-output
+GEMV, the dequant kernel) and a measured HBM copy bandwidth.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       [--no-extra] [--profile-kernel fp4_gemv|copy]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import fp8_weight_only_fp4w_amd as fw  # noqa: E402
+import workloads  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense BF16 / FP16 MFMA
+ROTATE_BYTES = 1 << 30          # rotate weight copies past the 256 MB MALL
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fp4_gemv_decode_traffic.json")
+GEMV_SOURCES = ["fp8_weight_only_fp4w_amd/csrc/gemv.hip", "fp8_weight_only_fp4w_amd/csrc/device.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------------ inputs on device
+
+def dev_bits(bits, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda")
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16)
+
+
+def dev_u8(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+
+
+def fp4_on_device(p, copies=1):
+    """Activations, bias, ws2 once; `copies` distinct device copies of B and scales."""
+    B = dev_u8(p.B)
+    ws = dev_u8(p.weight_scale)
+    Bs = [B] + [B.clone() for _ in range(copies - 1)]
+    wss = [ws] + [ws.clone() for _ in range(copies - 1)]
+    return dict(A=dev_bits(p.A, p.dtype), B=Bs, ws=wss,
+                ws2=torch.tensor([p.weight_scale_2], dtype=torch.float32, device="cuda"),
+                bias=None if p.bias is None else dev_bits(p.bias, p.dtype))
+
+
+def fp8_on_device(p, copies=1):
+    B = dev_u8(p.B)
+    bs = torch.from_numpy(p.b_scale).to("cuda")
+    return dict(A=dev_bits(p.A, p.dtype), B=[B] + [B.clone() for _ in range(copies - 1)],
+                bs=[bs] + [bs.clone() for _ in range(copies - 1)],
+                bias=None if p.bias is None else dev_bits(p.bias, p.dtype))
+
+
+def copies_for(weight_bytes):
+    return max(1, -(-ROTATE_BYTES // weight_bytes))
+
+
+# ------------------------------------------------------------------ timing helpers
+
+def capture(fn):
+    """Capture fn() (enqueue-only work on the current stream) into a graph."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # warm the allocator / library outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graphs(graphs, steps, warmup):
+    """Replay graphs round-robin: warmup untimed, then exactly `steps` timed
+    replays bracketed by synchronisation; returns (wall s, event s)."""
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, start.elapsed_time(stop) / 1e3
+
+
+def time_calls(fn_list, steps, warmup):
+    """Direct launches (for long kernels where launch overhead is hidden)."""
+    for i in range(warmup):
+        fn_list[i % len(fn_list)]()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn_list[i % len(fn_list)]()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / 1e3
+
+
+# ------------------------------------------------------------------ headline
+
+def gemv_decode(steps, warmup):
+    w = workloads.WORKLOADS["fp4_gemv_decode"]
+    Ms = w.Ms
+    probs = {M: w.make(M=M) for M in Ms}
+    p0 = probs[Ms[0]]
+    weight_bytes = p0.B.nbytes + p0.weight_scale.nbytes
+    R = copies_for(weight_bytes)
+    d = fp4_on_device(p0, copies=R)
+    A = {M: dev_bits(probs[M].A, "bf16") for M in Ms}
+    out = {M: torch.empty(M, w.N, dtype=torch.bfloat16, device="cuda") for M in Ms}
+
+    def step(r):
+        for M in Ms:
+            fw.fp4w_matmul(A[M], d["B"][r], d["ws"][r], d["ws2"], d["bias"], 16, out=out[M])
+
+    graphs = [capture(lambda r=r: step(r)) for r in range(R)]
+    wall, ev = time_graphs(graphs, steps, warmup)
+    per_step = ev / steps
+    # algorithmic bytes of one step (four launches)
+    alg = 0
+    for M in Ms:
+        alg += weight_bytes + M * w.K * 2 + w.N * 2 + M * w.N * 2 + 4
+    # per-M breakdown (graphs of one launch each, same rotation)
+    per_m = {}
+    for M in Ms:
+        gs = [capture(lambda r=r, M=M: fw.fp4w_matmul(A[M], d["B"][r], d["ws"][r], d["ws2"], d["bias"], 16,
+                                                       out=out[M])) for r in range(R)]
+        _, e = time_graphs(gs, max(steps, 100), warmup)
+        t = e / max(steps, 100)
+        per_m[str(M)] = {"us": round(t * 1e6, 3), "weight_GBps": round(weight_bytes / t / 1e9, 1)}
+        del gs
+    del graphs
+    return dict(workload=w, Ms=Ms, weight_bytes=weight_bytes, R=R, per_step=per_step, wall=wall,
+                alg_bytes_step=alg, per_m=per_m)
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(min_seconds=10.0):
+    """The CPU oracle, as it stands, on the headline workload: all four M of
+    one step (full N), repeated until at least `min_seconds` have passed."""
+    from oracle import reference as ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = None
+    w = workloads.WORKLOADS["fp4_gemv_decode"]
+    probs = [w.make(M=M) for M in w.Ms]
+    wb = probs[0].B.nbytes + probs[0].weight_scale.nbytes
+    done, t0 = 0, time.perf_counter()
+    while True:
+        for p in probs:
+            ref.matmul_fp4_reference(p.A, p.dtype, p.B, p.weight_scale, 16, p.weight_scale_2, p.bias)
+            done += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return {"value": round(done * wb / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} oracle calls (M in {list(w.Ms)}, N=K=5120, full output) in {el:.1f} s; "
+                      f"float64 dequant + numpy BLAS dgemm; cores = BLAS threads; host has "
+                      f"{os.cpu_count()} logical CPUs, affinity {len(os.sched_getaffinity(0))}"}
+
+
+# ------------------------------------------------------------------ extra workloads
+
+def hbm_copy_gbps():
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    t = time_calls([lambda: dst.copy_(src)], 20, 3)
+    return round(2 * n * 20 / t / 1e9, 1)
+
+
+def extra_small_gemv(steps, warmup):
+    w = workloads.WORKLOADS["fp4_gemv_small"]
+    p = w.make()
+    d = fp4_on_device(p)
+    out = torch.empty(1, w.N, dtype=torch.float16, device="cuda")
+    g = capture(lambda: fw.fp4w_matmul(d["A"], d["B"][0], d["ws"][0], d["ws2"], None, 16, out=out))
+    _, e = time_graphs([g], steps, warmup)
+    return {"us_per_call": round(e / steps * 1e6, 3), "note": "75 KB working set, L2-resident"}
+
+
+def extra_prefill_fp4(reps=10, warmup=3):
+    w = workloads.WORKLOADS["fp4_prefill"]
+    p = w.make()
+    d = fp4_on_device(p)
+    flops = 2.0 * p.M * p.N * p.K
+    out = torch.empty(p.M, p.N, dtype=torch.bfloat16, device="cuda")
+    t = time_calls([lambda: fw.fp4w_matmul(d["A"], d["B"][0], d["ws"][0], d["ws2"], None, 16, out=out)],
+                   reps, warmup) / reps
+    res = {"fused_ms": round(t * 1e3, 3), "fused_TFLOPs": round(flops / t / 1e12, 1),
+           "fused_frac_of_bf16_peak": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    # baseline: dequant to a [N, K] scratch, then hipBLASLt (torch.matmul)
+    scratch = torch.empty(p.N, p.K, dtype=torch.bfloat16, device="cuda")
+
+    def base():
+        fw.fp4w_dequant(d["B"][0], d["ws"][0], d["ws2"], 16, out=scratch)
+        torch.matmul(d["A"], scratch.t(), out=out)
+
+    tb = time_calls([base], reps, warmup) / reps
+    td = time_calls([lambda: fw.fp4w_dequant(d["B"][0], d["ws"][0], d["ws2"], 16, out=scratch)],
+                    reps * 5, warmup) / (reps * 5)
+    dq_bytes = p.B.nbytes + p.weight_scale.nbytes + scratch.numel() * 2
+    res.update({"baseline_dequant_plus_hipblaslt_ms": round(tb * 1e3, 3),
+                "baseline_TFLOPs": round(flops / tb / 1e12, 1),
+                "dequant_ms": round(td * 1e3, 4), "dequant_GBps": round(dq_bytes / td / 1e9, 1)})
+    del scratch
+    return res
+
+
+def extra_fp8(steps, warmup, reps=10):
+    w = workloads.WORKLOADS["fp8_gemv"]
+    p = w.make(M=4)
+    wb = p.B.nbytes + p.b_scale.nbytes
+    R = copies_for(wb)
+    d = fp8_on_device(p, copies=R)
+    out = torch.empty(4, p.N, dtype=torch.bfloat16, device="cuda")
+    gs = [capture(lambda r=r: fw.fp8w_matmul(d["A"], d["B"][r], d["bs"][r], None, 128, out=out)) for r in range(R)]
+    _, e = time_graphs(gs, steps, warmup)
+    t = e / steps
+    res = {"gemv_M4_us": round(t * 1e6, 2), "gemv_M4_weight_GBps": round(wb / t / 1e9, 1)}
+    del gs, d
+    p8 = w.make(M=8192)
+    d = fp8_on_device(p8)
+    out = torch.empty(8192, p8.N, dtype=torch.bfloat16, device="cuda")
+    flops = 2.0 * p8.M * p8.N * p8.K
+    tp = time_calls([lambda: fw.fp8w_matmul(d["A"], d["B"][0], d["bs"][0], None, 128, out=out)], reps, 3) / reps
+    res.update({"prefill_ms": round(tp * 1e3, 3), "prefill_TFLOPs": round(flops / tp / 1e12, 1)})
+    return res
+
+
+def extra_wide(steps, warmup):
+    w = workloads.WORKLOADS["fp4_gemv_wide"]
+    p = w.make()
+    wb = p.B.nbytes + p.weight_scale.nbytes
+    R = copies_for(wb)
+    d = fp4_on_device(p, copies=R)
+    out = torch.empty(4, p.N, dtype=torch.bfloat16, device="cuda")
+    gs = [capture(lambda r=r: fw.fp4w_matmul(d["A"], d["B"][r], d["ws"][r], d["ws2"], None, 16, out=out))
+          for r in range(R)]
+    _, e = time_graphs(gs, steps, warmup)
+    t = e / steps
+    return {"us": round(t * 1e6, 2), "weight_GBps": round(wb / t / 1e9, 1), "copies": R}
+
+
+# ------------------------------------------------------------------ profiling mode
+
+def profile_kernel(which, launches=50):
+    """Launch one kernel `launches` times without graphs, for rocprofv3 runs
+    (kernel trace or PMC counters)."""
+    if which == "copy":
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(launches):
+            dst.copy_(src)
+    else:
+        w = workloads.WORKLOADS["fp4_gemv_decode"]
+        p = w.make(M=8)
+        R = copies_for(p.B.nbytes + p.weight_scale.nbytes)
+        d = fp4_on_device(p, copies=R)
+        out = torch.empty(8, w.N, dtype=torch.bfloat16, device="cuda")
+        for i in range(launches):
+            fw.fp4w_matmul(d["A"], d["B"][i % R], d["ws"][i % R], d["ws2"], d["bias"], 16, out=out)
+    torch.cuda.synchronize()
+    log(f"profiled {launches} launches of {which}")
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--profile-kernel", choices=["fp4_gemv", "copy"])
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library runs on a single MI355X and has no "
+              "multi-GPU path (--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    fw.load_library()
+    if args.profile_kernel:
+        profile_kernel(args.profile_kernel)
+        return
+
+    torch.cuda.synchronize()
+    h = gemv_decode(args.steps, args.warmup)
+    log(f"headline: {h['per_step'] * 1e6:.2f} us/step")
+    w = h["workload"]
+    value = len(h["Ms"]) * h["weight_bytes"] / h["per_step"] / 1e9
+    launches_per_step = len(h["Ms"])
+    mean_launch = h["per_step"] / launches_per_step
+    alg_per_launch = h["alg_bytes_step"] / launches_per_step
+    achieved = alg_per_launch / mean_launch / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("source_hash") == source_hash(GEMV_SOURCES):
+            traffic = tr.get("bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "kernel": "fp4_gemv_kernel (MFMA decode GEMV)",
+                "alg_bytes_per_launch": round(alg_per_launch), "mean_launch_us": round(mean_launch * 1e6, 3)}
+
+    extra = {"per_M": h["per_m"], "weight_copies": h["R"]}
+    if not args.no_extra:
+        for name, fn in (("hbm_copy_GBps", hbm_copy_gbps),
+                         ("fp4_gemv_small", lambda: extra_small_gemv(args.steps, args.warmup)),
+                         ("fp4_gemv_wide", lambda: extra_wide(args.steps, args.warmup)),
+                         ("fp8", lambda: extra_fp8(args.steps, args.warmup)),
+                         ("fp4_prefill", extra_prefill_fp4)):
+            t0 = time.perf_counter()
+            extra[name] = fn()
+            torch.cuda.empty_cache()
+            log(f"{name}: {extra[name]} ({time.perf_counter() - t0:.1f} s)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline()
+        log(f"cpu baseline: {cpu}")
+
+    line = {
+        "metric": "FP4 GEMV weight GB/s (M=1..8) & prefill TFLOP/s, % of HBM/MFMA peak",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(h["per_step"] * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; shapes and distributions of the workload)",
+        "config": {"workload": "fp4_gemv_decode", "M": list(h["Ms"]), "N": w.N, "K": w.K,
+                   "block_size": 16, "activation": "bf16", "bias": True, "weight_copies": h["R"],
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,259 @@
+// C ABI entry points: argument validation and kernel-path dispatch.
+//
+// Plain host C++ (no device code).  The dispatch chain follows the shape of
+// [FP4 doc] §3 and [FP8 doc] §3 ("MatMulBlockQuantizedFp4Weight /
+// MatMulBlockQuantizedFp8Weight - CUDA Operator Documentation", Dispatch
+// Chain): empty output returns at once, small M takes the fused decode GEMV,
+// everything else a GEMM.  Unlike the pages' default path, the GEMM here is
+// fused (decode into MFMA operands), so no [N, K] scratch copy exists.
+
+#include <limits.h>
+#include <stdint.h>
+
+#include "../../include/fp4w.h"
+#include "launch.h"
+
+namespace {
+
+using fp4w::Act;
+using fp4w::DequantArgs;
+using fp4w::MatmulArgs;
+
+constexpr int64_t kMaxElems = int64_t(1) << 62;
+
+bool mul_ok(int64_t a, int64_t b) { return a == 0 || b <= kMaxElems / a; }
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+// [lo, lo + bytes) and [lo2, lo2 + bytes2) overlap?
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  if (a == nullptr || b == nullptr || abytes <= 0 || bbytes <= 0) return false;
+  uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + static_cast<uintptr_t>(bbytes) && b0 < a0 + static_cast<uintptr_t>(abytes);
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Shape rules shared by every op.  Returns FP4W_OK or an error status.
+int check_shape(int op, int64_t M, int64_t N, int64_t K, int64_t bs, int64_t cols) {
+  if (M < 0 || N < 0 || K < 0 || cols < 0) return FP4W_ERR_SHAPE;
+  if (bs < 1) return FP4W_ERR_BLOCK;
+  if (op == FP4W_OP_FP4_MATMUL || op == FP4W_OP_FP4_DEQUANT) {
+    if (K % 2 != 0) return FP4W_ERR_SHAPE;  // two E2M1 codes per byte ([FP4 doc] §2)
+  }
+  if (!mul_ok(M, K) || !mul_ok(N, K) || !mul_ok(M, N) || !mul_ok(N, cols)) return FP4W_ERR_SHAPE;
+  if (K > 0) {
+    // ceil(K/bs) columns, or floor(K/bs) >= 1 when the last block is partial
+    const int64_t c_ceil = ceil_div(K, bs), c_floor = K / bs;
+    const bool ok = cols == c_ceil || (K % bs != 0 && c_floor >= 1 && cols == c_floor);
+    if (!ok) return FP4W_ERR_SHAPE;
+  }
+  return FP4W_OK;
+}
+
+bool fp4_gemv_ok(int64_t M, int64_t K, int64_t bs) {
+  return M >= 1 && M <= 8 && bs == 16 && K % 32 == 0 && K > 0;
+}
+bool fp4_gemm_ok(int64_t M, int64_t K, int64_t bs) { return M >= 1 && bs == 16 && K % 64 == 0 && K > 0; }
+bool fp8_gemv_ok(int64_t M, int64_t K, int64_t bs) {
+  return M >= 1 && M <= 8 && bs % 128 == 0 && K % 128 == 0 && K > 0;
+}
+bool fp8_gemm_ok(int64_t M, int64_t K, int64_t bs) { return M >= 1 && bs % 64 == 0 && K % 64 == 0 && K > 0; }
+bool dequant_vec_ok(int64_t N, int64_t K, int64_t bs) {
+  return K % 8 == 0 && bs % 8 == 0 && K > 0 && N > 0 && (N * (K / 8)) < (int64_t(1) << 32);
+}
+
+// Path choice from sizes alone (pointers assumed 16-byte aligned).
+int shape_path(int op, int64_t M, int64_t N, int64_t K, int64_t bs) {
+  if (op == FP4W_OP_FP4_DEQUANT) {
+    if (N == 0 || K == 0) return FP4W_PATH_NONE;
+    return dequant_vec_ok(N, K, bs) ? FP4W_PATH_DEQUANT_VEC : FP4W_PATH_DEQUANT_GENERIC;
+  }
+  if (M == 0 || N == 0) return FP4W_PATH_NONE;
+  if (op == FP4W_OP_FP4_MATMUL) {
+    if (fp4_gemv_ok(M, K, bs)) return FP4W_PATH_FP4_GEMV;
+    if (M > 8 && fp4_gemm_ok(M, K, bs)) return FP4W_PATH_FP4_GEMM;
+    return FP4W_PATH_FP4_GENERIC;
+  }
+  if (fp8_gemv_ok(M, K, bs)) return FP4W_PATH_FP8_GEMV;
+  if (M > 8 && fp8_gemm_ok(M, K, bs)) return FP4W_PATH_FP8_GEMM;
+  return FP4W_PATH_FP8_GENERIC;
+}
+
+// Does `path` apply to these arguments, including pointer alignment?
+bool path_applies(int path, const MatmulArgs& a) {
+  switch (path) {
+    case FP4W_PATH_FP4_GEMV:
+      return fp4_gemv_ok(a.M, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 16) &&
+             aligned(a.scales, 2) && aligned(a.bias, 2) && aligned(a.Y, 2);
+    case FP4W_PATH_FP4_GEMM:
+      return fp4_gemm_ok(a.M, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 8) &&
+             aligned(a.bias, 2) && aligned(a.Y, 2);
+    case FP4W_PATH_FP4_GENERIC:
+    case FP4W_PATH_FP8_GENERIC:
+      return true;
+    case FP4W_PATH_FP8_GEMV:
+      return fp8_gemv_ok(a.M, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 16) &&
+             aligned(a.scales, 4) && aligned(a.bias, 2) && aligned(a.Y, 2);
+    case FP4W_PATH_FP8_GEMM:
+      return fp8_gemm_ok(a.M, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 16) &&
+             aligned(a.scales, 4) && aligned(a.bias, 2) && aligned(a.Y, 2);
+    default:
+      return false;
+  }
+}
+
+int run_matmul(int op, MatmulArgs& a, const void* scale_ptr_for_alias, int64_t scale_elem_bytes,
+               int path) {
+  const int dtype = static_cast<int>(a.act);
+  if (dtype != FP4W_F16 && dtype != FP4W_BF16) return FP4W_ERR_DTYPE;
+  int st = check_shape(op, a.M, a.N, a.K, a.block_size, a.scale_cols);
+  if (st != FP4W_OK) return st;
+  const bool fp4 = op == FP4W_OP_FP4_MATMUL;
+  if (path != FP4W_PATH_AUTO) {
+    const bool family_ok = fp4 ? (path == FP4W_PATH_FP4_GEMV || path == FP4W_PATH_FP4_GEMM ||
+                                  path == FP4W_PATH_FP4_GENERIC)
+                               : (path == FP4W_PATH_FP8_GEMV || path == FP4W_PATH_FP8_GEMM ||
+                                  path == FP4W_PATH_FP8_GENERIC);
+    if (!family_ok) return FP4W_ERR_PATH;
+  }
+  if (a.M == 0 || a.N == 0) return FP4W_OK;  // empty output: nothing to do
+  if (a.Y == nullptr) return FP4W_ERR_NULL;
+  if (a.K > 0 && (a.A == nullptr || a.B == nullptr || a.scales == nullptr)) return FP4W_ERR_NULL;
+  if (fp4 && a.K > 0 && a.ws2 == nullptr) return FP4W_ERR_NULL;
+
+  const int64_t ybytes = a.M * a.N * 2;
+  const int64_t bbytes = fp4 ? a.N * (a.K / 2) : a.N * a.K;
+  if (overlaps(a.Y, ybytes, a.A, a.M * a.K * 2) || overlaps(a.Y, ybytes, a.B, bbytes) ||
+      overlaps(a.Y, ybytes, scale_ptr_for_alias, a.N * a.scale_cols * scale_elem_bytes) ||
+      overlaps(a.Y, ybytes, a.bias, a.N * 2) || overlaps(a.Y, ybytes, a.ws2, fp4 ? 4 : 0))
+    return FP4W_ERR_ALIAS;
+
+  int chosen = path;
+  if (path == FP4W_PATH_AUTO) {
+    chosen = shape_path(op, a.M, a.N, a.K, a.block_size);
+    if (!path_applies(chosen, a)) chosen = fp4 ? FP4W_PATH_FP4_GENERIC : FP4W_PATH_FP8_GENERIC;
+  } else if (!path_applies(path, a)) {
+    return FP4W_ERR_PATH;
+  }
+  int rc = -1;
+  switch (chosen) {
+    case FP4W_PATH_FP4_GEMV: rc = fp4w::launch_fp4_gemv(a); break;
+    case FP4W_PATH_FP4_GEMM: rc = fp4w::launch_fp4_gemm(a); break;
+    case FP4W_PATH_FP4_GENERIC: rc = fp4w::launch_fp4_generic(a); break;
+    case FP4W_PATH_FP8_GEMV: rc = fp4w::launch_fp8_gemv(a); break;
+    case FP4W_PATH_FP8_GEMM: rc = fp4w::launch_fp8_gemm(a); break;
+    case FP4W_PATH_FP8_GENERIC: rc = fp4w::launch_fp8_generic(a); break;
+    default: return FP4W_ERR_PATH;
+  }
+  return rc == 0 ? FP4W_OK : FP4W_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp4w_matmul_ex(const void* A, int64_t M, int64_t K, const uint8_t* B, int64_t N,
+                   const uint8_t* weight_scale, int64_t scale_cols, int64_t block_size,
+                   const float* weight_scale_2, const void* bias, void* Y, int dtype, void* stream,
+                   int path) {
+  MatmulArgs a{A, B, weight_scale, weight_scale_2, bias, Y, M, N, K, block_size, scale_cols,
+               static_cast<Act>(dtype), stream};
+  return run_matmul(FP4W_OP_FP4_MATMUL, a, weight_scale, 1, path);
+}
+
+int fp4w_matmul(const void* A, int64_t M, int64_t K, const uint8_t* B, int64_t N,
+                const uint8_t* weight_scale, int64_t scale_cols, int64_t block_size,
+                const float* weight_scale_2, const void* bias, void* Y, int dtype, void* stream) {
+  return fp4w_matmul_ex(A, M, K, B, N, weight_scale, scale_cols, block_size, weight_scale_2, bias,
+                        Y, dtype, stream, FP4W_PATH_AUTO);
+}
+
+int fp8w_matmul_ex(const void* A, int64_t M, int64_t K, const uint8_t* B, int64_t N,
+                   const float* b_scale, int64_t scale_cols, int64_t block_size, const void* bias,
+                   void* Y, int dtype, void* stream, int path) {
+  MatmulArgs a{A, B, b_scale, nullptr, bias, Y, M, N, K, block_size, scale_cols,
+               static_cast<Act>(dtype), stream};
+  return run_matmul(FP4W_OP_FP8_MATMUL, a, b_scale, 4, path);
+}
+
+int fp8w_matmul(const void* A, int64_t M, int64_t K, const uint8_t* B, int64_t N,
+                const float* b_scale, int64_t scale_cols, int64_t block_size, const void* bias,
+                void* Y, int dtype, void* stream) {
+  return fp8w_matmul_ex(A, M, K, B, N, b_scale, scale_cols, block_size, bias, Y, dtype, stream,
+                        FP4W_PATH_AUTO);
+}
+
+int fp4w_dequant_ex(const uint8_t* B, int64_t N, int64_t K, const uint8_t* weight_scale,
+                    int64_t scale_cols, int64_t block_size, const float* weight_scale_2, void* out,
+                    int dtype, void* stream, int path) {
+  if (dtype != FP4W_F16 && dtype != FP4W_BF16) return FP4W_ERR_DTYPE;
+  int st = check_shape(FP4W_OP_FP4_DEQUANT, 0, N, K, block_size, scale_cols);
+  if (st != FP4W_OK) return st;
+  if (path != FP4W_PATH_AUTO && path != FP4W_PATH_DEQUANT_VEC && path != FP4W_PATH_DEQUANT_GENERIC)
+    return FP4W_ERR_PATH;
+  if (N == 0 || K == 0) return FP4W_OK;
+  if (B == nullptr || weight_scale == nullptr || weight_scale_2 == nullptr || out == nullptr)
+    return FP4W_ERR_NULL;
+  const int64_t obytes = N * K * 2;
+  if (overlaps(out, obytes, B, N * (K / 2)) || overlaps(out, obytes, weight_scale, N * scale_cols) ||
+      overlaps(out, obytes, weight_scale_2, 4))
+    return FP4W_ERR_ALIAS;
+  DequantArgs a{B, weight_scale, weight_scale_2, out, N, K, block_size, scale_cols,
+                static_cast<Act>(dtype), stream};
+  const bool vec_ok = dequant_vec_ok(N, K, block_size) && aligned(B, 4) && aligned(out, 16);
+  int chosen = path;
+  if (path == FP4W_PATH_AUTO) chosen = vec_ok ? FP4W_PATH_DEQUANT_VEC : FP4W_PATH_DEQUANT_GENERIC;
+  if (chosen == FP4W_PATH_DEQUANT_VEC && !vec_ok) return FP4W_ERR_PATH;
+  const int rc = chosen == FP4W_PATH_DEQUANT_VEC ? fp4w::launch_dequant_vec(a)
+                                                 : fp4w::launch_dequant_generic(a);
+  return rc == 0 ? FP4W_OK : FP4W_ERR_LAUNCH;
+}
+
+int fp4w_dequant(const uint8_t* B, int64_t N, int64_t K, const uint8_t* weight_scale,
+                 int64_t scale_cols, int64_t block_size, const float* weight_scale_2, void* out,
+                 int dtype, void* stream) {
+  return fp4w_dequant_ex(B, N, K, weight_scale, scale_cols, block_size, weight_scale_2, out, dtype,
+                         stream, FP4W_PATH_AUTO);
+}
+
+int fp4w_select_path(int op, int64_t M, int64_t N, int64_t K, int64_t block_size,
+                     int64_t scale_cols) {
+  if (op != FP4W_OP_FP4_MATMUL && op != FP4W_OP_FP8_MATMUL && op != FP4W_OP_FP4_DEQUANT)
+    return FP4W_ERR_PATH;
+  int st = check_shape(op, op == FP4W_OP_FP4_DEQUANT ? 0 : M, N, K, block_size, scale_cols);
+  if (st != FP4W_OK) return st;
+  return shape_path(op, M, N, K, block_size);
+}
+
+const char* fp4w_status_string(int status) {
+  switch (status) {
+    case FP4W_OK: return "ok";
+    case FP4W_ERR_NULL: return "a required pointer is NULL";
+    case FP4W_ERR_SHAPE: return "invalid shape (negative size, odd K for FP4, bad scale_cols or overflow)";
+    case FP4W_ERR_DTYPE: return "dtype must be FP4W_F16 or FP4W_BF16";
+    case FP4W_ERR_BLOCK: return "block_size must be >= 1";
+    case FP4W_ERR_PATH: return "the requested kernel path does not apply to these arguments";
+    case FP4W_ERR_LAUNCH: return "HIP reported an error when enqueuing the kernel";
+    case FP4W_ERR_ALIAS: return "the output overlaps an input";
+    default: return "unknown status";
+  }
+}
+
+const char* fp4w_path_name(int path) {
+  switch (path) {
+    case FP4W_PATH_AUTO: return "auto";
+    case FP4W_PATH_NONE: return "none";
+    case FP4W_PATH_FP4_GEMV: return "fp4_gemv";
+    case FP4W_PATH_FP4_GEMM: return "fp4_gemm";
+    case FP4W_PATH_FP4_GENERIC: return "fp4_generic";
+    case FP4W_PATH_FP8_GEMV: return "fp8_gemv";
+    case FP4W_PATH_FP8_GEMM: return "fp8_gemm";
+    case FP4W_PATH_FP8_GENERIC: return "fp8_generic";
+    case FP4W_PATH_DEQUANT_VEC: return "dequant_vec";
+    case FP4W_PATH_DEQUANT_GENERIC: return "dequant_generic";
+    default: return "unknown";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Internal interface between the host-side dispatch (dispatch.cpp, plain C++)
+// and the HIP launchers (*.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+namespace fp4w {
+
+enum class Act : int { F16 = 0, BF16 = 1 };
+
+// Arguments of one matmul call after validation.  `scales` is uint8 E4M3
+// bytes for FP4 and float for FP8; `ws2` is only used by FP4.
+struct MatmulArgs {
+  const void* A;
+  const uint8_t* B;
+  const void* scales;
+  const float* ws2;
+  const void* bias;
+  void* Y;
+  int64_t M, N, K, block_size, scale_cols;
+  Act act;
+  void* stream;  // hipStream_t
+};
+
+struct DequantArgs {
+  const uint8_t* B;
+  const uint8_t* scales;
+  const float* ws2;
+  void* out;
+  int64_t N, K, block_size, scale_cols;
+  Act act;
+  void* stream;
+};
+
+// Each launcher enqueues its kernel(s) and returns 0, or -1 when HIP reports
+// an error at enqueue time.  Preconditions (checked by the dispatcher, never
+// by the launcher) are stated next to each.
+
+// 1 <= M <= 8, block_size == 16, K % 32 == 0, scale_cols == K / 16,
+// A / B 16-byte aligned, scales and bias 2-byte aligned.
+int launch_fp4_gemv(const MatmulArgs& a);
+// M >= 1, block_size == 16, K % 64 == 0, scale_cols == K / 16,
+// A 16-byte aligned, B 8-byte aligned.
+int launch_fp4_gemm(const MatmulArgs& a);
+// any validated FP4 arguments (K may be 0)
+int launch_fp4_generic(const MatmulArgs& a);
+
+// 1 <= M <= 8, block_size % 128 == 0, K % 128 == 0, A / B 16-byte aligned,
+// scales 4-byte aligned.
+int launch_fp8_gemv(const MatmulArgs& a);
+// M >= 1, block_size % 64 == 0, K % 64 == 0, A / B 16-byte aligned.
+int launch_fp8_gemm(const MatmulArgs& a);
+// any validated FP8 arguments (K may be 0)
+int launch_fp8_generic(const MatmulArgs& a);
+
+// K % 8 == 0, block_size % 8 == 0, B 4-byte aligned, out 16-byte aligned,
+// N * K / 8 < 2^32.
+int launch_dequant_vec(const DequantArgs& a);
+// any validated arguments with N, K > 0
+int launch_dequant_generic(const DequantArgs& a);
+
+}  // namespace fp4w

@@ -1,0 +1,157 @@
+/*
+ * fp4w.h - block-scaled weight-only FP4 / FP8 matmul for AMD MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes only; the library never allocates, frees or
+ * synchronises.  Every call validates its arguments, enqueues its kernel(s) on
+ * `stream` (a hipStream_t, NULL = the default stream) and returns.  Faults in a
+ * kernel surface at the caller's next synchronisation.
+ *
+ * Sources, cited by page title and section:
+ *   [FP4 doc] "MatMulBlockQuantizedFp4Weight - CUDA Operator Documentation"
+ *             (ONNX Runtime 1.29.0 contrib-op docs)
+ *   [FP8 doc] "MatMulBlockQuantizedFp8Weight - CUDA Operator Documentation"
+ *   [Blog]    "ONNX Runtime #32128 - Why Dequantizing 4-Bit Weights Became the
+ *             Most Expensive Kernel in H200 Prefill"
+ *
+ * Common conventions
+ *   - All tensor pointers are DEVICE pointers owned by the caller, row-major
+ *     and contiguous.  Scalars passed by pointer (weight_scale_2) are device
+ *     pointers too: the kernel reads the value, so no host sync is needed.
+ *   - T (dtype) is FP16 or BF16 and is the type of A, bias and Y ([FP8 doc] §1
+ *     type constraints; [FP4 doc] §1: Y has A's type).  M is the product of
+ *     A's leading dimensions; Y is [M, N].
+ *   - Scale column of element k: min(k / block_size, scale_cols - 1).  A
+ *     partial final K block therefore uses the last scale column ([FP8 doc]
+ *     §2); scale_cols may be ceil(K / block_size) or, when K % block_size != 0,
+ *     floor(K / block_size) >= 1.  The same rule applies to FP4.
+ *   - M == 0 or N == 0: returns FP4W_OK and launches nothing ([FP4 doc] §3,
+ *     empty output).  K == 0: Y = bias, or 0 without bias (an empty sum).
+ *   - Y must not overlap any input (FP4W_ERR_ALIAS).
+ *   - Unaligned pointers or shapes outside a fast kernel's predicate run the
+ *     generic kernel; correctness never depends on the fast path.
+ *   - Accumulation is FP32.  The result is rounded once to T (round to
+ *     nearest even) after the tensor scale and bias are applied.
+ *   - Re-entrant and stateless; calls on different streams may overlap.
+ */
+#ifndef FP4W_H
+#define FP4W_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FP4W_F16 = 0, FP4W_BF16 = 1 } fp4w_dtype;
+
+typedef enum {
+  FP4W_OK = 0,
+  FP4W_ERR_NULL = -1,   /* a required pointer is NULL */
+  FP4W_ERR_SHAPE = -2,  /* negative size, odd K for FP4, bad scale_cols, size overflow */
+  FP4W_ERR_DTYPE = -3,  /* dtype is not FP4W_F16 / FP4W_BF16 */
+  FP4W_ERR_BLOCK = -4,  /* block_size < 1 */
+  FP4W_ERR_PATH = -5,   /* a forced path (the *_ex calls) does not apply to these arguments */
+  FP4W_ERR_LAUNCH = -6, /* HIP reported an error when the kernel was enqueued */
+  FP4W_ERR_ALIAS = -7   /* the output overlaps an input */
+} fp4w_status;
+
+/* Kernel paths.  FP4W_PATH_AUTO picks the fastest applicable one. */
+typedef enum {
+  FP4W_PATH_AUTO = 0,
+  FP4W_PATH_NONE = 1,            /* empty output: nothing launched */
+  FP4W_PATH_FP4_GEMV = 2,        /* MFMA decode GEMV: 1 <= M <= 8, block_size 16, K % 32 == 0 */
+  FP4W_PATH_FP4_GEMM = 3,        /* fused MFMA prefill GEMM: block_size 16, K % 64 == 0 */
+  FP4W_PATH_FP4_GENERIC = 4,     /* any legal FP4 arguments */
+  FP4W_PATH_FP8_GEMV = 5,        /* MFMA decode GEMV: 1 <= M <= 8, block_size % 128 == 0, K % 128 == 0 */
+  FP4W_PATH_FP8_GEMM = 6,        /* MFMA prefill GEMM: block_size % 64 == 0, K % 64 == 0 */
+  FP4W_PATH_FP8_GENERIC = 7,     /* any legal FP8 arguments */
+  FP4W_PATH_DEQUANT_VEC = 8,     /* vectorised dequant: K % 8 == 0, block_size % 8 == 0 */
+  FP4W_PATH_DEQUANT_GENERIC = 9  /* any legal dequant arguments */
+} fp4w_path;
+
+/* Operation selector for fp4w_select_path. */
+typedef enum { FP4W_OP_FP4_MATMUL = 0, FP4W_OP_FP8_MATMUL = 1, FP4W_OP_FP4_DEQUANT = 2 } fp4w_op;
+
+/*
+ * fp4w_matmul - weight-only FP4 matmul, Y = A * dequant(B)^T (+ bias).
+ * [FP4 doc] header and §2 Weight Format:
+ *   B_dq[n, k] = e2m1(B[n, k]) * e4m3(weight_scale[n, k / block_size]) * weight_scale_2
+ *
+ *   A              T[M, K]
+ *   B              uint8[N, K/2]: two E2M1 codes per byte, low nibble = even k,
+ *                  high nibble = odd k.  K must be even.
+ *   weight_scale   uint8[N, scale_cols]: raw E4M3 ("fn") bytes, unswizzled.
+ *   weight_scale_2 device float*: FP32 tensor scale.
+ *   bias           T[N] or NULL.
+ *   Y              T[M, N] (written).
+ * Errors: FP4W_ERR_NULL (A, B, weight_scale, weight_scale_2 or Y NULL while
+ * M, N > 0), FP4W_ERR_SHAPE, FP4W_ERR_BLOCK, FP4W_ERR_DTYPE, FP4W_ERR_ALIAS,
+ * FP4W_ERR_LAUNCH.  Nothing is launched when an error is returned.
+ */
+int fp4w_matmul(const void* A, int64_t M, int64_t K, const uint8_t* B, int64_t N,
+                const uint8_t* weight_scale, int64_t scale_cols, int64_t block_size,
+                const float* weight_scale_2, const void* bias, void* Y, int dtype, void* stream);
+
+/* Same as fp4w_matmul, with the kernel path forced (FP4W_PATH_AUTO, _FP4_GEMV,
+ * _FP4_GEMM or _FP4_GENERIC).  FP4W_ERR_PATH if the path does not apply. */
+int fp4w_matmul_ex(const void* A, int64_t M, int64_t K, const uint8_t* B, int64_t N,
+                   const uint8_t* weight_scale, int64_t scale_cols, int64_t block_size,
+                   const float* weight_scale_2, const void* bias, void* Y, int dtype, void* stream,
+                   int path);
+
+/*
+ * fp8w_matmul - weight-only FP8 matmul ([FP8 doc] §2 Tensor and Scale Format):
+ *   Y[m, n] = sum_k A[m, k] * (e4m3(B[n, k]) * b_scale[n, k / block_size]) + bias[n]
+ *
+ *   A        T[M, K]
+ *   B        uint8[N, K]: E4M3 ("fn") bytes.
+ *   b_scale  float[N, scale_cols]: FP32 block scales.
+ *   bias     T[N] or NULL.   Y  T[M, N].
+ * Errors as fp4w_matmul (no evenness rule on K).
+ */
+int fp8w_matmul(const void* A, int64_t M, int64_t K, const uint8_t* B, int64_t N,
+                const float* b_scale, int64_t scale_cols, int64_t block_size, const void* bias,
+                void* Y, int dtype, void* stream);
+
+/* Path-forcing variant (FP4W_PATH_AUTO, _FP8_GEMV, _FP8_GEMM, _FP8_GENERIC). */
+int fp8w_matmul_ex(const void* A, int64_t M, int64_t K, const uint8_t* B, int64_t N,
+                   const float* b_scale, int64_t scale_cols, int64_t block_size, const void* bias,
+                   void* Y, int dtype, void* stream, int path);
+
+/*
+ * fp4w_dequant - expand packed FP4 weights to T[N, K] ([FP4 doc] §5 step 1;
+ * [Blog] vectorised dequant).  out[n, k] = RNE_T(RNE_f32(e2m1 * e4m3 * ws2)):
+ * the E2M1 x E4M3 product is exact, the FP32 multiply by weight_scale_2 rounds
+ * once, then the FP32 value is rounded to T.  Bit-exact; no FTZ.
+ *
+ *   B, weight_scale, weight_scale_2: as fp4w_matmul.   out: T[N, K] (written).
+ * N == 0 or K == 0: FP4W_OK, nothing launched.
+ */
+int fp4w_dequant(const uint8_t* B, int64_t N, int64_t K, const uint8_t* weight_scale,
+                 int64_t scale_cols, int64_t block_size, const float* weight_scale_2, void* out,
+                 int dtype, void* stream);
+
+/* Path-forcing variant (FP4W_PATH_AUTO, _DEQUANT_VEC, _DEQUANT_GENERIC). */
+int fp4w_dequant_ex(const uint8_t* B, int64_t N, int64_t K, const uint8_t* weight_scale,
+                    int64_t scale_cols, int64_t block_size, const float* weight_scale_2, void* out,
+                    int dtype, void* stream, int path);
+
+/*
+ * fp4w_select_path - the path FP4W_PATH_AUTO takes for these sizes, assuming
+ * 16-byte-aligned pointers ([FP4 doc] §3 and [FP8 doc] §3 dispatch chains,
+ * re-derived for this library).  `op` is an fp4w_op.  For dequant, M is
+ * ignored.  Returns an fp4w_path, or a negative fp4w_status for illegal
+ * arguments.  Host-only; never touches the GPU.
+ */
+int fp4w_select_path(int op, int64_t M, int64_t N, int64_t K, int64_t block_size,
+                     int64_t scale_cols);
+
+/* Static strings; never NULL. */
+const char* fp4w_status_string(int status);
+const char* fp4w_path_name(int path);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4W_H */

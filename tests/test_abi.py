@@ -1,0 +1,170 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function
+include/fp4w.h declares, validates arguments before touching the device and
+reports the dispatch path.  No call here reaches a kernel launch."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_weight_only_fp4w_amd as fw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp4w.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(fp4w_\w+|fp8w_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("fp4w_matmul", "fp8w_matmul", "fp4w_dequant", "fp4w_status_string",
+                     "fp4w_select_path"):
+        assert required in names
+    assert sorted(fw.EXPORTED) == names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fw.load_library()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_and_path_strings():
+    assert fw.fp4w_status_string(fw.OK) == "ok"
+    for st in (fw.ERR_NULL, fw.ERR_SHAPE, fw.ERR_DTYPE, fw.ERR_BLOCK, fw.ERR_PATH, fw.ERR_LAUNCH, fw.ERR_ALIAS):
+        assert fw.fp4w_status_string(st) not in ("ok", "unknown status")
+    assert fw.fp4w_status_string(12345) == "unknown status"
+    assert fw.fp4w_path_name(fw.PATH_FP4_GEMV) == "fp4_gemv"
+    assert fw.fp4w_path_name(99) == "unknown"
+
+
+# -------------------------------------------------------------- dispatch
+
+def sel(op, M, N, K, bs, cols=None):
+    if cols is None:
+        cols = -(-K // bs) if (K and bs > 0) else 1
+    return fw.fp4w_select_path(op, M, N, K, bs, cols)
+
+
+def test_dispatch_fp4():
+    F = fw.OP_FP4_MATMUL
+    # decode GEMV for small M with the fast predicate
+    for M in (1, 2, 4, 8):
+        assert sel(F, M, 5120, 5120, 16) == fw.PATH_FP4_GEMV
+    assert sel(F, 1, 256, 512, 16) == fw.PATH_FP4_GEMV
+    # prefill GEMM for M > 8
+    assert sel(F, 9, 5120, 5120, 16) == fw.PATH_FP4_GEMM
+    assert sel(F, 8192, 17408, 5120, 16) == fw.PATH_FP4_GEMM
+    # outside the fast predicates -> generic ([Blog] "Existing FP4 tests did not
+    # reach the prefill kernel": every leaf must be reachable and tested)
+    assert sel(F, 4, 64, 48, 16) == fw.PATH_FP4_GENERIC        # K % 32 != 0
+    assert sel(F, 4, 64, 64, 32) == fw.PATH_FP4_GENERIC        # block_size != 16
+    assert sel(F, 4, 64, 30, 15) == fw.PATH_FP4_GENERIC        # odd block size
+    assert sel(F, 100, 64, 96, 16) == fw.PATH_FP4_GENERIC      # K % 64 != 0 for GEMM
+    assert sel(F, 3, 64, 0, 16) == fw.PATH_FP4_GENERIC         # K == 0: Y = bias
+    # empty output
+    assert sel(F, 0, 64, 64, 16) == fw.PATH_NONE
+    assert sel(F, 5, 0, 64, 16) == fw.PATH_NONE
+
+
+def test_dispatch_fp8():
+    F = fw.OP_FP8_MATMUL
+    assert sel(F, 4, 17408, 5120, 128) == fw.PATH_FP8_GEMV
+    assert sel(F, 8192, 17408, 5120, 128) == fw.PATH_FP8_GEMM
+    assert sel(F, 64, 256, 256, 64) == fw.PATH_FP8_GEMM
+    assert sel(F, 4, 256, 256, 64) == fw.PATH_FP8_GENERIC      # GEMV needs bs % 128
+    assert sel(F, 4, 256, 208, 128) == fw.PATH_FP8_GENERIC     # K % 128 != 0
+    assert sel(F, 64, 256, 208, 128) == fw.PATH_FP8_GENERIC
+    assert sel(F, 3, 256, 37, 16) == fw.PATH_FP8_GENERIC       # odd K is legal for FP8
+    assert sel(F, 0, 256, 256, 128) == fw.PATH_NONE
+
+
+def test_dispatch_dequant():
+    F = fw.OP_FP4_DEQUANT
+    assert sel(F, 0, 17408, 5120, 16) == fw.PATH_DEQUANT_VEC
+    assert sel(F, 0, 64, 40, 8) == fw.PATH_DEQUANT_VEC
+    assert sel(F, 0, 64, 30, 15) == fw.PATH_DEQUANT_GENERIC    # odd block size
+    assert sel(F, 0, 64, 12, 4) == fw.PATH_DEQUANT_GENERIC     # K % 8 != 0
+    assert sel(F, 0, 0, 64, 16) == fw.PATH_NONE
+    assert sel(F, 0, 64, 0, 16) == fw.PATH_NONE
+
+
+def test_select_path_rejects_illegal_shapes():
+    F = fw.OP_FP4_MATMUL
+    assert sel(F, 1, 16, 33, 16) == fw.ERR_SHAPE             # odd K for FP4
+    assert sel(F, -1, 16, 32, 16) == fw.ERR_SHAPE
+    assert sel(F, 1, 16, 32, 0) == fw.ERR_BLOCK
+    assert sel(F, 1, 16, 32, 16, cols=3) == fw.ERR_SHAPE     # wrong scale_cols
+    assert sel(F, 1, 16, 40, 16, cols=2) == fw.PATH_FP4_GENERIC  # floor(40/16) with partial block
+    assert sel(F, 1, 16, 32, 16, cols=1) == fw.ERR_SHAPE     # floor only allowed for partial blocks
+    assert sel(fw.OP_FP8_MATMUL, 1, 16, 33, 16) == fw.PATH_FP8_GENERIC
+    assert fw.fp4w_select_path(7, 1, 1, 2, 1, 2) == fw.ERR_PATH
+
+
+# -------------------------------------------------------------- validation (no launch)
+
+def _fp4(lib, A=1, M=1, K=32, B=1, N=16, ws=1, cols=2, bs=16, ws2=1, bias=None, Y=1, dtype=fw.BF16, path=0):
+    vp = ctypes.c_void_p
+    return lib.fp4w_matmul_ex(vp(A), M, K, vp(B), N, vp(ws), cols, bs, vp(ws2), vp(bias), vp(Y), dtype,
+                              None, path)
+
+
+def test_validation_errors_return_before_launch():
+    lib = fw.load_library()
+    # fake, distinct, non-overlapping "device" addresses: every case below must
+    # be rejected before any HIP call is made
+    base = dict(A=0x100000, B=0x200000, ws=0x300000, ws2=0x400000, Y=0x500000)
+    assert _fp4(lib, **{**base, "K": 33}) == fw.ERR_SHAPE
+    assert _fp4(lib, **{**base, "bs": 0}) == fw.ERR_BLOCK
+    assert _fp4(lib, **{**base, "dtype": 7}) == fw.ERR_DTYPE
+    assert _fp4(lib, **{**base, "cols": 5}) == fw.ERR_SHAPE
+    assert _fp4(lib, **{**base, "M": -1}) == fw.ERR_SHAPE
+    assert _fp4(lib, **{**base, "A": 0}) == fw.ERR_NULL
+    assert _fp4(lib, **{**base, "B": 0}) == fw.ERR_NULL
+    assert _fp4(lib, **{**base, "ws": 0}) == fw.ERR_NULL
+    assert _fp4(lib, **{**base, "ws2": 0}) == fw.ERR_NULL
+    assert _fp4(lib, **{**base, "Y": 0}) == fw.ERR_NULL
+    assert _fp4(lib, **{**base, "Y": 0x100000 + 8}) == fw.ERR_ALIAS       # Y inside A
+    assert _fp4(lib, **{**base, "path": fw.PATH_FP8_GEMV}) == fw.ERR_PATH  # wrong family
+    assert _fp4(lib, **{**base, "M": 9, "path": fw.PATH_FP4_GEMV}) == fw.ERR_PATH  # M > 8
+    assert _fp4(lib, **{**base, "A": 0x100002, "path": fw.PATH_FP4_GEMV}) == fw.ERR_PATH  # unaligned
+
+
+def test_empty_output_is_ok_without_pointers():
+    lib = fw.load_library()
+    assert _fp4(lib, A=0, B=0, ws=0, ws2=0, Y=0, M=0) == fw.OK
+    assert _fp4(lib, A=0, B=0, ws=0, ws2=0, Y=0, N=0) == fw.OK
+    vp = ctypes.c_void_p
+    assert lib.fp4w_dequant(None, 0, 32, None, 2, 16, None, None, fw.BF16, None) == fw.OK
+    assert lib.fp8w_matmul(None, 0, 128, None, 16, None, 1, 128, None, None, fw.BF16, None) == fw.OK
+
+
+def test_fp8_and_dequant_validation():
+    lib = fw.load_library()
+    vp = ctypes.c_void_p
+    A, B, S, Y = vp(0x100000), vp(0x200000), vp(0x300000), vp(0x500000)
+    assert lib.fp8w_matmul(A, 1, 128, B, 16, S, 2, 128, None, Y, fw.BF16, None) == fw.ERR_SHAPE
+    assert lib.fp8w_matmul(A, 1, 128, B, 16, S, 1, 0, None, Y, fw.BF16, None) == fw.ERR_BLOCK
+    assert lib.fp8w_matmul(A, 1, 128, None, 16, S, 1, 128, None, Y, fw.BF16, None) == fw.ERR_NULL
+    assert lib.fp4w_dequant(B, 16, 31, S, 2, 16, vp(0x400000), Y, fw.BF16, None) == fw.ERR_SHAPE
+    assert lib.fp4w_dequant(B, 16, 32, S, 2, 16, None, Y, fw.BF16, None) == fw.ERR_NULL
+    assert lib.fp4w_dequant(B, 16, 32, S, 2, 16, vp(0x400000), vp(0x200000), fw.BF16, None) == fw.ERR_ALIAS
+    assert lib.fp4w_dequant_ex(B, 16, 12, S, 3, 4, vp(0x400000), Y, fw.BF16, None,
+                               fw.PATH_DEQUANT_VEC) == fw.ERR_PATH
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    import importlib
+    mod = importlib.reload(fw)
+    try:
+        mod._lib = None
+        with pytest.raises(RuntimeError):
+            mod.load_library(str(tmp_path / "missing.so"))
+    finally:
+        importlib.reload(fw)
