@@ -293,21 +293,40 @@ def extra_wide(steps, warmup):
 
 def profile_kernel(which, launches=50):
     """Launch one kernel `launches` times without graphs, for rocprofv3 runs
-    (kernel trace or PMC counters)."""
+    (kernel trace or PMC counters).  Weight copies rotate as in the timed runs."""
     if which == "copy":
         n = 256 << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(launches):
             dst.copy_(src)
-    else:
-        w = workloads.WORKLOADS["fp4_gemv_decode"]
-        p = w.make(M=8)
+    elif which in ("fp4_gemv", "fp4_gemv_wide"):
+        w = workloads.WORKLOADS["fp4_gemv_decode" if which == "fp4_gemv" else "fp4_gemv_wide"]
+        p = w.make(M=8 if which == "fp4_gemv" else 4)
         R = copies_for(p.B.nbytes + p.weight_scale.nbytes)
         d = fp4_on_device(p, copies=R)
-        out = torch.empty(8, w.N, dtype=torch.bfloat16, device="cuda")
+        out = torch.empty(p.M, w.N, dtype=torch.bfloat16, device="cuda")
         for i in range(launches):
             fw.fp4w_matmul(d["A"], d["B"][i % R], d["ws"][i % R], d["ws2"], d["bias"], 16, out=out)
+    elif which == "fp8_gemv":
+        p = workloads.WORKLOADS["fp8_gemv"].make(M=4)
+        R = copies_for(p.B.nbytes + p.b_scale.nbytes)
+        d = fp8_on_device(p, copies=R)
+        out = torch.empty(4, p.N, dtype=torch.bfloat16, device="cuda")
+        for i in range(launches):
+            fw.fp8w_matmul(d["A"], d["B"][i % R], d["bs"][i % R], None, 128, out=out)
+    elif which == "fp4_gemm":
+        p = workloads.WORKLOADS["fp4_prefill"].make()
+        d = fp4_on_device(p)
+        out = torch.empty(p.M, p.N, dtype=torch.bfloat16, device="cuda")
+        for _ in range(min(launches, 10)):
+            fw.fp4w_matmul(d["A"], d["B"][0], d["ws"][0], d["ws2"], None, 16, out=out)
+    elif which == "dequant":
+        p = workloads.WORKLOADS["fp4_prefill"].make(M=1)
+        d = fp4_on_device(p)
+        out = torch.empty(p.N, p.K, dtype=torch.bfloat16, device="cuda")
+        for _ in range(launches):
+            fw.fp4w_dequant(d["B"][0], d["ws"][0], d["ws2"], 16, out=out)
     torch.cuda.synchronize()
     log(f"profiled {launches} launches of {which}")
 
@@ -321,7 +340,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--profile-kernel", choices=["fp4_gemv", "copy"])
+    ap.add_argument("--profile-kernel", choices=["fp4_gemv", "fp4_gemv_wide", "fp8_gemv", "fp4_gemm", "dequant", "copy"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library runs on a single MI355X and has no "

@@ -28,25 +28,6 @@
 namespace fp4w {
 namespace {
 
-// n / d for 32-bit n by a fixed divisor d >= 1 (Granlund & Montgomery,
-// "Division by invariant integers using multiplication", 1994):
-// q = (umulhi(n, m) + n) >> l with l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1.
-struct FastDiv {
-  uint32_t m, l, d;
-};
-
-FastDiv make_fastdiv(uint32_t d) {
-  uint32_t l = 0;
-  while ((uint64_t(1) << l) < d) ++l;
-  const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
-  return FastDiv{static_cast<uint32_t>(m), l, d};
-}
-
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
-  const uint64_t t = static_cast<uint64_t>(__umulhi(n, f.m)) + n;
-  return static_cast<uint32_t>(t >> f.l);
-}
-
 template <typename T>
 struct Store8;
 template <>

@@ -134,6 +134,69 @@ struct ActTraits<_Float16> {
   __device__ __forceinline__ static float to_f32(_Float16 x) { return static_cast<float>(x); }
 };
 
+// ------------------------------------------------------------------ 16x16x16 MFMA
+//
+// v_mfma_f32_16x16x16_{bf16,f16}: K = 16 is exactly one FP4 scale block, so
+// a block can be multiplied unscaled (E2M1 -> T is a plain conversion) and
+// its FP32 result scaled afterwards.  Operand layout (checked on gfx950):
+// lane l supplies row / column l % 16 and k = 4 (l / 16) .. 4 (l / 16) + 3;
+// the result lane l holds column l % 16, rows 4 (l / 16) .. 4 (l / 16) + 3.
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+struct Mfma16;
+
+template <>
+struct Mfma16<__bf16> {
+  typedef bf16x4 vec4;
+  // 4 E2M1 codes in half H (bytes 2H, 2H+1) of `w`, low nibble first -> 4 x T
+  template <int H>
+  __device__ __forceinline__ static vec4 decode4(uint32_t w) {
+    const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2 * H);
+    const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2 * H + 1);
+    vec4 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = hi[0]; r[3] = hi[1];
+    return r;
+  }
+  __device__ __forceinline__ static f32x4 mfma(vec4 a, vec4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mfma16<_Float16> {
+  typedef f16x4 vec4;
+  template <int H>
+  __device__ __forceinline__ static vec4 decode4(uint32_t w) {
+    const f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2 * H);
+    const f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2 * H + 1);
+    vec4 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = hi[0]; r[3] = hi[1];
+    return r;
+  }
+  __device__ __forceinline__ static f32x4 mfma(vec4 a, vec4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  }
+};
+
+// 4 x 4 transpose of dwords across the four 16-lane groups of a wave: on
+// entry lane group g holds x[h] (h = 0..3) meant for group h; on exit lane
+// group g holds, in x[h], what group h held in x[g].  Two v_permlane32_swap
+// (exchange between lane halves) then two v_permlane16_swap (exchange between
+// neighbouring 16-lane rows).
+__device__ __forceinline__ void transpose4x4_groups(uint32_t (&x)[4]) {
+  const auto a = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  x[0] = c[0];
+  x[1] = c[1];
+  x[2] = d[0];
+  x[3] = d[1];
+}
+
 // Materialise an FP32 value in a VGPR.  Without this the backend may fold
 // "multiply in FP32, then convert to FP16" into one mixed-precision FMA
 // (v_fma_mix*_f16 with a +0 addend), which rounds once instead of twice and
@@ -149,6 +212,71 @@ __device__ __forceinline__ float f32_barrier(float x) {
 template <typename T>
 __device__ __forceinline__ T round_to(float x) {
   return static_cast<T>(f32_barrier(x));
+}
+
+// ------------------------------------------------------------------ division
+//
+// n / d for 32-bit n by a divisor d >= 1 fixed at launch (Granlund &
+// Montgomery, "Division by invariant integers using multiplication", 1994):
+// q = (umulhi(n, m) + n) >> l with l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1.
+struct FastDiv {
+  uint32_t m, l, d;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((uint64_t(1) << l) < d) ++l;
+  const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
+  return FastDiv{static_cast<uint32_t>(m), l, d};
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+  const uint64_t t = static_cast<uint64_t>(__umulhi(n, f.m)) + n;
+  return static_cast<uint32_t>(t >> f.l);
+}
+
+// ------------------------------------------------------------------ buffer loads
+//
+// Raw buffer loads through a wave-uniform resource descriptor: an access at or
+// beyond `bytes` from the base returns zero instead of faulting, so tails and
+// masked lanes need no branch around the load (branches there make the
+// compiler wait for every outstanding load).  Offsets are 32-bit.
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // any offset >= every `bytes` used here
+
+// `base` and `bytes` must be the same on every lane of the wave.  They are
+// passed through readfirstlane so the compiler knows it too: a descriptor it
+// cannot prove uniform is wrapped in a per-lane loop around every load.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  void* up = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  // third descriptor dword for raw (untyped, unswizzled) buffers on gfx9-family GPUs
+  return __builtin_amdgcn_make_buffer_rsrc(up, static_cast<short>(0), static_cast<int>(n), 0x00020000);
+}
+// The offsets passed below are often `cond ? offset : kOutOfRange`; left as
+// is, the compiler may turn that select into two branches, each with its own
+// load, and then wait for all loads where they join.  Pinning the offset in a
+// VGPR first keeps it a select (the barrier emits no instruction).
+__device__ __forceinline__ uint32_t vgpr(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+__device__ __forceinline__ u32x4 buf_load_b128(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, vgpr(off), 0, 0));
+}
+__device__ __forceinline__ u32x2 buf_load_b64(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, vgpr(off), 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load_b32(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, vgpr(off), 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load_u16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, vgpr(off), 0, 0);
 }
 
 // 16-byte global load of 8 T values, reinterpreted as the MFMA operand type.

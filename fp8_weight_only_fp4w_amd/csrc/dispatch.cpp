@@ -52,7 +52,7 @@ int check_shape(int op, int64_t M, int64_t N, int64_t K, int64_t bs, int64_t col
 }
 
 bool fp4_gemv_ok(int64_t M, int64_t K, int64_t bs) {
-  return M >= 1 && M <= 8 && bs == 16 && K % 32 == 0 && K > 0;
+  return M >= 1 && M <= 8 && bs == 16 && K % 128 == 0 && K > 0;
 }
 bool fp4_gemm_ok(int64_t M, int64_t K, int64_t bs) { return M >= 1 && bs == 16 && K % 64 == 0 && K > 0; }
 bool fp8_gemv_ok(int64_t M, int64_t K, int64_t bs) {
@@ -85,7 +85,7 @@ bool path_applies(int path, const MatmulArgs& a) {
   switch (path) {
     case FP4W_PATH_FP4_GEMV:
       return fp4_gemv_ok(a.M, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 16) &&
-             aligned(a.scales, 2) && aligned(a.bias, 2) && aligned(a.Y, 2);
+             aligned(a.scales, 4) && aligned(a.bias, 2) && aligned(a.Y, 2);
     case FP4W_PATH_FP4_GEMM:
       return fp4_gemm_ok(a.M, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 8) &&
              aligned(a.bias, 2) && aligned(a.Y, 2);

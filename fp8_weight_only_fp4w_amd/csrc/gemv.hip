@@ -1,29 +1,45 @@
 // Decode GEMV (1 <= M <= 8) for weight-only FP4 and FP8, on MFMA.
 //
 // Memory-bound: every packed weight byte and scale byte is read from HBM once
-// with 16-byte loads; activations (M x K, at most 80 KiB) are re-read from L2
-// only once per 16 output columns.
+// with 16-byte loads; activations (M x K, at most a few hundred KiB) come from
+// LDS or L2.
 //
-// Structure (per wave64; see [FP4 doc] §4 "Tensor-core sub-path" and [FP8
-// doc] §4.1 for the pages' CUDA mma.m16n8k16 version, which this re-derives
-// for the CDNA4 v_mfma_f32_16x16x32_{bf16,f16} operand layout):
-//  * one MFMA tile = 16 output columns n (the B operand: lane l supplies
-//    column l % 16) x 16 activation rows m (the A operand, rows >= M are
-//    zero) x 32 k-slots, lane group g = l / 16 supplying k-slots 8g..8g+7;
-//  * K is a reduction axis, so it is permuted: in window w (128 k), lane group
-//    g owns the contiguous chunk c = 4w + g of 32 k.  One 16-byte load gives
-//    that lane its 32 FP4 codes (one uint4 per lane per window, as on the
-//    page), and MFMA i (i = 0..3) takes k = 32c + 8i .. 32c + 8i + 7 for both
-//    operands;
-//  * FP4: the E4M3 block scale is folded into the decoded weight before the
-//    MFMA, exactly (E2M1 x E4M3 needs <= 6 significand bits: [FP4 doc] §4);
-//    weight_scale_2 is applied once in the epilogue, bias fused there too
-//    ([FP4 doc] §4);
-//  * FP8: E4M3 -> T is exact, but the FP32 block scale is not, so each
-//    window (which lies inside one scale block, block_size % 128 == 0) is
-//    accumulated in a fresh MFMA accumulator and then scaled in FP32;
-//  * KS waves of a workgroup split the K windows (the page's KSplit) and are
-//    reduced through LDS; R column tiles per wave share one activation load.
+// Common structure (the pages' CUDA version is [FP4 doc] §4 "Tensor-core
+// sub-path" / [FP8 doc] §4.1, with mma.m16n8k16; this is re-derived for the
+// CDNA4 MFMA layouts).  A wave owns a tile of 16 output columns n (the MFMA B
+// operand: lane l supplies column l % 16).  K is a reduction axis, so it is
+// permuted freely as long as both operands agree: in window w (128 k) lane
+// group g = l / 16 loads the contiguous chunk c = 4w + g of 32 k of its
+// column, one 16-byte load per lane for FP4 (two for FP8).
+//
+// FP4 (16x16x16 MFMA, "block-diagonal" activations).  Folding the E4M3 scale
+// into BF16 weights would be exact ([FP4 doc] §4), but costs a convert, two
+// FP32 multiplies and a pack per pair of weights, which makes a wave64 GEMV
+// VALU-bound on CDNA4.  Instead the weights are converted unscaled (one
+// instruction per pair) and every 16-k scale block gets its own FP32 dot,
+// scaled by its E4M3 value with one FMA.  Four blocks share each MFMA: lane
+// group g holds blocks 2g and 2g + 1 of the window, so in MFMA (s, p) the
+// four lane groups supply piece p (4 k) of blocks 2g + s, g = 0..3.  Row
+// i = 4 m' + q of the A operand carries activation row m = m' (+ 4 for the
+// second row half) in the k slots of lane group q only, and zeros elsewhere;
+// summing the four pieces p therefore leaves in result row (m', q) the full
+// dot of row m with block 2q + s.  The result lane (column n, group g) holds
+// rows 4g .. 4g + 3 = the four blocks of one activation row, so a window
+// costs 8 MFMAs and 8 FMAs per row half, with no data exchange between lanes.
+// weight_scale_2 and the bias are applied once in the epilogue.
+//
+// FP8 (16x16x32 MFMA).  E4M3 -> T is exact and the FP32 block scale is
+// applied to a window (128 k, inside one scale block: block_size % 128 == 0)
+// accumulated in a fresh MFMA accumulator.  Result lane (n, g) holds rows
+// 4g .. 4g + 3.
+//
+// Latency hiding (what decides the bandwidth): a wave keeps D windows of
+// weights in flight ahead of the one it multiplies; the pipeline runs as one
+// flat sequence over all tile groups the (persistent) workgroup owns, so it
+// never drains between tiles.  All loads are raw buffer loads and
+// branch-free (tails read zeros), so the loop only ever waits for its oldest
+// load.  A workgroup is KS x TPW waves: KS waves split the K windows of one
+// tile (the page's KSplit, reduced through LDS), TPW tiles side by side.
 //
 // [FP4 doc] = "MatMulBlockQuantizedFp4Weight - CUDA Operator Documentation"
 // [FP8 doc] = "MatMulBlockQuantizedFp8Weight - CUDA Operator Documentation"
@@ -36,319 +52,479 @@
 namespace fp4w {
 namespace {
 
-template <typename V>
-__device__ __forceinline__ V zero_vec() {
-  V v;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = 0;
-  return v;
+constexpr int kWaves = 8;  // waves per workgroup (KS x TPW)
+
+// Raw data of one window for one lane.  FP4: 16 weight bytes, the 8 E4M3
+// scale bytes of the lane's column for the window's 8 blocks, and (when they
+// come from L2) the lane's 64 activation bytes per row half.  FP8: 32 weight
+// bytes, the window's FP32 scale, the activations.  The bias bits of the
+// lane's column ride along with the last window of each tile group, so the
+// epilogue never waits on a late load (loads retire in order: waiting on one
+// issued after the prefetches would drain them all).
+template <bool FP8, bool ACT_REG, int R>
+struct Raw;
+template <bool ACT_REG, int R>
+struct Raw<false, ACT_REG, R> {
+  u32x4 w;
+  u32x2 s;
+  uint32_t bias;
+  u32x4 a[ACT_REG ? 4 * R : 1];
+};
+template <bool ACT_REG, int R>
+struct Raw<true, ACT_REG, R> {
+  u32x4 w0, w1;
+  float s;
+  uint32_t bias;
+  u32x4 a[ACT_REG ? 4 : 1];  // 4 x 8 activations (k 32c .. 32c + 31)
+};
+
+// Position of a wave in its flat window sequence: tile group and window.
+struct Pos {
+  int tg, j;
+  __device__ __forceinline__ void advance(int nws, int stride) {
+    if (++j == nws) {
+      j = 0;
+      tg += stride;
+    }
+  }
+};
+
+// Dwords 2J, 2J + 1 of a 16-byte register as a 4-wide MFMA operand.
+template <typename V4, int J>
+__device__ __forceinline__ V4 half_of(u32x4 v) {
+  return __builtin_bit_cast(V4, u32x2{v[2 * J], v[2 * J + 1]});
 }
 
-// Activations of one lane for one chunk: A[m][32c .. 32c + 31] (4 x 16 bytes).
-template <typename T, typename V>
-__device__ __forceinline__ void load_act(const T* __restrict__ arow, int c, bool ok, V (&a)[4]) {
-  if (ok) {
-    const T* p = arow + 32 * c;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = load16<V>(p + 8 * i);
+// Activations, two ways (ACT_LDS):
+//  * false: loaded from L2 with the weights, at the same pipeline depth;
+//  * true: copied once into LDS by the persistent workgroup (rows zero-padded
+//    to whole 128-k windows; for FP4 one all-zero row follows the M rows), so
+//    the loop issues weight loads only.
+// Either way the load consumed next is always the oldest one in flight.
+// R: FP4 - row halves (1: M <= 4, 2: M <= 8); FP8 - result rows a lane
+// scales (1, 2 or 4).  D: windows in flight ahead of the multiply.
+template <typename T, int KS, bool FP8, bool ACT_LDS, int R, int D>
+__global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
+    const T* __restrict__ A, const uint8_t* __restrict__ B, const void* __restrict__ scales,
+    const float* __restrict__ ws2p, const T* __restrict__ bias, T* __restrict__ Y, int M, int N,
+    int K, int cols, FastDiv win_per_block, FastDiv chunks_per_row, int num_tiles, int nws) {
+  constexpr bool ACT_REG = !ACT_LDS;
+  constexpr int TPW = kWaves / KS;
+  constexpr int S = D + 1;  // register slots of the pipeline
+  typedef Raw<FP8, ACT_REG, R> RawT;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int li = lane & 15, g = lane >> 4;
+  const int ks = wave % KS, tw = wave / KS;
+  const int NW = K >> 7;  // 128-k windows (K % 128 == 0)
+  const int ntg = (num_tiles + TPW - 1) / TPW;
+  const int iters = (ntg - static_cast<int>(blockIdx.x) + static_cast<int>(gridDim.x) - 1) /
+                    static_cast<int>(gridDim.x);
+  // every wave of the workgroup runs the same sequence, so the barriers of
+  // the K-split reduction are uniform
+  const int total = iters * nws;
+  const int stride = gridDim.x;
+  const uint32_t row_bytes = FP8 ? static_cast<uint32_t>(K) : static_cast<uint32_t>(K >> 1);
+  const uint32_t srow_bytes = FP8 ? static_cast<uint32_t>(cols) * 4u : static_cast<uint32_t>(cols);
+  const float ws2 = FP8 ? 1.0f : *ws2p;  // one scalar load, kept in a register
+
+  f32x4* red = reinterpret_cast<f32x4*>(smem);  // [kWaves][64] when KS > 1
+  unsigned char* a_lds = smem + (KS > 1 ? kWaves * 64 * sizeof(f32x4) : 0);
+  const uint32_t lds_pitch = static_cast<uint32_t>(NW) * 256u + 16u;  // bytes per LDS row of A
+  const uint32_t a_bytes = static_cast<uint32_t>(M) * static_cast<uint32_t>(K) * 2u;
+  const rsrc_t a_rsrc = make_rsrc(A, a_bytes);
+
+  // Per-lane activation offsets (bytes, window 0).  FP4: lane (li = 4m' + q,
+  // g) carries row m = m' + 4h of half h when q == g, else zeros (the zero
+  // LDS row, or an out-of-range offset).  FP8: row li (rows >= M are never
+  // stored, so lanes li >= M may read any valid row).
+  uint32_t a_off[FP8 ? 1 : R];
+  if constexpr (FP8) {
+    a_off[0] = ACT_LDS ? static_cast<uint32_t>(li % M) * lds_pitch
+                       : static_cast<uint32_t>(li) * static_cast<uint32_t>(K) * 2u;
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = zero_vec<V>();
-  }
-}
-
-// --------------------------------------------------------------------- FP4
-
-template <typename T, int R, int KS>
-__global__ __launch_bounds__(64 * KS) void fp4_gemv_kernel(
-    const T* __restrict__ A, const uint8_t* __restrict__ B, const uint8_t* __restrict__ ws,
-    const float* __restrict__ ws2p, const T* __restrict__ bias, T* __restrict__ Y, int M, int N,
-    int K) {
-  typedef ActTraits<T> Tr;
-  typedef typename Tr::vec8 V;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int li = lane & 15, g = lane >> 4;
-  const int n_base = blockIdx.x * (16 * R);
-  const int NC = K >> 5;          // 32-k chunks
-  const int NW = (NC + 3) >> 2;   // 128-k windows
-  const int half_k = K >> 1;      // bytes per packed row
-  const int cols = K >> 4;        // scale bytes per row
-
-  const bool m_ok = li < M;
-  const T* arow = A + static_cast<size_t>(m_ok ? li : 0) * K;
-  const uint8_t* brow[R];
-  const uint8_t* srow[R];
-  bool n_ok[R];
-#pragma unroll
-  for (int t = 0; t < R; ++t) {
-    const int n = n_base + 16 * t + li;
-    n_ok[t] = n < N;
-    const size_t nn = n_ok[t] ? n : 0;
-    brow[t] = B + nn * half_k;
-    srow[t] = ws + nn * cols;
+    for (int h = 0; h < R; ++h) {
+      const int m = (li >> 2) + 4 * h;
+      const bool valid = (li & 3) == g && m < M;
+      if constexpr (ACT_LDS)
+        a_off[h] = static_cast<uint32_t>(valid ? m : M) * lds_pitch + 64u * g;
+      else
+        a_off[h] = valid ? static_cast<uint32_t>(m) * static_cast<uint32_t>(K) * 2u + 64u * g : kOutOfRange;
+    }
   }
 
-  f32x4 acc[R];
+  auto load = [&](Pos p, RawT& r) {
+    const int t = p.tg * TPW + tw;
+    const int rows = max(0, min(16, N - 16 * t));
+    const size_t n0 = static_cast<size_t>(16) * t;
+    const rsrc_t br = make_rsrc(B + n0 * row_bytes, rows * row_bytes);
+    const rsrc_t sr = make_rsrc(static_cast<const uint8_t*>(scales) + n0 * srow_bytes, rows * srow_bytes);
+    const rsrc_t biasr = make_rsrc(bias + n0, bias ? rows * 2u : 0u);
+    r.bias = buf_load_u16(biasr, p.j == nws - 1 ? 2u * li : kOutOfRange);
+    const int w = ks * nws + p.j;
+    const bool ok = w < NW;
+    const int c = 4 * w + g;
+    if constexpr (FP8) {
+      const uint32_t off = ok ? li * row_bytes + 32u * c : kOutOfRange;
+      r.w0 = buf_load_b128(br, off);
+      r.w1 = buf_load_b128(br, off + 16u);
+      // a window lies inside one scale column
+      const uint32_t col = min(fdiv(static_cast<uint32_t>(w), win_per_block), static_cast<uint32_t>(cols - 1));
+      r.s = __builtin_bit_cast(float, buf_load_b32(sr, ok ? li * srow_bytes + 4u * col : kOutOfRange));
+      if constexpr (ACT_REG) {
+        const uint32_t aoff = ok ? a_off[0] + 64u * c : kOutOfRange;
 #pragma unroll
-  for (int t = 0; t < R; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // software pipeline: raw data of the next window is in flight while the
-  // current one is decoded and multiplied
-  V a_cur[4];
-  u32x4 w_cur[R];
-  uint32_t s_cur[R];
-  int w = wave;
-  auto fetch = [&](int win, V (&a)[4], u32x4 (&wq)[R], uint32_t (&sc)[R]) {
-    const int c = 4 * win + g;
-    const bool c_ok = (win < NW) && (c < NC);
-    load_act<T, V>(arow, c, m_ok && c_ok, a);
+        for (int i = 0; i < 4; ++i) r.a[i] = buf_load_b128(a_rsrc, aoff + 16u * i);
+      }
+    } else {
+      r.w = buf_load_b128(br, ok ? li * row_bytes + 16u * c : kOutOfRange);
+      // the 8 scale bytes of the window's blocks 8w .. 8w + 7 in one 8-byte
+      // load, dword aligned and inside the row because K % 128 == 0
+      r.s = buf_load_b64(sr, ok ? li * srow_bytes + 8u * w : kOutOfRange);
+      if constexpr (ACT_REG) {
 #pragma unroll
-    for (int t = 0; t < R; ++t) {
-      if (n_ok[t] && c_ok) {
-        wq[t] = *reinterpret_cast<const u32x4*>(brow[t] + 16 * c);
-        sc[t] = *reinterpret_cast<const uint16_t*>(srow[t] + 2 * c);
-      } else {
-        wq[t] = u32x4{0u, 0u, 0u, 0u};
-        sc[t] = 0u;
+        for (int h = 0; h < R; ++h) {
+          // out-of-range lanes stay out of range: a_off < 2^31 or >= 2^31
+          const uint32_t aoff = ok ? a_off[h] + 256u * w : kOutOfRange;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) r.a[4 * h + i] = buf_load_b128(a_rsrc, aoff + 16u * i);
+        }
       }
     }
   };
-  fetch(w, a_cur, w_cur, s_cur);
-  for (; w < NW; w += KS) {
-    V a_nxt[4];
-    u32x4 w_nxt[R];
-    uint32_t s_nxt[R];
-    fetch(w + KS, a_nxt, w_nxt, s_nxt);
+
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  RawT raw[S];
+  Pos lp{static_cast<int>(blockIdx.x), 0};  // next window to load
+  Pos cp{static_cast<int>(blockIdx.x), 0};  // window being multiplied
+
 #pragma unroll
-    for (int t = 0; t < R; ++t) {
-      const typename Tr::scale_t s0 = Tr::make_scale(e4m3_to_f32<0>(s_cur[t]));
-      const typename Tr::scale_t s1 = Tr::make_scale(e4m3_to_f32<1>(s_cur[t]));
-      const V b0 = Tr::decode8(w_cur[t].x, s0);
-      const V b1 = Tr::decode8(w_cur[t].y, s0);
-      const V b2 = Tr::decode8(w_cur[t].z, s1);
-      const V b3 = Tr::decode8(w_cur[t].w, s1);
-      acc[t] = Tr::mfma(a_cur[0], b0, acc[t]);
-      acc[t] = Tr::mfma(a_cur[1], b1, acc[t]);
-      acc[t] = Tr::mfma(a_cur[2], b2, acc[t]);
-      acc[t] = Tr::mfma(a_cur[3], b3, acc[t]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a_cur[i] = a_nxt[i];
-#pragma unroll
-    for (int t = 0; t < R; ++t) {
-      w_cur[t] = w_nxt[t];
-      s_cur[t] = s_nxt[t];
-    }
+  for (int d = 0; d < D; ++d) {
+    load(lp, raw[d]);
+    lp.advance(nws, stride);
   }
 
-  // K-split reduction through LDS, then the epilogue on wave 0.
-  // Accumulator layout: lane (li, g) holds column n = n_base + 16t + li and
-  // rows m = 4g + r, r = 0..3.
-  if (KS > 1) {
-    __shared__ f32x4 red[KS][R][64];
+  if constexpr (ACT_LDS) {
+    // rows 0 .. M-1 of A, zero beyond K, then (FP4) the zero row; issued
+    // after the first weight loads so both memory latencies overlap, eight
+    // loads per thread in flight before their LDS writes.  Chunk indices past
+    // the end are clamped to the last chunk (same data, same address), so
+    // every load is consumed by a store and none stays in flight into the
+    // main loop.
+    const uint32_t cpr = chunks_per_row.d;  // lds_pitch / 16
+    const uint32_t nload = static_cast<uint32_t>(M) * cpr;
+    const uint32_t nall = FP8 ? nload : nload + cpr;
+    constexpr uint32_t kStep = 64u * kWaves;
+    for (uint32_t q0 = threadIdx.x; q0 < nall; q0 += 8u * kStep) {
+      u32x4 v[8];
 #pragma unroll
-    for (int t = 0; t < R; ++t) red[wave][t][lane] = acc[t];
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int t = 0; t < R; ++t) {
-      f32x4 s = red[0][t][lane];
-#pragma unroll
-      for (int v = 1; v < KS; ++v) s += red[v][t][lane];
-      acc[t] = s;
-    }
-  }
-  const float ws2 = *ws2p;
-#pragma unroll
-  for (int t = 0; t < R; ++t) {
-    const int n = n_base + 16 * t + li;
-    if (!n_ok[t]) continue;
-    const float b = bias ? static_cast<float>(bias[n]) : 0.0f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 4 * g + r;
-      if (m < M) Y[static_cast<size_t>(m) * N + n] = round_to<T>(fmaf(acc[t][r], ws2, b));
-    }
-  }
-}
-
-// --------------------------------------------------------------------- FP8
-
-template <typename T, int R, int KS>
-__global__ __launch_bounds__(64 * KS) void fp8_gemv_kernel(
-    const T* __restrict__ A, const uint8_t* __restrict__ B, const float* __restrict__ bscale,
-    const T* __restrict__ bias, T* __restrict__ Y, int M, int N, int K, int bs, int cols) {
-  typedef ActTraits<T> Tr;
-  typedef typename Tr::vec8 V;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int li = lane & 15, g = lane >> 4;
-  const int n_base = blockIdx.x * (16 * R);
-  const int NW = K >> 7;  // 128-k windows (K % 128 == 0)
-
-  const bool m_ok = li < M;
-  const T* arow = A + static_cast<size_t>(m_ok ? li : 0) * K;
-  const uint8_t* brow[R];
-  const float* srow[R];
-  bool n_ok[R];
-#pragma unroll
-  for (int t = 0; t < R; ++t) {
-    const int n = n_base + 16 * t + li;
-    n_ok[t] = n < N;
-    const size_t nn = n_ok[t] ? n : 0;
-    brow[t] = B + nn * K;
-    srow[t] = bscale + nn * cols;
-  }
-  f32x4 acc[R];
-#pragma unroll
-  for (int t = 0; t < R; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  V a_cur[4];
-  u32x4 w_cur[R][2];
-  float s_cur[R];
-  auto fetch = [&](int win, V (&a)[4], u32x4 (&wq)[R][2], float (&sc)[R]) {
-    const int c = 4 * win + g;
-    const bool ok = win < NW;
-    load_act<T, V>(arow, c, m_ok && ok, a);
-    // every k of window `win` lies in scale column min(128 win / bs, cols - 1)
-    const int col = ok ? min((128 * win) / bs, cols - 1) : 0;
-#pragma unroll
-    for (int t = 0; t < R; ++t) {
-      if (n_ok[t] && ok) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(brow[t] + 32 * c);
-        wq[t][0] = p[0];
-        wq[t][1] = p[1];
-        sc[t] = srow[t][col];
-      } else {
-        wq[t][0] = u32x4{0u, 0u, 0u, 0u};
-        wq[t][1] = u32x4{0u, 0u, 0u, 0u};
-        sc[t] = 0.0f;
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t q = min(q0 + i * kStep, nall - 1u);
+        const uint32_t row = fdiv(q, chunks_per_row), col = q - row * cpr;
+        const uint32_t off = (q < nload && col * 8u < static_cast<uint32_t>(K))
+                                 ? row * static_cast<uint32_t>(K) * 2u + col * 16u
+                                 : kOutOfRange;
+        v[i] = buf_load_b128(a_rsrc, off);
       }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<u32x4*>(a_lds + 16u * min(q0 + i * kStep, nall - 1u)) = v[i];
     }
-  };
-  int w = wave;
-  fetch(w, a_cur, w_cur, s_cur);
-  for (; w < NW; w += KS) {
-    V a_nxt[4];
-    u32x4 w_nxt[R][2];
-    float s_nxt[R];
-    fetch(w + KS, a_nxt, w_nxt, s_nxt);
-#pragma unroll
-    for (int t = 0; t < R; ++t) {
-      const V b0 = Tr::decode8_fp8(w_cur[t][0].x, w_cur[t][0].y);
-      const V b1 = Tr::decode8_fp8(w_cur[t][0].z, w_cur[t][0].w);
-      const V b2 = Tr::decode8_fp8(w_cur[t][1].x, w_cur[t][1].y);
-      const V b3 = Tr::decode8_fp8(w_cur[t][1].z, w_cur[t][1].w);
-      f32x4 blk = f32x4{0.f, 0.f, 0.f, 0.f};
-      blk = Tr::mfma(a_cur[0], b0, blk);
-      blk = Tr::mfma(a_cur[1], b1, blk);
-      blk = Tr::mfma(a_cur[2], b2, blk);
-      blk = Tr::mfma(a_cur[3], b3, blk);
-      // lane holds column n (one scale) and rows 4g..4g+3
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(blk[r], s_cur[t], acc[t][r]);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a_cur[i] = a_nxt[i];
-#pragma unroll
-    for (int t = 0; t < R; ++t) {
-      w_cur[t][0] = w_nxt[t][0];
-      w_cur[t][1] = w_nxt[t][1];
-      s_cur[t] = s_nxt[t];
-    }
-  }
-  if (KS > 1) {
-    __shared__ f32x4 red[KS][R][64];
-#pragma unroll
-    for (int t = 0; t < R; ++t) red[wave][t][lane] = acc[t];
     __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int t = 0; t < R; ++t) {
-      f32x4 s = red[0][t][lane];
-#pragma unroll
-      for (int v = 1; v < KS; ++v) s += red[v][t][lane];
-      acc[t] = s;
-    }
   }
+
+  // multiply one window (and finish its tile group after the last window)
+  auto consume = [&](const RawT& r) {
+      const int w = min(ks * nws + cp.j, NW - 1);  // windows past NW meet zero weights
+      if constexpr (FP8) {
+        typedef ActTraits<T> Tr;
+        typedef typename Tr::vec8 V;
+        V a[4];
+        if constexpr (ACT_LDS) {
+          const unsigned char* q = a_lds + a_off[0] + 64u * (4 * w + g);
 #pragma unroll
-  for (int t = 0; t < R; ++t) {
-    const int n = n_base + 16 * t + li;
-    if (!n_ok[t]) continue;
-    const float b = bias ? static_cast<float>(bias[n]) : 0.0f;
+          for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const V*>(q + 16u * i);
+        } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 4 * g + r;
-      if (m < M) Y[static_cast<size_t>(m) * N + n] = round_to<T>(acc[t][r] + b);
+          for (int i = 0; i < 4; ++i) a[i] = __builtin_bit_cast(V, r.a[i]);
+        }
+        f32x4 blk = f32x4{0.f, 0.f, 0.f, 0.f};
+        blk = Tr::mfma(a[0], Tr::decode8_fp8(r.w0.x, r.w0.y), blk);
+        blk = Tr::mfma(a[1], Tr::decode8_fp8(r.w0.z, r.w0.w), blk);
+        blk = Tr::mfma(a[2], Tr::decode8_fp8(r.w1.x, r.w1.y), blk);
+        blk = Tr::mfma(a[3], Tr::decode8_fp8(r.w1.z, r.w1.w), blk);
+        // lane holds column n (one scale) and rows 4g .. 4g + 3
+#pragma unroll
+        for (int i = 0; i < R; ++i) acc[i] = fmaf(blk[i], r.s, acc[i]);
+      } else {
+        typedef Mfma16<T> Mf;
+        typedef typename Mf::vec4 V4;
+        // activations of the lane: 4 x 16 bytes per row half, chunk i holds
+        // k 32g + 8i .. + 7 of the window (set i / 2, pieces 2 (i % 2), + 1)
+        u32x4 av[R][4];
+#pragma unroll
+        for (int h = 0; h < R; ++h) {
+          if constexpr (ACT_LDS) {
+            const unsigned char* q = a_lds + a_off[h] + 256u * w;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) av[h][i] = *reinterpret_cast<const u32x4*>(q + 16u * i);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) av[h][i] = r.a[4 * h + i];
+          }
+        }
+        // weights of set s (block 2g + s): dwords 2s, 2s + 1; piece p: dword
+        // 2s + p / 2, half p % 2
+        V4 bw[2][4];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          bw[s][0] = Mf::template decode4<0>(r.w[2 * s]);
+          bw[s][1] = Mf::template decode4<1>(r.w[2 * s]);
+          bw[s][2] = Mf::template decode4<0>(r.w[2 * s + 1]);
+          bw[s][3] = Mf::template decode4<1>(r.w[2 * s + 1]);
+        }
+        const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 d[R][2];
+#pragma unroll
+        for (int h = 0; h < R; ++h)
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            d[h][s] = Mf::mfma(half_of<V4, 0>(av[h][2 * s]), bw[s][0], zero);
+            d[h][s] = Mf::mfma(half_of<V4, 1>(av[h][2 * s]), bw[s][1], d[h][s]);
+            d[h][s] = Mf::mfma(half_of<V4, 0>(av[h][2 * s + 1]), bw[s][2], d[h][s]);
+            d[h][s] = Mf::mfma(half_of<V4, 1>(av[h][2 * s + 1]), bw[s][3], d[h][s]);
+          }
+        // result row r of set s is block 2r + s: scale byte 2r + s
+        const f32x2 s01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(r.s.x), false);
+        const f32x2 s23 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(r.s.x), true);
+        const f32x2 s45 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(r.s.y), false);
+        const f32x2 s67 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(r.s.y), true);
+        const float sc[8] = {s01.x, s01.y, s23.x, s23.y, s45.x, s45.y, s67.x, s67.y};
+#pragma unroll
+        for (int h = 0; h < R; ++h)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) acc[h] = fmaf(d[h][s][rr], sc[2 * rr + s], acc[h]);
+      }
+      if (cp.j == nws - 1) {
+        // end of this tile group: reduce the K split, then the epilogue
+        // (uniform across the workgroup: every wave has the same sequence)
+        if (KS > 1) {
+          red[wave * 64 + lane] = acc;
+          __syncthreads();
+          if (ks == 0) {
+#pragma unroll
+            for (int v = 1; v < KS; ++v) acc += red[(wave + v) * 64 + lane];
+          }
+          __syncthreads();
+        }
+        if (ks == 0) {
+          const int n = 16 * (cp.tg * TPW + tw) + li;
+          if (n < N) {
+            // zero bits when there is no bias (zero-length buffer)
+            const float b = static_cast<float>(__builtin_bit_cast(T, static_cast<uint16_t>(r.bias)));
+            if constexpr (FP8) {
+#pragma unroll
+              for (int r4 = 0; r4 < 4; ++r4) {
+                const int m = 4 * g + r4;
+                if (m < M) Y[static_cast<size_t>(m) * N + n] = round_to<T>(acc[r4] + b);
+              }
+            } else {
+#pragma unroll
+              for (int h = 0; h < R; ++h) {
+                const int m = g + 4 * h;
+                if (m < M) Y[static_cast<size_t>(m) * N + n] = round_to<T>(fmaf(acc[h], ws2, b));
+              }
+            }
+          }
+        }
+        acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      cp.advance(nws, stride);
+  };
+
+  // Window f sits in slot f % S.  Loads run ahead unconditionally (past the
+  // end they are out of range), so every step waits only for its own, oldest,
+  // loads; steps past the end of the sequence skip the multiply (the
+  // condition is uniform across the workgroup).
+  for (int f0 = 0; f0 < total; f0 += S) {
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      load(lp, raw[(u + D) % S]);
+      lp.advance(nws, stride);
+      if (f0 + u < total) consume(raw[u]);
     }
   }
 }
 
 // --------------------------------------------------------------------- launch
 
-// Launch shape: about 2048+ waves in flight (8 per CU on 256 CUs) so the HBM
-// pipe stays full, KS limited by the number of windows.
-struct GemvShape {
-  int R, KS;
+constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
+
+// Pipeline depth: with activations in LDS a window's registers are only the
+// weights and scales, so more windows fit in flight.
+template <bool FP8, bool ACT_LDS>
+constexpr int depth() {
+  return ACT_LDS ? (FP8 ? 5 : 7) : 3;
+}
+
+size_t lds_bytes(int KS, bool act_lds, bool fp8, int M, int NW) {
+  const size_t rows = static_cast<size_t>(M) + (fp8 ? 0 : 1);  // FP4: plus the zero row
+  return (KS > 1 ? kWaves * 64 * sizeof(f32x4) : 0) +
+         (act_lds ? rows * (static_cast<size_t>(NW) * 256 + 16) : 0);
+}
+
+int num_cus() {
+  static int cus = -1;
+  if (cus < 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
+      v = 256;
+    cus = v;
+  }
+  return cus;
+}
+
+template <typename T, int KS, bool FP8, bool ACT_LDS, int R>
+constexpr auto kernel_ptr() {
+  return &gemv_kernel<T, KS, FP8, ACT_LDS, R, depth<FP8, ACT_LDS>()>;
+}
+
+// Dynamic LDS above 64 KiB must be allowed per kernel, once.
+template <typename T, int KS, bool FP8, bool ACT_LDS, int R>
+void allow_lds() {
+  static bool done = false;
+  if (!done) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel_ptr<T, KS, FP8, ACT_LDS, R>()),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kMaxLds));
+    done = true;
+  }
+}
+
+// Resident workgroups per CU for a kernel variant and LDS size (the variant
+// with the most row registers is queried).
+template <typename T, int KS, bool FP8, bool ACT_LDS>
+int wg_per_cu(size_t lds) {
+  constexpr int R = FP8 ? 4 : 2;
+  allow_lds<T, KS, FP8, ACT_LDS, R>();
+  int v = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kernel_ptr<T, KS, FP8, ACT_LDS, R>(), 64 * kWaves,
+                                                   lds) != hipSuccess ||
+      v < 1)
+    v = 1;
+  return v;
+}
+
+template <typename T, bool FP8, bool ACT_LDS>
+int slots_for(int KS, int M, int NW) {
+  const size_t lds = lds_bytes(KS, ACT_LDS, FP8, M, NW);
+  int per = 1;
+  switch (KS) {
+    case 1: per = wg_per_cu<T, 1, FP8, ACT_LDS>(lds); break;
+    case 2: per = wg_per_cu<T, 2, FP8, ACT_LDS>(lds); break;
+    case 4: per = wg_per_cu<T, 4, FP8, ACT_LDS>(lds); break;
+    default: per = wg_per_cu<T, 8, FP8, ACT_LDS>(lds); break;
+  }
+  return num_cus() * per;
+}
+
+struct Plan {
+  int KS, grid, nws;
+  bool act_lds;
 };
 
-GemvShape pick_shape(int64_t N, int64_t windows) {
+// Launch plan: for each K split (1, 2, 4, 8 waves per tile) and activation
+// mode, the serial work of one wave slot is rounds x windows-per-wave, where
+// rounds = ceil(tile groups / resident workgroups); fewer workgroups than CUs
+// leave HBM channels idle, which the cost scales up by.  The cheapest plan
+// wins; ties go to the smaller split (fewer LDS reductions).
+template <typename T, bool FP8>
+Plan plan(int64_t N, int M, int NW) {
   const int64_t tiles = (N + 15) / 16;
-  GemvShape s{1, 1};
-  if (tiles >= 4096) s.R = 2;
-  const int64_t groups = (tiles + s.R - 1) / s.R;
-  while (s.KS < 8 && groups * s.KS < 2048 && windows >= 2 * s.KS * 2) s.KS *= 2;
-  return s;
+  const int cus = num_cus();
+  Plan best{1, 1, NW, false};
+  double best_cost = 1e300;
+  for (int mode = 0; mode < 2; ++mode) {
+    for (int ks = 1; ks <= 8; ks <<= 1) {
+      if (ks > 1 && NW < 2 * ks) continue;  // at least two windows per wave
+      if (mode == 1 && lds_bytes(ks, true, FP8, M, NW) > kMaxLds) continue;
+      const int64_t ntg = (tiles + kWaves / ks - 1) / (kWaves / ks);
+      const int64_t slots = mode ? slots_for<T, FP8, true>(ks, M, NW) : slots_for<T, FP8, false>(ks, M, NW);
+      const int nws = (NW + ks - 1) / ks;
+      const int64_t rounds = (ntg + slots - 1) / slots;
+      double cost = static_cast<double>(rounds) * nws;
+      if (ntg < cus) cost *= static_cast<double>(cus) / ntg;
+      if (cost < best_cost - 1e-9) {
+        best_cost = cost;
+        best = Plan{ks, static_cast<int>(ntg < slots ? ntg : slots), nws, mode == 1};
+      }
+    }
+  }
+  return best;
 }
 
-template <typename T, int R, int KS>
-void launch_fp4_t(const MatmulArgs& a) {
-  const int grid = static_cast<int>((a.N + 16 * R - 1) / (16 * R));
-  hipLaunchKernelGGL((fp4_gemv_kernel<T, R, KS>), dim3(grid), dim3(64 * KS), 0,
-                     static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.A), a.B,
-                     static_cast<const uint8_t*>(a.scales), a.ws2, static_cast<const T*>(a.bias),
-                     static_cast<T*>(a.Y), static_cast<int>(a.M), static_cast<int>(a.N),
-                     static_cast<int>(a.K));
-}
-
-template <typename T, int R, int KS>
-void launch_fp8_t(const MatmulArgs& a) {
-  const int grid = static_cast<int>((a.N + 16 * R - 1) / (16 * R));
-  hipLaunchKernelGGL((fp8_gemv_kernel<T, R, KS>), dim3(grid), dim3(64 * KS), 0,
-                     static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.A), a.B,
-                     static_cast<const float*>(a.scales), static_cast<const T*>(a.bias),
-                     static_cast<T*>(a.Y), static_cast<int>(a.M), static_cast<int>(a.N),
-                     static_cast<int>(a.K), static_cast<int>(a.block_size),
-                     static_cast<int>(a.scale_cols));
+template <typename T, int KS, bool FP8, bool LDS>
+void launch_v(const MatmulArgs& a, const Plan& p, int R, size_t lds, FastDiv wpb, FastDiv cpr, int tiles) {
+  hipStream_t s = static_cast<hipStream_t>(a.stream);
+#define FP4W_GEMV_LAUNCH(R_)                                                                           \
+  allow_lds<T, KS, FP8, LDS, R_>();                                                                    \
+  hipLaunchKernelGGL((gemv_kernel<T, KS, FP8, LDS, R_, depth<FP8, LDS>()>), dim3(p.grid),              \
+                     dim3(64 * kWaves), lds, s, static_cast<const T*>(a.A), a.B, a.scales, a.ws2,      \
+                     static_cast<const T*>(a.bias), static_cast<T*>(a.Y), static_cast<int>(a.M),       \
+                     static_cast<int>(a.N), static_cast<int>(a.K), static_cast<int>(a.scale_cols), wpb, \
+                     cpr, tiles, p.nws)
+  if (R == 1) {
+    FP4W_GEMV_LAUNCH(1);
+  } else if (R == 2) {
+    FP4W_GEMV_LAUNCH(2);
+  } else if constexpr (FP8) {
+    FP4W_GEMV_LAUNCH(4);
+  }
+#undef FP4W_GEMV_LAUNCH
 }
 
 template <typename T, bool FP8>
-void launch_any(const MatmulArgs& a, GemvShape s) {
-#define FP4W_GEMV_CASE(R_, KS_)                                        \
-  if (s.R == R_ && s.KS == KS_) {                                      \
-    if (FP8) launch_fp8_t<T, R_, KS_>(a); else launch_fp4_t<T, R_, KS_>(a); \
-    return;                                                            \
+int launch_t(const MatmulArgs& a) {
+  // buffer offsets are 32-bit: one 16-column tile and the activations must fit
+  if (a.N > 0x7fffffff - 16 || a.K > (int64_t(1) << 26) || a.M * a.K * 2 >= (int64_t(1) << 31))
+    return -1;
+  const int M = static_cast<int>(a.M);
+  const int NW = static_cast<int>(a.K / 128);
+  const Plan p = plan<T, FP8>(a.N, M, NW);
+  const int tiles = static_cast<int>((a.N + 15) / 16);
+  const size_t lds = lds_bytes(p.KS, p.act_lds, FP8, M, NW);
+  // FP8: result rows a lane scales; FP4: row halves
+  const int R = FP8 ? (M >= 3 ? 4 : M) : (M > 4 ? 2 : 1);
+  const FastDiv wpb = make_fastdiv(FP8 ? static_cast<uint32_t>(a.block_size / 128) : 1u);
+  const FastDiv cpr = make_fastdiv(static_cast<uint32_t>(NW) * 16u + 1u);  // 16-byte chunks per LDS row
+#define FP4W_GEMV_KS(LDS_)                                                   \
+  switch (p.KS) {                                                            \
+    case 1: launch_v<T, 1, FP8, LDS_>(a, p, R, lds, wpb, cpr, tiles); break;  \
+    case 2: launch_v<T, 2, FP8, LDS_>(a, p, R, lds, wpb, cpr, tiles); break;  \
+    case 4: launch_v<T, 4, FP8, LDS_>(a, p, R, lds, wpb, cpr, tiles); break;  \
+    default: launch_v<T, 8, FP8, LDS_>(a, p, R, lds, wpb, cpr, tiles); break; \
   }
-  FP4W_GEMV_CASE(1, 1) FP4W_GEMV_CASE(1, 2) FP4W_GEMV_CASE(1, 4) FP4W_GEMV_CASE(1, 8)
-  FP4W_GEMV_CASE(2, 1) FP4W_GEMV_CASE(2, 2) FP4W_GEMV_CASE(2, 4) FP4W_GEMV_CASE(2, 8)
-#undef FP4W_GEMV_CASE
+  if (p.act_lds) {
+    FP4W_GEMV_KS(true)
+  } else {
+    FP4W_GEMV_KS(false)
+  }
+#undef FP4W_GEMV_KS
+  return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace
 
 int launch_fp4_gemv(const MatmulArgs& a) {
-  if (a.N > 0x7fffffff || a.K > 0x7fffffff || a.N * (a.K / 2) > (int64_t(1) << 40)) return -1;
-  const GemvShape s = pick_shape(a.N, (a.K / 32 + 3) / 4);
-  if (a.act == Act::BF16) launch_any<__bf16, false>(a, s);
-  else launch_any<_Float16, false>(a, s);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  return a.act == Act::BF16 ? launch_t<__bf16, false>(a) : launch_t<_Float16, false>(a);
 }
 
 int launch_fp8_gemv(const MatmulArgs& a) {
-  if (a.N > 0x7fffffff || a.K > 0x7fffffff) return -1;
-  const GemvShape s = pick_shape(a.N, a.K / 128);
-  if (a.act == Act::BF16) launch_any<__bf16, true>(a, s);
-  else launch_any<_Float16, true>(a, s);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  return a.act == Act::BF16 ? launch_t<__bf16, true>(a) : launch_t<_Float16, true>(a);
 }
 
 }  // namespace fp4w

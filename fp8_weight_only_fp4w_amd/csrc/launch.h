@@ -36,8 +36,8 @@ struct DequantArgs {
 // an error at enqueue time.  Preconditions (checked by the dispatcher, never
 // by the launcher) are stated next to each.
 
-// 1 <= M <= 8, block_size == 16, K % 32 == 0, scale_cols == K / 16,
-// A / B 16-byte aligned, scales and bias 2-byte aligned.
+// 1 <= M <= 8, block_size == 16, K % 128 == 0, scale_cols == K / 16,
+// A / B 16-byte aligned, scales 4-byte aligned, bias 2-byte aligned.
 int launch_fp4_gemv(const MatmulArgs& a);
 // M >= 1, block_size == 16, K % 64 == 0, scale_cols == K / 16,
 // A 16-byte aligned, B 8-byte aligned.
