@@ -46,6 +46,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "device.h"
 #include "launch.h"
 
@@ -54,29 +56,35 @@ namespace {
 
 constexpr int kWaves = 8;  // waves per workgroup (KS x TPW)
 
-// Raw data of one window for one lane.  FP4: 16 weight bytes, the 8 E4M3
-// scale bytes of the lane's column for the window's 8 blocks, and (when they
-// come from L2) the lane's 64 activation bytes per row half.  FP8: 32 weight
-// bytes, the window's FP32 scale, the activations.  The bias bits of the
-// lane's column ride along with the last window of each tile group, so the
-// epilogue never waits on a late load (loads retire in order: waiting on one
-// issued after the prefetches would drain them all).
+// Raw data of one window for one lane.  FP4: 16 weight bytes; FP8: 32.  The
+// block scales of a tile are read in 64-byte pieces per column (one request
+// per row instead of one per row and window): the piece rides along with the
+// first window of each group of kScaleWin windows and is parked in a per-wave
+// LDS slice, from which every window of the group reads its scales.  The bias
+// bits of the lane's column ride along with the first window of a tile.
+// Activations ride along only when they come from L2 (ACT_REG).
 template <bool FP8, bool ACT_REG, int R>
 struct Raw;
 template <bool ACT_REG, int R>
 struct Raw<false, ACT_REG, R> {
   u32x4 w;
-  u32x2 s;
+  u32x4 sc;
   uint32_t bias;
-  u32x4 a[ACT_REG ? 4 * R : 1];
+  u32x4 a[ACT_REG ? 4 * R : 1];  // 64 activation bytes per row half
 };
 template <bool ACT_REG, int R>
 struct Raw<true, ACT_REG, R> {
   u32x4 w0, w1;
-  float s;
+  u32x4 sc;
   uint32_t bias;
-  u32x4 a[ACT_REG ? 4 : 1];  // 4 x 8 activations (k 32c .. 32c + 31)
+  u32x4 a[ACT_REG ? 4 : 1];  // 4 x 8 activations
 };
+
+// Windows per 64-byte scale piece: FP4 has 8 E4M3 bytes per window, FP8 one
+// FP32 scale per 128-k window (or per several windows: block_size % 128 == 0,
+// and 16 consecutive columns always cover 16 consecutive windows).
+template <bool FP8>
+constexpr int kScaleWin = FP8 ? 16 : 8;
 
 // Position of a wave in its flat window sequence: tile group and window.
 struct Pos {
@@ -103,6 +111,9 @@ __device__ __forceinline__ V4 half_of(u32x4 v) {
 // Either way the load consumed next is always the oldest one in flight.
 // R: FP4 - row halves (1: M <= 4, 2: M <= 8); FP8 - result rows a lane
 // scales (1, 2 or 4).  D: windows in flight ahead of the multiply.
+//
+// LDS: [kWaves][1 KiB] per-wave slices (scale pieces, and the K-split
+// reduction at the end of a tile), then the activation rows.
 template <typename T, int KS, bool FP8, bool ACT_LDS, int R, int D>
 __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
     const T* __restrict__ A, const uint8_t* __restrict__ B, const void* __restrict__ scales,
@@ -111,6 +122,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
   constexpr bool ACT_REG = !ACT_LDS;
   constexpr int TPW = kWaves / KS;
   constexpr int S = D + 1;  // register slots of the pipeline
+  constexpr int SW = kScaleWin<FP8>;
   typedef Raw<FP8, ACT_REG, R> RawT;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int lane = threadIdx.x & 63;
@@ -129,8 +141,9 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
   const uint32_t srow_bytes = FP8 ? static_cast<uint32_t>(cols) * 4u : static_cast<uint32_t>(cols);
   const float ws2 = FP8 ? 1.0f : *ws2p;  // one scalar load, kept in a register
 
-  f32x4* red = reinterpret_cast<f32x4*>(smem);  // [kWaves][64] when KS > 1
-  unsigned char* a_lds = smem + (KS > 1 ? kWaves * 64 * sizeof(f32x4) : 0);
+  f32x4* red = reinterpret_cast<f32x4*>(smem);       // [kWaves][64]
+  unsigned char* slice = smem + 1024 * wave;          // this wave's 1 KiB
+  unsigned char* a_lds = smem + kWaves * 1024;
   const uint32_t lds_pitch = static_cast<uint32_t>(NW) * 256u + 16u;  // bytes per LDS row of A
   const uint32_t a_bytes = static_cast<uint32_t>(M) * static_cast<uint32_t>(K) * 2u;
   const rsrc_t a_rsrc = make_rsrc(A, a_bytes);
@@ -154,7 +167,16 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
         a_off[h] = valid ? static_cast<uint32_t>(m) * static_cast<uint32_t>(K) * 2u + 64u * g : kOutOfRange;
     }
   }
+  // scale column of window w (FP8; windows past NW are clamped)
+  auto scol = [&](int w) {
+    return min(fdiv(static_cast<uint32_t>(min(w, NW - 1)), win_per_block), static_cast<uint32_t>(cols - 1));
+  };
 
+  // Window mapping.  FP4: lane group g loads the 32 k of chunk c = 4w + g
+  // (bytes 64w + 16g of its column: one wave instruction reads 64 contiguous
+  // bytes of each of 16 rows).  FP8: lane group g loads k 128w + 16g .. + 15
+  // and 128w + 64 + 16g .. + 15 (two instructions, each 64 contiguous bytes
+  // per row).
   auto load = [&](Pos p, RawT& r) {
     const int t = p.tg * TPW + tw;
     const int rows = max(0, min(16, N - 16 * t));
@@ -162,27 +184,30 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
     const rsrc_t br = make_rsrc(B + n0 * row_bytes, rows * row_bytes);
     const rsrc_t sr = make_rsrc(static_cast<const uint8_t*>(scales) + n0 * srow_bytes, rows * srow_bytes);
     const rsrc_t biasr = make_rsrc(bias + n0, bias ? rows * 2u : 0u);
-    r.bias = buf_load_u16(biasr, p.j == nws - 1 ? 2u * li : kOutOfRange);
+    // bias and scale pieces are only requested for the windows that carry
+    // them (uniform branches; an out-of-range request would still occupy the
+    // load pipeline for all 64 lanes)
+    if (p.j == 0) r.bias = buf_load_u16(biasr, 2u * li);
     const int w = ks * nws + p.j;
     const bool ok = w < NW;
-    const int c = 4 * w + g;
+    const bool piece = ok && p.j % SW == 0;
     if constexpr (FP8) {
-      const uint32_t off = ok ? li * row_bytes + 32u * c : kOutOfRange;
+      const uint32_t off = ok ? li * row_bytes + 128u * w + 16u * g : kOutOfRange;
       r.w0 = buf_load_b128(br, off);
-      r.w1 = buf_load_b128(br, off + 16u);
-      // a window lies inside one scale column
-      const uint32_t col = min(fdiv(static_cast<uint32_t>(w), win_per_block), static_cast<uint32_t>(cols - 1));
-      r.s = __builtin_bit_cast(float, buf_load_b32(sr, ok ? li * srow_bytes + 4u * col : kOutOfRange));
+      r.w1 = buf_load_b128(br, off + 64u);
+      // FP32 scales of columns scol(w) .. + 15 (bytes past the row are never used)
+      if (piece) r.sc = buf_load_b128(sr, li * srow_bytes + 4u * scol(w) + 16u * g);
       if constexpr (ACT_REG) {
-        const uint32_t aoff = ok ? a_off[0] + 64u * c : kOutOfRange;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r.a[i] = buf_load_b128(a_rsrc, aoff + 16u * i);
+        const uint32_t aoff = ok ? a_off[0] + 256u * w + 32u * g : kOutOfRange;
+        r.a[0] = buf_load_b128(a_rsrc, aoff);
+        r.a[1] = buf_load_b128(a_rsrc, aoff + 16u);
+        r.a[2] = buf_load_b128(a_rsrc, aoff + 128u);
+        r.a[3] = buf_load_b128(a_rsrc, aoff + 144u);
       }
     } else {
-      r.w = buf_load_b128(br, ok ? li * row_bytes + 16u * c : kOutOfRange);
-      // the 8 scale bytes of the window's blocks 8w .. 8w + 7 in one 8-byte
-      // load, dword aligned and inside the row because K % 128 == 0
-      r.s = buf_load_b64(sr, ok ? li * srow_bytes + 8u * w : kOutOfRange);
+      r.w = buf_load_b128(br, ok ? li * row_bytes + 64u * w + 16u * g : kOutOfRange);
+      // E4M3 scales of windows w .. w + 7 (bytes past the row are never used)
+      if (piece) r.sc = buf_load_b128(sr, li * srow_bytes + 8u * w + 16u * g);
       if constexpr (ACT_REG) {
 #pragma unroll
         for (int h = 0; h < R; ++h) {
@@ -196,154 +221,180 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
   };
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint32_t tbias = 0;  // bias bits of the lane's column, current tile
   RawT raw[S];
   Pos lp{static_cast<int>(blockIdx.x), 0};  // next window to load
   Pos cp{static_cast<int>(blockIdx.x), 0};  // window being multiplied
 
-#pragma unroll
-  for (int d = 0; d < D; ++d) {
-    load(lp, raw[d]);
-    lp.advance(nws, stride);
-  }
-
   if constexpr (ACT_LDS) {
-    // rows 0 .. M-1 of A, zero beyond K, then (FP4) the zero row; issued
-    // after the first weight loads so both memory latencies overlap, eight
-    // loads per thread in flight before their LDS writes.  Chunk indices past
-    // the end are clamped to the last chunk (same data, same address), so
-    // every load is consumed by a store and none stays in flight into the
-    // main loop.
+    // Rows 0 .. M-1 of A, zero beyond K, then (FP4) the zero row.  The first
+    // eight 16-byte chunks per thread are requested before the weights, so
+    // their stores wait for them alone (loads complete in order); any further
+    // chunks (large M x K) follow the weight requests.  Chunk indices past the
+    // end are clamped to the last chunk (same data, same address), so every
+    // load is consumed by a store and none stays in flight into the main loop.
     const uint32_t cpr = chunks_per_row.d;  // lds_pitch / 16
     const uint32_t nload = static_cast<uint32_t>(M) * cpr;
     const uint32_t nall = FP8 ? nload : nload + cpr;
     constexpr uint32_t kStep = 64u * kWaves;
-    for (uint32_t q0 = threadIdx.x; q0 < nall; q0 += 8u * kStep) {
-      u32x4 v[8];
+    auto fill_load = [&](uint32_t q0, u32x4 (&v)[8]) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t q = min(q0 + i * kStep, nall - 1u);
+        const uint32_t q = min(q0 + i * kStep, nload - 1u);
         const uint32_t row = fdiv(q, chunks_per_row), col = q - row * cpr;
-        const uint32_t off = (q < nload && col * 8u < static_cast<uint32_t>(K))
-                                 ? row * static_cast<uint32_t>(K) * 2u + col * 16u
-                                 : kOutOfRange;
+        const uint32_t off = col * 8u < static_cast<uint32_t>(K) ? row * static_cast<uint32_t>(K) * 2u + col * 16u
+                                                                : kOutOfRange;
         v[i] = buf_load_b128(a_rsrc, off);
       }
+    };
+    auto fill_store = [&](uint32_t q0, const u32x4 (&v)[8]) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<u32x4*>(a_lds + 16u * min(q0 + i * kStep, nall - 1u)) = v[i];
+        *reinterpret_cast<u32x4*>(a_lds + 16u * min(q0 + i * kStep, nload - 1u)) = v[i];
+    };
+    u32x4 v[8];
+    fill_load(threadIdx.x, v);
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      load(lp, raw[d]);
+      lp.advance(nws, stride);
     }
+    fill_store(threadIdx.x, v);
+    for (uint32_t q0 = threadIdx.x + 8u * kStep; q0 < nload; q0 += 8u * kStep) {
+      fill_load(q0, v);
+      fill_store(q0, v);
+    }
+    for (uint32_t q = nload + threadIdx.x; q < nall; q += kStep)
+      *reinterpret_cast<u32x4*>(a_lds + 16u * q) = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
+  } else {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      load(lp, raw[d]);
+      lp.advance(nws, stride);
+    }
   }
 
   // multiply one window (and finish its tile group after the last window)
   auto consume = [&](const RawT& r) {
-      const int w = min(ks * nws + cp.j, NW - 1);  // windows past NW meet zero weights
-      if constexpr (FP8) {
-        typedef ActTraits<T> Tr;
-        typedef typename Tr::vec8 V;
-        V a[4];
-        if constexpr (ACT_LDS) {
-          const unsigned char* q = a_lds + a_off[0] + 64u * (4 * w + g);
+    const int j = cp.j;
+    const int w = min(ks * nws + j, NW - 1);  // windows past NW meet zero weights
+    if (j % SW == 0) *reinterpret_cast<u32x4*>(slice + 64 * li + 16 * g) = r.sc;
+    if (j == 0) tbias = r.bias;
+    if constexpr (FP8) {
+      typedef ActTraits<T> Tr;
+      typedef typename Tr::vec8 V;
+      // the scale of this window's column, from the piece of the first
+      // window of its group (the column offset is at most 15)
+      const uint32_t c0 = scol(ks * nws + (j - j % SW));
+      const float sc = *reinterpret_cast<const float*>(slice + 64 * li + 4 * (scol(w) - c0));
+      V a[4];
+      if constexpr (ACT_LDS) {
+        const unsigned char* q = a_lds + a_off[0] + 256u * w + 32u * g;
+        a[0] = *reinterpret_cast<const V*>(q);
+        a[1] = *reinterpret_cast<const V*>(q + 16u);
+        a[2] = *reinterpret_cast<const V*>(q + 128u);
+        a[3] = *reinterpret_cast<const V*>(q + 144u);
+      } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const V*>(q + 16u * i);
+        for (int i = 0; i < 4; ++i) a[i] = __builtin_bit_cast(V, r.a[i]);
+      }
+      f32x4 blk = f32x4{0.f, 0.f, 0.f, 0.f};
+      blk = Tr::mfma(a[0], Tr::decode8_fp8(r.w0.x, r.w0.y), blk);
+      blk = Tr::mfma(a[1], Tr::decode8_fp8(r.w0.z, r.w0.w), blk);
+      blk = Tr::mfma(a[2], Tr::decode8_fp8(r.w1.x, r.w1.y), blk);
+      blk = Tr::mfma(a[3], Tr::decode8_fp8(r.w1.z, r.w1.w), blk);
+      // lane holds column n (one scale) and rows 4g .. 4g + 3
+#pragma unroll
+      for (int i = 0; i < R; ++i) acc[i] = fmaf(blk[i], sc, acc[i]);
+    } else {
+      typedef Mfma16<T> Mf;
+      typedef typename Mf::vec4 V4;
+      const u32x2 sb = *reinterpret_cast<const u32x2*>(slice + 64 * li + 8 * (j % SW));
+      // activations of the lane: 4 x 16 bytes per row half, chunk i holds
+      // k 32g + 8i .. + 7 of the window (set i / 2, pieces 2 (i % 2), + 1)
+      u32x4 av[R][4];
+#pragma unroll
+      for (int h = 0; h < R; ++h) {
+        if constexpr (ACT_LDS) {
+          const unsigned char* q = a_lds + a_off[h] + 256u * w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) av[h][i] = *reinterpret_cast<const u32x4*>(q + 16u * i);
         } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) a[i] = __builtin_bit_cast(V, r.a[i]);
+          for (int i = 0; i < 4; ++i) av[h][i] = r.a[4 * h + i];
         }
-        f32x4 blk = f32x4{0.f, 0.f, 0.f, 0.f};
-        blk = Tr::mfma(a[0], Tr::decode8_fp8(r.w0.x, r.w0.y), blk);
-        blk = Tr::mfma(a[1], Tr::decode8_fp8(r.w0.z, r.w0.w), blk);
-        blk = Tr::mfma(a[2], Tr::decode8_fp8(r.w1.x, r.w1.y), blk);
-        blk = Tr::mfma(a[3], Tr::decode8_fp8(r.w1.z, r.w1.w), blk);
-        // lane holds column n (one scale) and rows 4g .. 4g + 3
+      }
+      // weights of set s (block 2g + s): dwords 2s, 2s + 1; piece p: dword
+      // 2s + p / 2, half p % 2
+      V4 bw[2][4];
 #pragma unroll
-        for (int i = 0; i < R; ++i) acc[i] = fmaf(blk[i], r.s, acc[i]);
-      } else {
-        typedef Mfma16<T> Mf;
-        typedef typename Mf::vec4 V4;
-        // activations of the lane: 4 x 16 bytes per row half, chunk i holds
-        // k 32g + 8i .. + 7 of the window (set i / 2, pieces 2 (i % 2), + 1)
-        u32x4 av[R][4];
+      for (int s = 0; s < 2; ++s) {
+        bw[s][0] = Mf::template decode4<0>(r.w[2 * s]);
+        bw[s][1] = Mf::template decode4<1>(r.w[2 * s]);
+        bw[s][2] = Mf::template decode4<0>(r.w[2 * s + 1]);
+        bw[s][3] = Mf::template decode4<1>(r.w[2 * s + 1]);
+      }
+      const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 d[R][2];
 #pragma unroll
-        for (int h = 0; h < R; ++h) {
-          if constexpr (ACT_LDS) {
-            const unsigned char* q = a_lds + a_off[h] + 256u * w;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) av[h][i] = *reinterpret_cast<const u32x4*>(q + 16u * i);
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) av[h][i] = r.a[4 * h + i];
-          }
-        }
-        // weights of set s (block 2g + s): dwords 2s, 2s + 1; piece p: dword
-        // 2s + p / 2, half p % 2
-        V4 bw[2][4];
+      for (int h = 0; h < R; ++h)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          bw[s][0] = Mf::template decode4<0>(r.w[2 * s]);
-          bw[s][1] = Mf::template decode4<1>(r.w[2 * s]);
-          bw[s][2] = Mf::template decode4<0>(r.w[2 * s + 1]);
-          bw[s][3] = Mf::template decode4<1>(r.w[2 * s + 1]);
+          d[h][s] = Mf::mfma(half_of<V4, 0>(av[h][2 * s]), bw[s][0], zero);
+          d[h][s] = Mf::mfma(half_of<V4, 1>(av[h][2 * s]), bw[s][1], d[h][s]);
+          d[h][s] = Mf::mfma(half_of<V4, 0>(av[h][2 * s + 1]), bw[s][2], d[h][s]);
+          d[h][s] = Mf::mfma(half_of<V4, 1>(av[h][2 * s + 1]), bw[s][3], d[h][s]);
         }
-        const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
-        f32x4 d[R][2];
+      // result row r of set s is block 2r + s: scale byte 2r + s
+      const f32x2 s01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb.x), false);
+      const f32x2 s23 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb.x), true);
+      const f32x2 s45 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb.y), false);
+      const f32x2 s67 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb.y), true);
+      const float sc[8] = {s01.x, s01.y, s23.x, s23.y, s45.x, s45.y, s67.x, s67.y};
 #pragma unroll
-        for (int h = 0; h < R; ++h)
+      for (int h = 0; h < R; ++h)
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            d[h][s] = Mf::mfma(half_of<V4, 0>(av[h][2 * s]), bw[s][0], zero);
-            d[h][s] = Mf::mfma(half_of<V4, 1>(av[h][2 * s]), bw[s][1], d[h][s]);
-            d[h][s] = Mf::mfma(half_of<V4, 0>(av[h][2 * s + 1]), bw[s][2], d[h][s]);
-            d[h][s] = Mf::mfma(half_of<V4, 1>(av[h][2 * s + 1]), bw[s][3], d[h][s]);
-          }
-        // result row r of set s is block 2r + s: scale byte 2r + s
-        const f32x2 s01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(r.s.x), false);
-        const f32x2 s23 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(r.s.x), true);
-        const f32x2 s45 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(r.s.y), false);
-        const f32x2 s67 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(r.s.y), true);
-        const float sc[8] = {s01.x, s01.y, s23.x, s23.y, s45.x, s45.y, s67.x, s67.y};
+        for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
-        for (int h = 0; h < R; ++h)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) acc[h] = fmaf(d[h][s][rr], sc[2 * rr + s], acc[h]);
-      }
-      if (cp.j == nws - 1) {
-        // end of this tile group: reduce the K split, then the epilogue
-        // (uniform across the workgroup: every wave has the same sequence)
-        if (KS > 1) {
-          red[wave * 64 + lane] = acc;
-          __syncthreads();
-          if (ks == 0) {
-#pragma unroll
-            for (int v = 1; v < KS; ++v) acc += red[(wave + v) * 64 + lane];
-          }
-          __syncthreads();
-        }
+          for (int s = 0; s < 2; ++s) acc[h] = fmaf(d[h][s][rr], sc[2 * rr + s], acc[h]);
+    }
+    if (j == nws - 1) {
+      // end of this tile group: reduce the K split (the slices are free: every
+      // wave has read its scales for this window), then the epilogue (uniform
+      // across the workgroup: every wave has the same sequence)
+      if (KS > 1) {
+        red[wave * 64 + lane] = acc;
+        __syncthreads();
         if (ks == 0) {
-          const int n = 16 * (cp.tg * TPW + tw) + li;
-          if (n < N) {
-            // zero bits when there is no bias (zero-length buffer)
-            const float b = static_cast<float>(__builtin_bit_cast(T, static_cast<uint16_t>(r.bias)));
-            if constexpr (FP8) {
 #pragma unroll
-              for (int r4 = 0; r4 < 4; ++r4) {
-                const int m = 4 * g + r4;
-                if (m < M) Y[static_cast<size_t>(m) * N + n] = round_to<T>(acc[r4] + b);
-              }
-            } else {
+          for (int v = 1; v < KS; ++v) acc += red[(wave + v) * 64 + lane];
+        }
+        __syncthreads();
+      }
+      if (ks == 0) {
+        const int n = 16 * (cp.tg * TPW + tw) + li;
+        if (n < N) {
+          // zero bits when there is no bias (zero-length buffer)
+          const float b = static_cast<float>(__builtin_bit_cast(T, static_cast<uint16_t>(tbias)));
+          if constexpr (FP8) {
 #pragma unroll
-              for (int h = 0; h < R; ++h) {
-                const int m = g + 4 * h;
-                if (m < M) Y[static_cast<size_t>(m) * N + n] = round_to<T>(fmaf(acc[h], ws2, b));
-              }
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const int m = 4 * g + r4;
+              if (m < M) Y[static_cast<size_t>(m) * N + n] = round_to<T>(acc[r4] + b);
+            }
+          } else {
+#pragma unroll
+            for (int h = 0; h < R; ++h) {
+              const int m = g + 4 * h;
+              if (m < M) Y[static_cast<size_t>(m) * N + n] = round_to<T>(fmaf(acc[h], ws2, b));
             }
           }
         }
-        acc = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      cp.advance(nws, stride);
+      acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    cp.advance(nws, stride);
   };
 
   // Window f sits in slot f % S.  Loads run ahead unconditionally (past the
@@ -371,10 +422,9 @@ constexpr int depth() {
   return ACT_LDS ? (FP8 ? 5 : 7) : 3;
 }
 
-size_t lds_bytes(int KS, bool act_lds, bool fp8, int M, int NW) {
+size_t lds_bytes(bool act_lds, bool fp8, int M, int NW) {
   const size_t rows = static_cast<size_t>(M) + (fp8 ? 0 : 1);  // FP4: plus the zero row
-  return (KS > 1 ? kWaves * 64 * sizeof(f32x4) : 0) +
-         (act_lds ? rows * (static_cast<size_t>(NW) * 256 + 16) : 0);
+  return kWaves * 1024 + (act_lds ? rows * (static_cast<size_t>(NW) * 256 + 16) : 0);
 }
 
 int num_cus() {
@@ -405,11 +455,9 @@ void allow_lds() {
   }
 }
 
-// Resident workgroups per CU for a kernel variant and LDS size (the variant
-// with the most row registers is queried).
-template <typename T, int KS, bool FP8, bool ACT_LDS>
+// Resident workgroups per CU for a kernel variant and LDS size.
+template <typename T, int KS, bool FP8, bool ACT_LDS, int R>
 int wg_per_cu(size_t lds) {
-  constexpr int R = FP8 ? 4 : 2;
   allow_lds<T, KS, FP8, ACT_LDS, R>();
   int v = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kernel_ptr<T, KS, FP8, ACT_LDS, R>(), 64 * kWaves,
@@ -419,15 +467,22 @@ int wg_per_cu(size_t lds) {
   return v;
 }
 
+template <typename T, int KS, bool FP8, bool ACT_LDS>
+int wg_per_cu_r(int R, size_t lds) {
+  if (R == 1) return wg_per_cu<T, KS, FP8, ACT_LDS, 1>(lds);
+  if (R == 2 || !FP8) return wg_per_cu<T, KS, FP8, ACT_LDS, 2>(lds);
+  return wg_per_cu<T, KS, FP8, ACT_LDS, (FP8 ? 4 : 2)>(lds);
+}
+
 template <typename T, bool FP8, bool ACT_LDS>
-int slots_for(int KS, int M, int NW) {
-  const size_t lds = lds_bytes(KS, ACT_LDS, FP8, M, NW);
+int slots_for(int KS, int R, int M, int NW) {
+  const size_t lds = lds_bytes(ACT_LDS, FP8, M, NW);
   int per = 1;
   switch (KS) {
-    case 1: per = wg_per_cu<T, 1, FP8, ACT_LDS>(lds); break;
-    case 2: per = wg_per_cu<T, 2, FP8, ACT_LDS>(lds); break;
-    case 4: per = wg_per_cu<T, 4, FP8, ACT_LDS>(lds); break;
-    default: per = wg_per_cu<T, 8, FP8, ACT_LDS>(lds); break;
+    case 1: per = wg_per_cu_r<T, 1, FP8, ACT_LDS>(R, lds); break;
+    case 2: per = wg_per_cu_r<T, 2, FP8, ACT_LDS>(R, lds); break;
+    case 4: per = wg_per_cu_r<T, 4, FP8, ACT_LDS>(R, lds); break;
+    default: per = wg_per_cu_r<T, 8, FP8, ACT_LDS>(R, lds); break;
   }
   return num_cus() * per;
 }
@@ -443,7 +498,7 @@ struct Plan {
 // leave HBM channels idle, which the cost scales up by.  The cheapest plan
 // wins; ties go to the smaller split (fewer LDS reductions).
 template <typename T, bool FP8>
-Plan plan(int64_t N, int M, int NW) {
+Plan plan(int64_t N, int M, int R, int NW) {
   const int64_t tiles = (N + 15) / 16;
   const int cus = num_cus();
   Plan best{1, 1, NW, false};
@@ -451,9 +506,9 @@ Plan plan(int64_t N, int M, int NW) {
   for (int mode = 0; mode < 2; ++mode) {
     for (int ks = 1; ks <= 8; ks <<= 1) {
       if (ks > 1 && NW < 2 * ks) continue;  // at least two windows per wave
-      if (mode == 1 && lds_bytes(ks, true, FP8, M, NW) > kMaxLds) continue;
+      if (mode == 1 && lds_bytes(true, FP8, M, NW) > kMaxLds) continue;
       const int64_t ntg = (tiles + kWaves / ks - 1) / (kWaves / ks);
-      const int64_t slots = mode ? slots_for<T, FP8, true>(ks, M, NW) : slots_for<T, FP8, false>(ks, M, NW);
+      const int64_t slots = mode ? slots_for<T, FP8, true>(ks, R, M, NW) : slots_for<T, FP8, false>(ks, R, M, NW);
       const int nws = (NW + ks - 1) / ks;
       const int64_t rounds = (ntg + slots - 1) / slots;
       double cost = static_cast<double>(rounds) * nws;
@@ -465,6 +520,39 @@ Plan plan(int64_t N, int M, int NW) {
     }
   }
   return best;
+}
+
+// The plan depends only on the sizes, the device and the variant's resource
+// use; it is computed once per shape (the occupancy queries cost several
+// microseconds, more than a decode GEMV takes on the GPU).
+struct PlanEntry {
+  int64_t N;
+  int M, NW, dev, kind;
+  Plan p;
+};
+
+template <typename T, bool FP8>
+Plan cached_plan(int64_t N, int M, int R, int NW) {
+  constexpr int kEntries = 64;
+  static PlanEntry table[kEntries];
+  static int used = 0, next = 0;
+  static std::mutex mu;
+  const int kind = (FP8 ? 2 : 0) + (sizeof(T) == 2 && __is_same(T, __bf16) ? 1 : 0);
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i) {
+      const PlanEntry& e = table[i];
+      if (e.N == N && e.M == M && e.NW == NW && e.dev == dev && e.kind == kind) return e.p;
+    }
+  }
+  const Plan p = plan<T, FP8>(N, M, R, NW);
+  std::lock_guard<std::mutex> lock(mu);
+  table[next] = PlanEntry{N, M, NW, dev, kind, p};
+  next = (next + 1) % kEntries;
+  if (used < kEntries) ++used;
+  return p;
 }
 
 template <typename T, int KS, bool FP8, bool LDS>
@@ -494,11 +582,11 @@ int launch_t(const MatmulArgs& a) {
     return -1;
   const int M = static_cast<int>(a.M);
   const int NW = static_cast<int>(a.K / 128);
-  const Plan p = plan<T, FP8>(a.N, M, NW);
-  const int tiles = static_cast<int>((a.N + 15) / 16);
-  const size_t lds = lds_bytes(p.KS, p.act_lds, FP8, M, NW);
   // FP8: result rows a lane scales; FP4: row halves
   const int R = FP8 ? (M >= 3 ? 4 : M) : (M > 4 ? 2 : 1);
+  const Plan p = cached_plan<T, FP8>(a.N, M, R, NW);
+  const int tiles = static_cast<int>((a.N + 15) / 16);
+  const size_t lds = lds_bytes(p.act_lds, FP8, M, NW);
   const FastDiv wpb = make_fastdiv(FP8 ? static_cast<uint32_t>(a.block_size / 128) : 1u);
   const FastDiv cpr = make_fastdiv(static_cast<uint32_t>(NW) * 16u + 1u);  // 16-byte chunks per LDS row
 #define FP4W_GEMV_KS(LDS_)                                                   \
