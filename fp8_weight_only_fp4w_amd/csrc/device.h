@@ -81,6 +81,17 @@ struct ActTraits<__bf16> {
     r[6] = static_cast<__bf16>(p3.x); r[7] = static_cast<__bf16>(p3.y);
     return r;
   }
+  // 8 E2M1 codes of `w` -> bf16x8 (exact, no scale)
+  __device__ __forceinline__ static vec8 decode8_fp4(uint32_t w) {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3);
+    vec8 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+    r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+    return r;
+  }
   // 8 E4M3 codes of (lo, hi) -> bf16x8 (exact, no scale)
   __device__ __forceinline__ static vec8 decode8_fp8(uint32_t lo, uint32_t hi) {
     bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
@@ -118,6 +129,16 @@ struct ActTraits<_Float16> {
     r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
     return r;
   }
+  __device__ __forceinline__ static vec8 decode8_fp4(uint32_t w) {
+    const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+    const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+    const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+    const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+    vec8 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+    r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+    return r;
+  }
   __device__ __forceinline__ static vec8 decode8_fp8(uint32_t lo, uint32_t hi) {
     f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
     f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
@@ -133,69 +154,6 @@ struct ActTraits<_Float16> {
   }
   __device__ __forceinline__ static float to_f32(_Float16 x) { return static_cast<float>(x); }
 };
-
-// ------------------------------------------------------------------ 16x16x16 MFMA
-//
-// v_mfma_f32_16x16x16_{bf16,f16}: K = 16 is exactly one FP4 scale block, so
-// a block can be multiplied unscaled (E2M1 -> T is a plain conversion) and
-// its FP32 result scaled afterwards.  Operand layout (checked on gfx950):
-// lane l supplies row / column l % 16 and k = 4 (l / 16) .. 4 (l / 16) + 3;
-// the result lane l holds column l % 16, rows 4 (l / 16) .. 4 (l / 16) + 3.
-
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-
-template <typename T>
-struct Mfma16;
-
-template <>
-struct Mfma16<__bf16> {
-  typedef bf16x4 vec4;
-  // 4 E2M1 codes in half H (bytes 2H, 2H+1) of `w`, low nibble first -> 4 x T
-  template <int H>
-  __device__ __forceinline__ static vec4 decode4(uint32_t w) {
-    const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2 * H);
-    const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2 * H + 1);
-    vec4 r;
-    r[0] = lo[0]; r[1] = lo[1]; r[2] = hi[0]; r[3] = hi[1];
-    return r;
-  }
-  __device__ __forceinline__ static f32x4 mfma(vec4 a, vec4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-  }
-};
-
-template <>
-struct Mfma16<_Float16> {
-  typedef f16x4 vec4;
-  template <int H>
-  __device__ __forceinline__ static vec4 decode4(uint32_t w) {
-    const f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2 * H);
-    const f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2 * H + 1);
-    vec4 r;
-    r[0] = lo[0]; r[1] = lo[1]; r[2] = hi[0]; r[3] = hi[1];
-    return r;
-  }
-  __device__ __forceinline__ static f32x4 mfma(vec4 a, vec4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-  }
-};
-
-// 4 x 4 transpose of dwords across the four 16-lane groups of a wave: on
-// entry lane group g holds x[h] (h = 0..3) meant for group h; on exit lane
-// group g holds, in x[h], what group h held in x[g].  Two v_permlane32_swap
-// (exchange between lane halves) then two v_permlane16_swap (exchange between
-// neighbouring 16-lane rows).
-__device__ __forceinline__ void transpose4x4_groups(uint32_t (&x)[4]) {
-  const auto a = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
-  const auto b = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
-  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
-  const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
-  x[0] = c[0];
-  x[1] = c[1];
-  x[2] = d[0];
-  x[3] = d[1];
-}
 
 // Materialise an FP32 value in a VGPR.  Without this the backend may fold
 // "multiply in FP32, then convert to FP16" into one mixed-precision FMA

@@ -12,20 +12,20 @@
 // group g = l / 16 loads the contiguous chunk c = 4w + g of 32 k of its
 // column, one 16-byte load per lane for FP4 (two for FP8).
 //
-// FP4 (16x16x16 MFMA, "block-diagonal" activations).  Folding the E4M3 scale
+// FP4 (16x16x32 MFMA, "block-diagonal" activations).  Folding the E4M3 scale
 // into BF16 weights would be exact ([FP4 doc] §4), but costs a convert, two
 // FP32 multiplies and a pack per pair of weights, which makes a wave64 GEMV
 // VALU-bound on CDNA4.  Instead the weights are converted unscaled (one
 // instruction per pair) and every 16-k scale block gets its own FP32 dot,
 // scaled by its E4M3 value with one FMA.  Four blocks share each MFMA: lane
 // group g holds blocks 2g and 2g + 1 of the window, so in MFMA (s, p) the
-// four lane groups supply piece p (4 k) of blocks 2g + s, g = 0..3.  Row
+// four lane groups supply piece p (8 k) of blocks 2g + s, g = 0..3.  Row
 // i = 4 m' + q of the A operand carries activation row m = m' (+ 4 for the
 // second row half) in the k slots of lane group q only, and zeros elsewhere;
-// summing the four pieces p therefore leaves in result row (m', q) the full
+// summing the two pieces p therefore leaves in result row (m', q) the full
 // dot of row m with block 2q + s.  The result lane (column n, group g) holds
 // rows 4g .. 4g + 3 = the four blocks of one activation row, so a window
-// costs 8 MFMAs and 8 FMAs per row half, with no data exchange between lanes.
+// costs 4 MFMAs and 8 FMAs per row half, with no data exchange between lanes.
 // weight_scale_2 and the bias are applied once in the epilogue.
 //
 // FP8 (16x16x32 MFMA).  E4M3 -> T is exact and the FP32 block scale is
@@ -96,12 +96,6 @@ struct Pos {
     }
   }
 };
-
-// Dwords 2J, 2J + 1 of a 16-byte register as a 4-wide MFMA operand.
-template <typename V4, int J>
-__device__ __forceinline__ V4 half_of(u32x4 v) {
-  return __builtin_bit_cast(V4, u32x2{v[2 * J], v[2 * J + 1]});
-}
 
 // Activations, two ways (ACT_LDS):
 //  * false: loaded from L2 with the weights, at the same pipeline depth;
@@ -308,11 +302,11 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
 #pragma unroll
       for (int i = 0; i < R; ++i) acc[i] = fmaf(blk[i], sc, acc[i]);
     } else {
-      typedef Mfma16<T> Mf;
-      typedef typename Mf::vec4 V4;
+      typedef ActTraits<T> Tr;
+      typedef typename Tr::vec8 V;
       const u32x2 sb = *reinterpret_cast<const u32x2*>(slice + 64 * li + 8 * (j % SW));
-      // activations of the lane: 4 x 16 bytes per row half, chunk i holds
-      // k 32g + 8i .. + 7 of the window (set i / 2, pieces 2 (i % 2), + 1)
+      // activations of the lane: 4 x 16 bytes per row half; chunk i = 2s + p
+      // holds k 32g + 16s + 8p .. + 7 of the window (piece p of set s)
       u32x4 av[R][4];
 #pragma unroll
       for (int h = 0; h < R; ++h) {
@@ -325,26 +319,18 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
           for (int i = 0; i < 4; ++i) av[h][i] = r.a[4 * h + i];
         }
       }
-      // weights of set s (block 2g + s): dwords 2s, 2s + 1; piece p: dword
-      // 2s + p / 2, half p % 2
-      V4 bw[2][4];
+      // weights of piece p of set s (block 2g + s): dword 2s + p (8 codes)
+      V bw[4];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        bw[s][0] = Mf::template decode4<0>(r.w[2 * s]);
-        bw[s][1] = Mf::template decode4<1>(r.w[2 * s]);
-        bw[s][2] = Mf::template decode4<0>(r.w[2 * s + 1]);
-        bw[s][3] = Mf::template decode4<1>(r.w[2 * s + 1]);
-      }
+      for (int i = 0; i < 4; ++i) bw[i] = Tr::decode8_fp4(r.w[i]);
       const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
       f32x4 d[R][2];
 #pragma unroll
       for (int h = 0; h < R; ++h)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          d[h][s] = Mf::mfma(half_of<V4, 0>(av[h][2 * s]), bw[s][0], zero);
-          d[h][s] = Mf::mfma(half_of<V4, 1>(av[h][2 * s]), bw[s][1], d[h][s]);
-          d[h][s] = Mf::mfma(half_of<V4, 0>(av[h][2 * s + 1]), bw[s][2], d[h][s]);
-          d[h][s] = Mf::mfma(half_of<V4, 1>(av[h][2 * s + 1]), bw[s][3], d[h][s]);
+          d[h][s] = Tr::mfma(__builtin_bit_cast(V, av[h][2 * s]), bw[2 * s], zero);
+          d[h][s] = Tr::mfma(__builtin_bit_cast(V, av[h][2 * s + 1]), bw[2 * s + 1], d[h][s]);
         }
       // result row r of set s is block 2r + s: scale byte 2r + s
       const f32x2 s01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb.x), false);
@@ -415,11 +401,12 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
 
 constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 
-// Pipeline depth: with activations in LDS a window's registers are only the
-// weights and scales, so more windows fit in flight.
+// Pipeline depth (windows in flight per wave), from measurement: FP4 with
+// activations in LDS gains up to 5; FP8 loads twice the bytes per window and
+// is best at 3.
 template <bool FP8, bool ACT_LDS>
 constexpr int depth() {
-  return ACT_LDS ? (FP8 ? 5 : 7) : 3;
+  return ACT_LDS && !FP8 ? 5 : 3;
 }
 
 size_t lds_bytes(bool act_lds, bool fp8, int M, int NW) {
@@ -492,34 +479,23 @@ struct Plan {
   bool act_lds;
 };
 
-// Launch plan: for each K split (1, 2, 4, 8 waves per tile) and activation
-// mode, the serial work of one wave slot is rounds x windows-per-wave, where
-// rounds = ceil(tile groups / resident workgroups); fewer workgroups than CUs
-// leave HBM channels idle, which the cost scales up by.  The cheapest plan
-// wins; ties go to the smaller split (fewer LDS reductions).
+// Launch plan (rules from measurements on the decode, FP8 and wide-output
+// shapes).  Activations go to LDS whenever they fit (reading them from L2 per
+// window costs more load instructions than the weights themselves).  Few
+// tiles (fewer than two per CU): 4 waves split K and a workgroup owns two
+// tiles, which halves the activation fill per tile; many tiles: 8 waves split
+// K of one tile.  Each wave keeps at least two windows.  The grid is the
+// number of tile groups, capped at the resident workgroups (persistent).
 template <typename T, bool FP8>
 Plan plan(int64_t N, int M, int R, int NW) {
   const int64_t tiles = (N + 15) / 16;
   const int cus = num_cus();
-  Plan best{1, 1, NW, false};
-  double best_cost = 1e300;
-  for (int mode = 0; mode < 2; ++mode) {
-    for (int ks = 1; ks <= 8; ks <<= 1) {
-      if (ks > 1 && NW < 2 * ks) continue;  // at least two windows per wave
-      if (mode == 1 && lds_bytes(true, FP8, M, NW) > kMaxLds) continue;
-      const int64_t ntg = (tiles + kWaves / ks - 1) / (kWaves / ks);
-      const int64_t slots = mode ? slots_for<T, FP8, true>(ks, R, M, NW) : slots_for<T, FP8, false>(ks, R, M, NW);
-      const int nws = (NW + ks - 1) / ks;
-      const int64_t rounds = (ntg + slots - 1) / slots;
-      double cost = static_cast<double>(rounds) * nws;
-      if (ntg < cus) cost *= static_cast<double>(cus) / ntg;
-      if (cost < best_cost - 1e-9) {
-        best_cost = cost;
-        best = Plan{ks, static_cast<int>(ntg < slots ? ntg : slots), nws, mode == 1};
-      }
-    }
-  }
-  return best;
+  const bool lds = lds_bytes(true, FP8, M, NW) <= kMaxLds;
+  int ks = tiles < 2 * static_cast<int64_t>(cus) ? 4 : 8;
+  while (ks > 1 && NW < 2 * ks) ks >>= 1;
+  const int64_t ntg = (tiles + kWaves / ks - 1) / (kWaves / ks);
+  const int64_t slots = lds ? slots_for<T, FP8, true>(ks, R, M, NW) : slots_for<T, FP8, false>(ks, R, M, NW);
+  return Plan{ks, static_cast<int>(ntg < slots ? ntg : slots), (NW + ks - 1) / ks, lds};
 }
 
 // The plan depends only on the sizes, the device and the variant's resource
