@@ -5,12 +5,13 @@ Headline (one JSON line on stdout): the FP4 decode GEMV, M in {1, 2, 4, 8},
 N = K = 5120, block 16, BF16 activations N(0,1), bias.  One step = the four
 GEMV calls (one per M), each on its own copy of the weights; 73 copies
 (about 1 GiB) rotate so every call streams its weights from HBM rather than
-from the 256 MB last-level cache.  Each step is a captured HIP graph, so host
-launch overhead does not sit between the kernels.
+from the 256 MB last-level cache.  Steps run as captured HIP graphs of eight
+steps each, so host launch overhead does not sit between the kernels.
 
     value    = packed weight + scale bytes per step / step time  [GB/s]
     roofline = the GEMV kernel: algorithmic bytes (weights, scales,
-               activations, bias, output) per launch / mean launch time,
+               activations, bias, output) per launch / mean launch time
+               (timed region / launches, HIP events on the launch stream),
                against the 8 TB/s HBM3E peak
     cpu_baseline = the CPU oracle on the same workload (GB/s of weights)
 
@@ -125,6 +126,17 @@ def time_graphs(graphs, steps, warmup):
     return wall, start.elapsed_time(stop) / 1e3
 
 
+def time_rotating(call, R, launches, G=8):
+    """Per-launch seconds of call(r) over rotating copies r = 0 .. R-1, from
+    graphs of G launches each (HIP events around the timed replays)."""
+    n = -(-R // G)
+    gs = [capture(lambda i=i: [call((i * G + k) % R) for k in range(G)]) for i in range(n)]
+    reps = max(1, launches // G)
+    _, e = time_graphs(gs, reps, min(reps, 4))
+    del gs
+    return e / (reps * G)
+
+
 def time_calls(fn_list, steps, warmup):
     """Direct launches (for long kernels where launch overhead is hidden)."""
     for i in range(warmup):
@@ -141,6 +153,9 @@ def time_calls(fn_list, steps, warmup):
 
 # ------------------------------------------------------------------ headline
 
+STEPS_PER_GRAPH = 8   # steps captured in one graph (amortises the graph launch)
+
+
 def gemv_decode(steps, warmup):
     w = workloads.WORKLOADS["fp4_gemv_decode"]
     Ms = w.Ms
@@ -156,23 +171,44 @@ def gemv_decode(steps, warmup):
         for M in Ms:
             fw.fp4w_matmul(A[M], d["B"][r], d["ws"][r], d["ws2"], d["bias"], 16, out=out[M])
 
-    graphs = [capture(lambda r=r: step(r)) for r in range(R)]
-    wall, ev = time_graphs(graphs, steps, warmup)
-    per_step = ev / steps
+    # graphs of STEPS_PER_GRAPH consecutive steps (each step on the next copy
+    # of the weights), and single-step graphs for a remainder
+    G = STEPS_PER_GRAPH
+    n_groups = -(-R // G)
+    groups = [capture(lambda i=i: [step((i * G + k) % R) for k in range(G)]) for i in range(n_groups)]
+    singles = [capture(lambda r=r: step(r)) for r in range(min(R, G))]
+    for i in range(max(1, warmup // G)):
+        groups[i % n_groups].replay()
+    for i in range(warmup % G):
+        singles[i % len(singles)].replay()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps // G):
+        groups[i % n_groups].replay()
+    for i in range(steps % G):
+        singles[i % len(singles)].replay()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_step = start.elapsed_time(stop) / 1e3 / steps
+    del groups, singles
     # algorithmic bytes of one step (four launches)
     alg = 0
     for M in Ms:
         alg += weight_bytes + M * w.K * 2 + w.N * 2 + M * w.N * 2 + 4
-    # per-M breakdown (graphs of one launch each, same rotation)
+    # per-M breakdown (graphs of G launches of one M, same rotation)
     per_m = {}
     for M in Ms:
-        gs = [capture(lambda r=r, M=M: fw.fp4w_matmul(A[M], d["B"][r], d["ws"][r], d["ws2"], d["bias"], 16,
-                                                       out=out[M])) for r in range(R)]
-        _, e = time_graphs(gs, max(steps, 100), warmup)
-        t = e / max(steps, 100)
+        gs = [capture(lambda i=i, M=M: [fw.fp4w_matmul(A[M], d["B"][(i * G + k) % R], d["ws"][(i * G + k) % R],
+                                                        d["ws2"], d["bias"], 16, out=out[M]) for k in range(G)])
+              for i in range(n_groups)]
+        reps = max(steps // G, 16)
+        _, e = time_graphs(gs, reps, 2)
+        t = e / (reps * G)
         per_m[str(M)] = {"us": round(t * 1e6, 3), "weight_GBps": round(weight_bytes / t / 1e9, 1)}
         del gs
-    del graphs
     return dict(workload=w, Ms=Ms, weight_bytes=weight_bytes, R=R, per_step=per_step, wall=wall,
                 alg_bytes_step=alg, per_m=per_m)
 
@@ -221,9 +257,9 @@ def extra_small_gemv(steps, warmup):
     p = w.make()
     d = fp4_on_device(p)
     out = torch.empty(1, w.N, dtype=torch.float16, device="cuda")
-    g = capture(lambda: fw.fp4w_matmul(d["A"], d["B"][0], d["ws"][0], d["ws2"], None, 16, out=out))
-    _, e = time_graphs([g], steps, warmup)
-    return {"us_per_call": round(e / steps * 1e6, 3), "note": "75 KB working set, L2-resident"}
+    t = time_rotating(lambda r: fw.fp4w_matmul(d["A"], d["B"][0], d["ws"][0], d["ws2"], None, 16, out=out),
+                      1, steps)
+    return {"us_per_call": round(t * 1e6, 3), "note": "75 KB working set, L2-resident"}
 
 
 def extra_prefill_fp4(reps=10, warmup=3):
@@ -261,11 +297,9 @@ def extra_fp8(steps, warmup, reps=10):
     R = copies_for(wb)
     d = fp8_on_device(p, copies=R)
     out = torch.empty(4, p.N, dtype=torch.bfloat16, device="cuda")
-    gs = [capture(lambda r=r: fw.fp8w_matmul(d["A"], d["B"][r], d["bs"][r], None, 128, out=out)) for r in range(R)]
-    _, e = time_graphs(gs, steps, warmup)
-    t = e / steps
+    t = time_rotating(lambda r: fw.fp8w_matmul(d["A"], d["B"][r], d["bs"][r], None, 128, out=out), R, steps)
     res = {"gemv_M4_us": round(t * 1e6, 2), "gemv_M4_weight_GBps": round(wb / t / 1e9, 1)}
-    del gs, d
+    del d
     p8 = w.make(M=8192)
     d = fp8_on_device(p8)
     out = torch.empty(8192, p8.N, dtype=torch.bfloat16, device="cuda")
@@ -282,10 +316,8 @@ def extra_wide(steps, warmup):
     R = copies_for(wb)
     d = fp4_on_device(p, copies=R)
     out = torch.empty(4, p.N, dtype=torch.bfloat16, device="cuda")
-    gs = [capture(lambda r=r: fw.fp4w_matmul(d["A"], d["B"][r], d["ws"][r], d["ws2"], None, 16, out=out))
-          for r in range(R)]
-    _, e = time_graphs(gs, steps, warmup)
-    t = e / steps
+    t = time_rotating(lambda r: fw.fp4w_matmul(d["A"], d["B"][r], d["ws"][r], d["ws2"], None, 16, out=out),
+                      R, min(steps, 64))
     return {"us": round(t * 1e6, 2), "weight_GBps": round(wb / t / 1e9, 1), "copies": R}
 
 
@@ -300,9 +332,21 @@ def profile_kernel(which, launches=50):
         dst = torch.empty_like(src)
         for _ in range(launches):
             dst.copy_(src)
-    elif which in ("fp4_gemv", "fp4_gemv_wide"):
-        w = workloads.WORKLOADS["fp4_gemv_decode" if which == "fp4_gemv" else "fp4_gemv_wide"]
-        p = w.make(M=8 if which == "fp4_gemv" else 4)
+    elif which == "fp4_gemv":
+        # the headline step: M = 1, 2, 4, 8 on rotating weight copies
+        w = workloads.WORKLOADS["fp4_gemv_decode"]
+        probs = {M: w.make(M=M) for M in w.Ms}
+        p0 = probs[w.Ms[0]]
+        R = copies_for(p0.B.nbytes + p0.weight_scale.nbytes)
+        d = fp4_on_device(p0, copies=R)
+        A = {M: dev_bits(probs[M].A, "bf16") for M in w.Ms}
+        out = {M: torch.empty(M, w.N, dtype=torch.bfloat16, device="cuda") for M in w.Ms}
+        for i in range(launches):
+            for M in w.Ms:
+                fw.fp4w_matmul(A[M], d["B"][i % R], d["ws"][i % R], d["ws2"], d["bias"], 16, out=out[M])
+    elif which == "fp4_gemv_wide":
+        w = workloads.WORKLOADS["fp4_gemv_wide"]
+        p = w.make(M=4)
         R = copies_for(p.B.nbytes + p.weight_scale.nbytes)
         d = fp4_on_device(p, copies=R)
         out = torch.empty(p.M, w.N, dtype=torch.bfloat16, device="cuda")
