@@ -34,6 +34,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -222,6 +224,208 @@ __global__ __launch_bounds__(256 * WM) void gemm_kernel(
   }
 }
 
+// FP4 prefill GEMM, large tiles.  Workgroup 256 (M) x 256 (N) x 64 (K per
+// step), 4 waves in a 2 x 2 grid, each wave 128 x 128 = 8 x 8 tiles of
+// v_mfma_f32_16x16x32 (256 FP32 accumulators per lane: one wave per SIMD
+// uses the whole register file).  A 128 x 128 wave tile reads each activation
+// operand once per 8 MFMAs and decodes each weight operand once per 8 MFMAs.
+//  * Every operand tile (activations, packed weights, scale bytes) moves
+//    global -> LDS by direct loads (global_load_lds: no registers), three
+//    stages deep: the tiles of step t + 2 are requested during step t, so a
+//    load has two steps of MFMA work to arrive.  The only wait is, at the end
+//    of each step, for the tiles of the next step (loads complete in order).
+//  * LDS layout per stage: activations [256 rows][64] of T with 16-byte chunks
+//    XOR-swizzled by row (the swizzle is applied to the global addresses,
+//    since one direct load writes 1 KiB contiguously), packed weights
+//    [256 columns][32 bytes], scale bytes [256 columns][4].
+//  * Lane (li, g) takes k 16g .. 16g + 15 of each step for both operands
+//    (one 16-element scale block), split in two 8-k halves over two MFMAs;
+//    the E4M3 scale is folded into the decoded BF16/FP16 operand (exact).
+//  * Tile order: workgroups are dispatched round-robin over the 8 XCDs, each
+//    with its own L2, so the workgroup index is remapped to give every XCD a
+//    contiguous range of tiles, walked in groups of 8 tile rows.
+constexpr int L_BM = 256, L_BN = 256;
+
+template <typename T>
+struct LargeStage {
+  T a[L_BM * kLdsRow];      // 32 KiB
+  uint8_t b[L_BN * 32];     // 8 KiB
+  uint8_t s[L_BN * 4];      // 1 KiB
+};
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// direct 16-byte (or 4-byte) global -> LDS load: lane l writes lds + l * size
+template <int SIZE>
+__device__ __forceinline__ void load_lds(const void* gptr, void* lds) {
+  static_assert(SIZE == 16 || SIZE == 4, "direct load size");
+  if constexpr (SIZE == 16)
+    __builtin_amdgcn_global_load_lds(gptr, (lds_ptr_t)(lds), 16, 0, 0);
+  else
+    __builtin_amdgcn_global_load_lds(gptr, (lds_ptr_t)(lds), 4, 0, 0);
+}
+
+// wait until at most N vector-memory loads are in flight and every LDS access
+// has completed, then barrier (the compiler fences keep LDS accesses on
+// their side of it)
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));  // lgkmcnt(0), vmcnt(N)
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void gemm_fp4_large_kernel(
+    const T* __restrict__ A, const uint8_t* __restrict__ B, const uint8_t* __restrict__ scales,
+    const float* __restrict__ ws2p, const T* __restrict__ bias, T* __restrict__ Y, int M, int N,
+    int K, int cols, int tiles_m, int tiles_n) {
+  typedef ActTraits<T> Tr;
+  typedef typename Tr::vec8 V;
+  __shared__ __attribute__((aligned(16))) LargeStage<T> st0, st1, st2;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, g = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // tile index: contiguous range per XCD, then groups of 8 tile rows
+  const int ntiles = tiles_m * tiles_n;
+  int t = blockIdx.x;
+  if (ntiles % 8 == 0) t = (t % 8) * (ntiles / 8) + t / 8;
+  constexpr int GM = 8;
+  const int per_group = GM * tiles_n;
+  const int first_m = (t / per_group) * GM;
+  const int gsize = min(tiles_m - first_m, GM);
+  const int tm = first_m + (t % per_group) % gsize;
+  const int tn = (t % per_group) / gsize;
+  const int m0 = tm * L_BM, n0 = tn * L_BN;
+
+  // Direct-load sources of this lane (element / byte offsets, step 0).
+  // Activations: instruction j of wave w writes rows 8q .. 8q + 7 of the
+  // stage, q = 4j + w; lane l lands in row 8q + l / 8, LDS chunk l % 8, which
+  // holds global chunk (l % 8) ^ (l / 8) under the swizzle.
+  int a_off[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int row = 8 * (4 * j + wave) + (lane >> 3);
+    const int chunk = (lane & 7) ^ (lane >> 3);
+    a_off[j] = min(m0 + row, M - 1) * K + 8 * chunk;
+  }
+  // packed weights: instruction j of wave w covers columns 32q .. 32q + 31,
+  // q = 4j + w (j = 0, 1); lane l: column 32q + l / 2, bytes 16 (l % 2) ..
+  int b_off[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = 32 * (4 * j + wave) + (lane >> 1);
+    b_off[j] = min(n0 + col, N - 1) * (K / 2) + 16 * (lane & 1);
+  }
+  // scale bytes: wave w covers columns 64w .. 64w + 63, 4 bytes each
+  const int s_off = min(n0 + 64 * wave + lane, N - 1) * cols;
+
+  const int nsteps = K / BK;
+  auto issue = [&](int step, LargeStage<T>& st) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      load_lds<16>(A + a_off[j] + step * BK, &st.a[(4 * j + wave) * 8 * kLdsRow]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) load_lds<16>(B + b_off[j] + step * (BK / 2), &st.b[(4 * j + wave) * 32 * 32]);
+    load_lds<4>(scales + s_off + step * (BK / 16), &st.s[64 * wave * 4]);
+  };
+  constexpr int kLoadsPerStep = 11;  // per wave: 8 + 2 + 1 direct loads
+
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // One step: two halves of 8 k per lane.  The LDS reads of both halves and
+  // the weight decode of the first are issued up front; the decode of the
+  // second half (VALU) is interleaved with the 64 MFMAs of the first, so the
+  // vector ALU works while the matrix cores are busy.
+  auto compute = [&](const LargeStage<T>& st) {
+    u32x2 bw[8];
+    float sc[8];
+#pragma unroll
+    for (int ns = 0; ns < 8; ++ns) {
+      const int col = 128 * wn + 16 * ns + li;
+      bw[ns] = *reinterpret_cast<const u32x2*>(&st.b[col * 32 + 8 * g]);
+      sc[ns] = e4m3_to_f32<0>(st.s[col * 4 + g]);
+    }
+    V aop[2][8];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int ms = 0; ms < 8; ++ms)
+        aop[s][ms] = *reinterpret_cast<const V*>(&st.a[lds_index(128 * wm + 16 * ms + li, 2 * g + s)]);
+    V bop[2][8];
+#pragma unroll
+    for (int ns = 0; ns < 8; ++ns) bop[0][ns] = Tr::decode8(bw[ns][0], Tr::make_scale(sc[ns]));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ms = 0; ms < 8; ++ms)
+#pragma unroll
+      for (int ns = 0; ns < 8; ++ns) acc[ms][ns] = Tr::mfma(aop[0][ms], bop[0][ns], acc[ms][ns]);
+#pragma unroll
+    for (int ns = 0; ns < 8; ++ns) bop[1][ns] = Tr::decode8(bw[ns][1], Tr::make_scale(sc[ns]));
+    // 64 MFMAs, each followed by up to 2 VALU instructions of the decode
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ms = 0; ms < 8; ++ms)
+#pragma unroll
+      for (int ns = 0; ns < 8; ++ns) acc[ms][ns] = Tr::mfma(aop[1][ms], bop[1][ns], acc[ms][ns]);
+  };
+
+  // one step on stage S (the stage of step + 2 is S + 2 mod 3)
+  auto do_step = [&](int step, LargeStage<T>& cur, LargeStage<T>& ahead2) {
+    const bool issue2 = step + 2 < nsteps;
+    if (issue2) issue(step + 2, ahead2);
+    compute(cur);
+    if (issue2)
+      wait_barrier<kLoadsPerStep>();  // the tiles of step + 1 have landed
+    else
+      wait_barrier<0>();
+  };
+
+  issue(0, st0);
+  if (nsteps > 1) issue(1, st1);
+  if (nsteps > 1)
+    wait_barrier<kLoadsPerStep>();
+  else
+    wait_barrier<0>();
+  for (int step = 0; step < nsteps; step += 3) {
+    do_step(step, st0, st2);
+    if (step + 1 < nsteps) do_step(step + 1, st1, st0);
+    if (step + 2 < nsteps) do_step(step + 2, st2, st1);
+  }
+
+  // epilogue: lane (li, g) holds columns n0 + 128 wn + 16 ns + li and rows
+  // m0 + 128 wm + 16 ms + 4 g + r
+  const float ws2 = *ws2p;
+#pragma unroll
+  for (int ns = 0; ns < 8; ++ns) {
+    const int n = n0 + 128 * wn + 16 * ns + li;
+    if (n >= N) continue;
+    const float b = bias ? static_cast<float>(bias[n]) : 0.0f;
+#pragma unroll
+    for (int ms = 0; ms < 8; ++ms) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 128 * wm + 16 * ms + 4 * g + r;
+        if (m < M) Y[static_cast<size_t>(m) * N + n] = round_to<T>(fmaf(acc[ms][ns][r], ws2, b));
+      }
+    }
+  }
+}
+
 template <typename T, bool FP8>
 int launch(const MatmulArgs& a) {
   constexpr int WM = FP8 ? 1 : 2;
@@ -240,8 +444,25 @@ int launch(const MatmulArgs& a) {
 
 }  // namespace
 
+template <typename T>
+int launch_fp4_large(const MatmulArgs& a) {
+  if (a.M > 0x7fffffff || a.N > 0x7fffffff || a.K > 0x7fffffff) return -1;
+  // 32-bit element offsets inside the kernel
+  if (a.N * (a.K / 2) >= (int64_t(1) << 31) || a.N * a.scale_cols >= (int64_t(1) << 31) ||
+      static_cast<int64_t>(L_BM) * a.K >= (int64_t(1) << 31))
+    return launch<T, false>(a);
+  const int64_t tiles_m = (a.M + L_BM - 1) / L_BM, tiles_n = (a.N + L_BN - 1) / L_BN;
+  if (tiles_m * tiles_n > 0x7fffffff) return -1;
+  hipLaunchKernelGGL((gemm_fp4_large_kernel<T>), dim3(static_cast<unsigned>(tiles_m * tiles_n)), dim3(256), 0,
+                     static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.A), a.B,
+                     static_cast<const uint8_t*>(a.scales), a.ws2, static_cast<const T*>(a.bias),
+                     static_cast<T*>(a.Y), static_cast<int>(a.M), static_cast<int>(a.N), static_cast<int>(a.K),
+                     static_cast<int>(a.scale_cols), static_cast<int>(tiles_m), static_cast<int>(tiles_n));
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int launch_fp4_gemm(const MatmulArgs& a) {
-  return a.act == Act::BF16 ? launch<__bf16, false>(a) : launch<_Float16, false>(a);
+  return a.act == Act::BF16 ? launch_fp4_large<__bf16>(a) : launch_fp4_large<_Float16>(a);
 }
 
 int launch_fp8_gemm(const MatmulArgs& a) {
