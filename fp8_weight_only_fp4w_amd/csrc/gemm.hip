@@ -225,10 +225,10 @@ __global__ __launch_bounds__(256 * WM) void gemm_kernel(
 }
 
 // FP4 prefill GEMM, large tiles.  Workgroup 256 (M) x 256 (N) x 64 (K per
-// step), 4 waves in a 2 x 2 grid, each wave 128 x 128 = 8 x 8 tiles of
-// v_mfma_f32_16x16x32 (256 FP32 accumulators per lane: one wave per SIMD
-// uses the whole register file).  A 128 x 128 wave tile reads each activation
-// operand once per 8 MFMAs and decodes each weight operand once per 8 MFMAs.
+// step), 8 waves in a 2 (M) x 4 (N) grid, each wave 128 x 64 = 8 x 4 tiles of
+// v_mfma_f32_16x16x32 (128 FP32 accumulators per lane), two waves per SIMD:
+// a wave's weight decode (vector ALU) runs while the other wave's MFMAs
+// occupy the matrix core (one wave alone does not overlap the two).
 //  * Every operand tile (activations, packed weights, scale bytes) moves
 //    global -> LDS by direct loads (global_load_lds: no registers), three
 //    stages deep: the tiles of step t + 2 are requested during step t, so a
@@ -278,18 +278,18 @@ __device__ __forceinline__ void wait_barrier() {
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void gemm_fp4_large_kernel(
+__global__ __launch_bounds__(512) void gemm_fp4_large_kernel(
     const T* __restrict__ A, const uint8_t* __restrict__ B, const uint8_t* __restrict__ scales,
     const float* __restrict__ ws2p, const T* __restrict__ bias, T* __restrict__ Y, int M, int N,
     int K, int cols, int tiles_m, int tiles_n) {
   typedef ActTraits<T> Tr;
   typedef typename Tr::vec8 V;
-  __shared__ __attribute__((aligned(16))) LargeStage<T> st0, st1, st2;
+  __shared__ __attribute__((aligned(16))) LargeStage<T> st[3];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, g = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
 
   // tile index: contiguous range per XCD, then groups of 8 tile rows
   const int ntiles = tiles_m * tiles_n;
@@ -305,87 +305,66 @@ __global__ __launch_bounds__(256) void gemm_fp4_large_kernel(
 
   // Direct-load sources of this lane (element / byte offsets, step 0).
   // Activations: instruction j of wave w writes rows 8q .. 8q + 7 of the
-  // stage, q = 4j + w; lane l lands in row 8q + l / 8, LDS chunk l % 8, which
+  // stage, q = 8j + w; lane l lands in row 8q + l / 8, LDS chunk l % 8, which
   // holds global chunk (l % 8) ^ (l / 8) under the swizzle.
-  int a_off[8];
+  int a_off[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = 8 * (4 * j + wave) + (lane >> 3);
+  for (int j = 0; j < 4; ++j) {
+    const int row = 8 * (8 * j + wave) + (lane >> 3);
     const int chunk = (lane & 7) ^ (lane >> 3);
     a_off[j] = min(m0 + row, M - 1) * K + 8 * chunk;
   }
-  // packed weights: instruction j of wave w covers columns 32q .. 32q + 31,
-  // q = 4j + w (j = 0, 1); lane l: column 32q + l / 2, bytes 16 (l % 2) ..
-  int b_off[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int col = 32 * (4 * j + wave) + (lane >> 1);
-    b_off[j] = min(n0 + col, N - 1) * (K / 2) + 16 * (lane & 1);
-  }
-  // scale bytes: wave w covers columns 64w .. 64w + 63, 4 bytes each
-  const int s_off = min(n0 + 64 * wave + lane, N - 1) * cols;
+  // packed weights: wave w covers columns 32w .. 32w + 31; lane l: column
+  // 32w + l / 2, bytes 16 (l % 2) .. + 15
+  const int b_off = min(n0 + 32 * wave + (lane >> 1), N - 1) * (K / 2) + 16 * (lane & 1);
+  // scale bytes: wave w covers columns 64 (w % 4) .. + 63, 4 bytes each
+  // (waves 4..7 repeat waves 0..3: identical data to identical addresses,
+  // which keeps the number of loads per wave uniform)
+  const int s_col = 64 * (wave & 3) + lane;
+  const int s_off = min(n0 + s_col, N - 1) * cols;
 
   const int nsteps = K / BK;
   auto issue = [&](int step, LargeStage<T>& st) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      load_lds<16>(A + a_off[j] + step * BK, &st.a[(4 * j + wave) * 8 * kLdsRow]);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) load_lds<16>(B + b_off[j] + step * (BK / 2), &st.b[(4 * j + wave) * 32 * 32]);
-    load_lds<4>(scales + s_off + step * (BK / 16), &st.s[64 * wave * 4]);
+    for (int j = 0; j < 4; ++j)
+      load_lds<16>(A + a_off[j] + step * BK, &st.a[(8 * j + wave) * 8 * kLdsRow]);
+    load_lds<16>(B + b_off + step * (BK / 2), &st.b[wave * 32 * 32]);
+    load_lds<4>(scales + s_off + step * (BK / 16), &st.s[64 * (wave & 3) * 4]);
   };
-  constexpr int kLoadsPerStep = 11;  // per wave: 8 + 2 + 1 direct loads
+  constexpr int kLoadsPerStep = 6;  // per wave: 4 + 1 + 1 direct loads
 
-  f32x4 acc[8][8];
+  f32x4 acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // One step: two halves of 8 k per lane.  The LDS reads of both halves and
-  // the weight decode of the first are issued up front; the decode of the
-  // second half (VALU) is interleaved with the 64 MFMAs of the first, so the
-  // vector ALU works while the matrix cores are busy.
   auto compute = [&](const LargeStage<T>& st) {
-    u32x2 bw[8];
-    float sc[8];
+    u32x2 bw[4];
+    float sc[4];
 #pragma unroll
-    for (int ns = 0; ns < 8; ++ns) {
-      const int col = 128 * wn + 16 * ns + li;
+    for (int ns = 0; ns < 4; ++ns) {
+      const int col = 64 * wn + 16 * ns + li;
       bw[ns] = *reinterpret_cast<const u32x2*>(&st.b[col * 32 + 8 * g]);
       sc[ns] = e4m3_to_f32<0>(st.s[col * 4 + g]);
     }
-    V aop[2][8];
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int s = 0; s < 2; ++s) {
+      V aop[8];
 #pragma unroll
       for (int ms = 0; ms < 8; ++ms)
-        aop[s][ms] = *reinterpret_cast<const V*>(&st.a[lds_index(128 * wm + 16 * ms + li, 2 * g + s)]);
-    V bop[2][8];
+        aop[ms] = *reinterpret_cast<const V*>(&st.a[lds_index(128 * wm + 16 * ms + li, 2 * g + s)]);
+      V bop[4];
 #pragma unroll
-    for (int ns = 0; ns < 8; ++ns) bop[0][ns] = Tr::decode8(bw[ns][0], Tr::make_scale(sc[ns]));
-    __builtin_amdgcn_sched_barrier(0);
+      for (int ns = 0; ns < 4; ++ns) bop[ns] = Tr::decode8(bw[ns][s], Tr::make_scale(sc[ns]));
 #pragma unroll
-    for (int ms = 0; ms < 8; ++ms)
+      for (int ms = 0; ms < 8; ++ms)
 #pragma unroll
-      for (int ns = 0; ns < 8; ++ns) acc[ms][ns] = Tr::mfma(aop[0][ms], bop[0][ns], acc[ms][ns]);
-#pragma unroll
-    for (int ns = 0; ns < 8; ++ns) bop[1][ns] = Tr::decode8(bw[ns][1], Tr::make_scale(sc[ns]));
-    // 64 MFMAs, each followed by up to 2 VALU instructions of the decode
-#pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = Tr::mfma(aop[ms], bop[ns], acc[ms][ns]);
     }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ms = 0; ms < 8; ++ms)
-#pragma unroll
-      for (int ns = 0; ns < 8; ++ns) acc[ms][ns] = Tr::mfma(aop[1][ms], bop[1][ns], acc[ms][ns]);
   };
 
-  // one step on stage S (the stage of step + 2 is S + 2 mod 3)
-  auto do_step = [&](int step, LargeStage<T>& cur, LargeStage<T>& ahead2) {
+  auto do_step = [&](int step, const LargeStage<T>& cur, LargeStage<T>& ahead2) {
     const bool issue2 = step + 2 < nsteps;
     if (issue2) issue(step + 2, ahead2);
     compute(cur);
@@ -395,34 +374,65 @@ __global__ __launch_bounds__(256) void gemm_fp4_large_kernel(
       wait_barrier<0>();
   };
 
-  issue(0, st0);
-  if (nsteps > 1) issue(1, st1);
+  issue(0, st[0]);
+  if (nsteps > 1) issue(1, st[1]);
   if (nsteps > 1)
     wait_barrier<kLoadsPerStep>();
   else
     wait_barrier<0>();
   for (int step = 0; step < nsteps; step += 3) {
-    do_step(step, st0, st2);
-    if (step + 1 < nsteps) do_step(step + 1, st1, st0);
-    if (step + 2 < nsteps) do_step(step + 2, st2, st1);
+    do_step(step, st[0], st[2]);
+    if (step + 1 < nsteps) do_step(step + 1, st[1], st[0]);
+    if (step + 2 < nsteps) do_step(step + 2, st[2], st[1]);
   }
 
-  // epilogue: lane (li, g) holds columns n0 + 128 wn + 16 ns + li and rows
-  // m0 + 128 wm + 16 ms + 4 g + r
+  // Epilogue: lane (li, g) holds columns 64 wn + 16 ns + li and rows
+  // 128 wm + 16 ms + 4 g + r of the tile.  Y = acc * ws2 + bias, rounded once
+  // to T, is staged in LDS (the operand stages are free now) one 128-row half
+  // at a time and written back in whole 16-byte row pieces; tiles on the
+  // ragged edge, or outputs that are not 16-byte aligned, store element-wise.
   const float ws2 = *ws2p;
+  constexpr int kOutPitch = L_BN + 8;  // elements per staged row (breaks bank aliasing)
+  T* out = reinterpret_cast<T*>(&st[0]);
+  const bool wide = (N % 8 == 0) && (reinterpret_cast<uintptr_t>(Y) % 16 == 0) && n0 + L_BN <= N;
+  float bsum[4];
 #pragma unroll
-  for (int ns = 0; ns < 8; ++ns) {
-    const int n = n0 + 128 * wn + 16 * ns + li;
-    if (n >= N) continue;
-    const float b = bias ? static_cast<float>(bias[n]) : 0.0f;
+  for (int ns = 0; ns < 4; ++ns) {
+    const int n = min(n0 + 64 * wn + 16 * ns + li, N - 1);
+    bsum[ns] = bias ? static_cast<float>(bias[n]) : 0.0f;
+  }
 #pragma unroll
-    for (int ms = 0; ms < 8; ++ms) {
+  for (int half = 0; half < 2; ++half) {
+    if (wm == half) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + 128 * wm + 16 * ms + 4 * g + r;
-        if (m < M) Y[static_cast<size_t>(m) * N + n] = round_to<T>(fmaf(acc[ms][ns][r], ws2, b));
+      for (int ms = 0; ms < 8; ++ms)
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            out[(16 * ms + 4 * g + r) * kOutPitch + 64 * wn + 16 * ns + li] =
+                round_to<T>(fmaf(acc[ms][ns][r], ws2, bsum[ns]));
+    }
+    __syncthreads();
+    const int mrow0 = m0 + 128 * half;
+    if (wide) {
+      // 128 rows x 32 pieces of 16 bytes, 8 per thread
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int q = tid + 512 * i;
+        const int row = q >> 5, piece = q & 31;
+        if (mrow0 + row < M)
+          *reinterpret_cast<u32x4*>(&Y[static_cast<size_t>(mrow0 + row) * N + n0 + 8 * piece]) =
+              *reinterpret_cast<const u32x4*>(&out[row * kOutPitch + 8 * piece]);
+      }
+    } else {
+      for (int q = tid; q < 128 * L_BN; q += 512) {
+        const int row = q / L_BN, col = q % L_BN;
+        if (mrow0 + row < M && n0 + col < N)
+          Y[static_cast<size_t>(mrow0 + row) * N + n0 + col] = out[row * kOutPitch + col];
       }
     }
+    __syncthreads();
   }
 }
 
@@ -453,7 +463,7 @@ int launch_fp4_large(const MatmulArgs& a) {
     return launch<T, false>(a);
   const int64_t tiles_m = (a.M + L_BM - 1) / L_BM, tiles_n = (a.N + L_BN - 1) / L_BN;
   if (tiles_m * tiles_n > 0x7fffffff) return -1;
-  hipLaunchKernelGGL((gemm_fp4_large_kernel<T>), dim3(static_cast<unsigned>(tiles_m * tiles_n)), dim3(256), 0,
+  hipLaunchKernelGGL((gemm_fp4_large_kernel<T>), dim3(static_cast<unsigned>(tiles_m * tiles_n)), dim3(512), 0,
                      static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.A), a.B,
                      static_cast<const uint8_t*>(a.scales), a.ws2, static_cast<const T*>(a.bias),
                      static_cast<T*>(a.Y), static_cast<int>(a.M), static_cast<int>(a.N), static_cast<int>(a.K),
