@@ -45,8 +45,12 @@ namespace {
 constexpr int BN = 256, BK = 64;
 constexpr int kLdsRow = BK;  // elements per LDS row (no padding: XOR swizzle)
 
+// 16-byte chunk c of row r sits in slot c ^ ((r >> 1) & 7): the 16 rows read
+// by a 16-lane group at one logical chunk land in 16 distinct 16-byte slots of
+// a 256-byte LDS line (rows are 128 bytes), so ds_read_b128 is conflict free.
+__device__ __forceinline__ int lds_swz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int lds_index(int row, int chunk) {
-  return row * kLdsRow + ((chunk ^ (row & 7)) << 3);
+  return row * kLdsRow + ((chunk ^ lds_swz(row)) << 3);
 }
 
 template <typename T, bool FP8, int WM>
@@ -311,12 +315,15 @@ __global__ __launch_bounds__(512) void gemm_fp4_large_kernel(
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = 8 * (8 * j + wave) + (lane >> 3);
-    const int chunk = (lane & 7) ^ (lane >> 3);
+    const int chunk = (lane & 7) ^ lds_swz(row);
     a_off[j] = min(m0 + row, M - 1) * K + 8 * chunk;
   }
-  // packed weights: wave w covers columns 32w .. 32w + 31; lane l: column
-  // 32w + l / 2, bytes 16 (l % 2) .. + 15
-  const int b_off = min(n0 + 32 * wave + (lane >> 1), N - 1) * (K / 2) + 16 * (lane & 1);
+  // packed weights: wave w covers columns 32w .. 32w + 31; lane l lands in
+  // column 32w + l / 2, 16-byte half l % 2, which holds global half
+  // (l % 2) ^ ((column / 8) % 2): the 16 columns read by a 16-lane group then
+  // fall in distinct banks
+  const int b_col = 32 * wave + (lane >> 1);
+  const int b_off = min(n0 + b_col, N - 1) * (K / 2) + 16 * ((lane & 1) ^ ((b_col >> 3) & 1));
   // scale bytes: wave w covers columns 64 (w % 4) .. + 63, 4 bytes each
   // (waves 4..7 repeat waves 0..3: identical data to identical addresses,
   // which keeps the number of loads per wave uniform)
@@ -345,7 +352,7 @@ __global__ __launch_bounds__(512) void gemm_fp4_large_kernel(
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) {
       const int col = 64 * wn + 16 * ns + li;
-      bw[ns] = *reinterpret_cast<const u32x2*>(&st.b[col * 32 + 8 * g]);
+      bw[ns] = *reinterpret_cast<const u32x2*>(&st.b[col * 32 + 16 * ((g >> 1) ^ ((col >> 3) & 1)) + 8 * (g & 1)]);
       sc[ns] = e4m3_to_f32<0>(st.s[col * 4 + g]);
     }
 #pragma unroll
