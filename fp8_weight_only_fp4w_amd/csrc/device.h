@@ -172,6 +172,23 @@ __device__ __forceinline__ T round_to(float x) {
   return static_cast<T>(f32_barrier(x));
 }
 
+// 8 E4M3 codes of (lo, hi), low byte first, times an FP32 scale -> 8 x T:
+// each product is rounded once to FP32 and once to T, the dequantized weight
+// in the activation type (exact for the E4M3 code, rounded for the scale).
+template <typename T>
+__device__ __forceinline__ typename ActTraits<T>::vec8 decode8_fp8_scaled(uint32_t lo, uint32_t hi, float s) {
+  const f32x2 p0 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(lo), false);
+  const f32x2 p1 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(lo), true);
+  const f32x2 p2 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(hi), false);
+  const f32x2 p3 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(hi), true);
+  typename ActTraits<T>::vec8 r;
+  r[0] = round_to<T>(p0.x * s); r[1] = round_to<T>(p0.y * s);
+  r[2] = round_to<T>(p1.x * s); r[3] = round_to<T>(p1.y * s);
+  r[4] = round_to<T>(p2.x * s); r[5] = round_to<T>(p2.y * s);
+  r[6] = round_to<T>(p3.x * s); r[7] = round_to<T>(p3.y * s);
+  return r;
+}
+
 // ------------------------------------------------------------------ division
 //
 // n / d for 32-bit n by a divisor d >= 1 fixed at launch (Granlund &

@@ -250,11 +250,11 @@ __global__ __launch_bounds__(256 * WM) void gemm_kernel(
 //    contiguous range of tiles, walked in groups of 8 tile rows.
 constexpr int L_BM = 256, L_BN = 256;
 
-template <typename T>
+template <typename T, bool FP8>
 struct LargeStage {
-  T a[L_BM * kLdsRow];      // 32 KiB
-  uint8_t b[L_BN * 32];     // 8 KiB
-  uint8_t s[L_BN * 4];      // 1 KiB
+  T a[L_BM * kLdsRow];               // 32 KiB
+  uint8_t b[L_BN * (FP8 ? 64 : 32)];  // 16 / 8 KiB of weight bytes
+  uint8_t s[L_BN * 4];               // 1 KiB: 4 E4M3 bytes or one FP32 scale per column
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -281,14 +281,15 @@ __device__ __forceinline__ void wait_barrier() {
   __asm__ volatile("" ::: "memory");
 }
 
-template <typename T>
-__global__ __launch_bounds__(512) void gemm_fp4_large_kernel(
+template <typename T, bool FP8>
+__global__ __launch_bounds__(512) void gemm_large_kernel(
     const T* __restrict__ A, const uint8_t* __restrict__ B, const uint8_t* __restrict__ scales,
     const float* __restrict__ ws2p, const T* __restrict__ bias, T* __restrict__ Y, int M, int N,
-    int K, int cols, int tiles_m, int tiles_n) {
+    int K, int cols, int bs, int tiles_m, int tiles_n) {
   typedef ActTraits<T> Tr;
   typedef typename Tr::vec8 V;
-  __shared__ __attribute__((aligned(16))) LargeStage<T> st[3];
+  typedef LargeStage<T, FP8> Stage;
+  __shared__ __attribute__((aligned(16))) Stage st[3];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -318,27 +319,49 @@ __global__ __launch_bounds__(512) void gemm_fp4_large_kernel(
     const int chunk = (lane & 7) ^ lds_swz(row);
     a_off[j] = min(m0 + row, M - 1) * K + 8 * chunk;
   }
-  // packed weights: wave w covers columns 32w .. 32w + 31; lane l lands in
-  // column 32w + l / 2, 16-byte half l % 2, which holds global half
-  // (l % 2) ^ ((column / 8) % 2): the 16 columns read by a 16-lane group then
-  // fall in distinct banks
-  const int b_col = 32 * wave + (lane >> 1);
-  const int b_off = min(n0 + b_col, N - 1) * (K / 2) + 16 * ((lane & 1) ^ ((b_col >> 3) & 1));
-  // scale bytes: wave w covers columns 64 (w % 4) .. + 63, 4 bytes each
-  // (waves 4..7 repeat waves 0..3: identical data to identical addresses,
-  // which keeps the number of loads per wave uniform)
+  // Weights.  FP4 (32 bytes per column and step): instruction j of wave w
+  // covers columns 32q .. 32q + 31, q = w; lane l lands in column 32q + l / 2,
+  // 16-byte piece l % 2.  FP8 (64 bytes): q = 8j + w, 16 columns per
+  // instruction, lane l in column 16q + l / 4, piece l % 4.  Pieces are
+  // swizzled with the column (global piece = LDS piece ^ bit pattern of the
+  // column) so the 16 columns read by a 16-lane group fall in distinct banks.
+  constexpr int kBBytes = FP8 ? 64 : 32;            // per column and step
+  constexpr int kBLoads = FP8 ? 2 : 1;              // direct loads per wave and step
+  constexpr int kColsPerLoad = 1024 / kBBytes;      // columns per direct load
+  constexpr int kPieces = kBBytes / 16;
+  auto b_swz = [](int col) { return FP8 ? (col & 3) : ((col >> 3) & 1); };
+  const size_t b_row = FP8 ? static_cast<size_t>(K) : static_cast<size_t>(K / 2);
+  int b_off[kBLoads];
+#pragma unroll
+  for (int j = 0; j < kBLoads; ++j) {
+    const int col = kColsPerLoad * (8 * j + wave) + lane / kPieces;
+    const int piece = (lane % kPieces) ^ b_swz(col);
+    b_off[j] = min(n0 + col, N - 1) * static_cast<int>(b_row) + 16 * piece;
+  }
+  // scales: wave w covers columns 64 (w % 4) .. + 63, 4 bytes each: the 4
+  // E4M3 bytes of the step (FP4) or the FP32 scale of the step's block (FP8;
+  // block_size % 64 == 0, so a step lies in one block).  Waves 4..7 repeat
+  // waves 0..3: identical data to identical addresses, which keeps the number
+  // of loads per wave uniform.
   const int s_col = 64 * (wave & 3) + lane;
-  const int s_off = min(n0 + s_col, N - 1) * cols;
+  const int s_off = min(n0 + s_col, N - 1) * cols;  // elements (bytes FP4, floats FP8)
 
   const int nsteps = K / BK;
-  auto issue = [&](int step, LargeStage<T>& st) {
+  auto issue = [&](int step, Stage& st) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       load_lds<16>(A + a_off[j] + step * BK, &st.a[(8 * j + wave) * 8 * kLdsRow]);
-    load_lds<16>(B + b_off + step * (BK / 2), &st.b[wave * 32 * 32]);
-    load_lds<4>(scales + s_off + step * (BK / 16), &st.s[64 * (wave & 3) * 4]);
+#pragma unroll
+    for (int j = 0; j < kBLoads; ++j)
+      load_lds<16>(B + b_off[j] + static_cast<size_t>(step) * (FP8 ? BK : BK / 2), &st.b[(8 * j + wave) * 1024]);
+    if constexpr (FP8) {
+      const int col = min(step * BK / bs, cols - 1);
+      load_lds<4>(reinterpret_cast<const float*>(scales) + s_off + col, &st.s[64 * (wave & 3) * 4]);
+    } else {
+      load_lds<4>(scales + s_off + step * (BK / 16), &st.s[64 * (wave & 3) * 4]);
+    }
   };
-  constexpr int kLoadsPerStep = 6;  // per wave: 4 + 1 + 1 direct loads
+  constexpr int kLoadsPerStep = 4 + kBLoads + 1;  // direct loads per wave and step
 
   f32x4 acc[8][4];
 #pragma unroll
@@ -346,14 +369,22 @@ __global__ __launch_bounds__(512) void gemm_fp4_large_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const LargeStage<T>& st) {
-    u32x2 bw[4];
+  auto compute = [&](const Stage& st) {
+    // lane (li, g): k 16g .. 16g + 15 of its 4 columns (FP4 8 bytes, FP8 16)
+    u32x4 bw[4];
     float sc[4];
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) {
       const int col = 64 * wn + 16 * ns + li;
-      bw[ns] = *reinterpret_cast<const u32x2*>(&st.b[col * 32 + 16 * ((g >> 1) ^ ((col >> 3) & 1)) + 8 * (g & 1)]);
-      sc[ns] = e4m3_to_f32<0>(st.s[col * 4 + g]);
+      if constexpr (FP8) {
+        bw[ns] = *reinterpret_cast<const u32x4*>(&st.b[col * 64 + 16 * (g ^ b_swz(col))]);
+        sc[ns] = *reinterpret_cast<const float*>(&st.s[col * 4]);
+      } else {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(&st.b[col * 32 + 16 * ((g >> 1) ^ b_swz(col)) + 8 * (g & 1)]);
+        bw[ns].x = v.x;
+        bw[ns].y = v.y;
+        sc[ns] = e4m3_to_f32<0>(st.s[col * 4 + g]);
+      }
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -363,7 +394,12 @@ __global__ __launch_bounds__(512) void gemm_fp4_large_kernel(
         aop[ms] = *reinterpret_cast<const V*>(&st.a[lds_index(128 * wm + 16 * ms + li, 2 * g + s)]);
       V bop[4];
 #pragma unroll
-      for (int ns = 0; ns < 4; ++ns) bop[ns] = Tr::decode8(bw[ns][s], Tr::make_scale(sc[ns]));
+      for (int ns = 0; ns < 4; ++ns) {
+        if constexpr (FP8)
+          bop[ns] = decode8_fp8_scaled<T>(bw[ns][2 * s], bw[ns][2 * s + 1], sc[ns]);
+        else
+          bop[ns] = Tr::decode8(bw[ns][s], Tr::make_scale(sc[ns]));
+      }
 #pragma unroll
       for (int ms = 0; ms < 8; ++ms)
 #pragma unroll
@@ -371,7 +407,7 @@ __global__ __launch_bounds__(512) void gemm_fp4_large_kernel(
     }
   };
 
-  auto do_step = [&](int step, const LargeStage<T>& cur, LargeStage<T>& ahead2) {
+  auto do_step = [&](int step, const Stage& cur, Stage& ahead2) {
     const bool issue2 = step + 2 < nsteps;
     if (issue2) issue(step + 2, ahead2);
     compute(cur);
@@ -398,7 +434,7 @@ __global__ __launch_bounds__(512) void gemm_fp4_large_kernel(
   // to T, is staged in LDS (the operand stages are free now) one 128-row half
   // at a time and written back in whole 16-byte row pieces; tiles on the
   // ragged edge, or outputs that are not 16-byte aligned, store element-wise.
-  const float ws2 = *ws2p;
+  const float ws2 = FP8 ? 1.0f : *ws2p;
   constexpr int kOutPitch = L_BN + 8;  // elements per staged row (breaks bank aliasing)
   T* out = reinterpret_cast<T*>(&st[0]);
   const bool wide = (N % 8 == 0) && (reinterpret_cast<uintptr_t>(Y) % 16 == 0) && n0 + L_BN <= N;
@@ -461,29 +497,31 @@ int launch(const MatmulArgs& a) {
 
 }  // namespace
 
-template <typename T>
-int launch_fp4_large(const MatmulArgs& a) {
+template <typename T, bool FP8>
+int launch_large(const MatmulArgs& a) {
   if (a.M > 0x7fffffff || a.N > 0x7fffffff || a.K > 0x7fffffff) return -1;
   // 32-bit element offsets inside the kernel
-  if (a.N * (a.K / 2) >= (int64_t(1) << 31) || a.N * a.scale_cols >= (int64_t(1) << 31) ||
-      static_cast<int64_t>(L_BM) * a.K >= (int64_t(1) << 31))
-    return launch<T, false>(a);
+  const int64_t b_bytes = a.N * (FP8 ? a.K : a.K / 2);
+  if (b_bytes >= (int64_t(1) << 31) || a.N * a.scale_cols >= (int64_t(1) << 31) ||
+      static_cast<int64_t>(L_BM) * a.K >= (int64_t(1) << 31) || a.M * a.K >= (int64_t(1) << 31))
+    return launch<T, FP8>(a);
   const int64_t tiles_m = (a.M + L_BM - 1) / L_BM, tiles_n = (a.N + L_BN - 1) / L_BN;
   if (tiles_m * tiles_n > 0x7fffffff) return -1;
-  hipLaunchKernelGGL((gemm_fp4_large_kernel<T>), dim3(static_cast<unsigned>(tiles_m * tiles_n)), dim3(512), 0,
+  hipLaunchKernelGGL((gemm_large_kernel<T, FP8>), dim3(static_cast<unsigned>(tiles_m * tiles_n)), dim3(512), 0,
                      static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.A), a.B,
                      static_cast<const uint8_t*>(a.scales), a.ws2, static_cast<const T*>(a.bias),
                      static_cast<T*>(a.Y), static_cast<int>(a.M), static_cast<int>(a.N), static_cast<int>(a.K),
-                     static_cast<int>(a.scale_cols), static_cast<int>(tiles_m), static_cast<int>(tiles_n));
+                     static_cast<int>(a.scale_cols), static_cast<int>(a.block_size), static_cast<int>(tiles_m),
+                     static_cast<int>(tiles_n));
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_fp4_gemm(const MatmulArgs& a) {
-  return a.act == Act::BF16 ? launch_fp4_large<__bf16>(a) : launch_fp4_large<_Float16>(a);
+  return a.act == Act::BF16 ? launch_large<__bf16, false>(a) : launch_large<_Float16, false>(a);
 }
 
 int launch_fp8_gemm(const MatmulArgs& a) {
-  return a.act == Act::BF16 ? launch<__bf16, true>(a) : launch<_Float16, true>(a);
+  return a.act == Act::BF16 ? launch_large<__bf16, true>(a) : launch_large<_Float16, true>(a);
 }
 
 }  // namespace fp4w
