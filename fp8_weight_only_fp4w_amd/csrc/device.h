@@ -244,6 +244,13 @@ __device__ __forceinline__ uint32_t vgpr(uint32_t x) {
 __device__ __forceinline__ u32x4 buf_load_b128(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, vgpr(off), 0, 0));
 }
+// Per-lane offset `voff` plus a wave-uniform offset `soff` (a scalar
+// register: no per-lane address arithmetic).  The caller keeps voff + soff +
+// 16 inside the bytes the lane may read: only `voff` is guaranteed to take
+// part in the range check.
+__device__ __forceinline__ u32x4 buf_load_b128_so(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
 __device__ __forceinline__ u32x2 buf_load_b64(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, vgpr(off), 0, 0));
 }

@@ -171,20 +171,32 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
   // bytes of each of 16 rows).  FP8: lane group g loads k 128w + 16g .. + 15
   // and 128w + 64 + 16g .. + 15 (two instructions, each 64 contiguous bytes
   // per row).
-  auto load = [&](Pos p, RawT& r) {
-    const int t = p.tg * TPW + tw;
+  // Load side of the pipeline: position and the (wave-uniform) descriptors
+  // of its tile, recomputed only when the position enters a new tile.
+  Pos lp{static_cast<int>(blockIdx.x), 0};  // next window to load
+  rsrc_t br, sr, biasr;
+  auto set_load_tile = [&]() {
+    const int t = lp.tg * TPW + tw;
     const int rows = max(0, min(16, N - 16 * t));
     const size_t n0 = static_cast<size_t>(16) * t;
-    const rsrc_t br = make_rsrc(B + n0 * row_bytes, rows * row_bytes);
-    const rsrc_t sr = make_rsrc(static_cast<const uint8_t*>(scales) + n0 * srow_bytes, rows * srow_bytes);
-    const rsrc_t biasr = make_rsrc(bias + n0, bias ? rows * 2u : 0u);
+    br = make_rsrc(B + n0 * row_bytes, rows * row_bytes);
+    sr = make_rsrc(static_cast<const uint8_t*>(scales) + n0 * srow_bytes, rows * srow_bytes);
+    biasr = make_rsrc(bias + n0, bias ? rows * 2u : 0u);
+  };
+  set_load_tile();
+  // per-lane byte offsets of the lane's column (window 0); the window's own
+  // offset is wave-uniform and rides in the scalar offset of the load.  Lanes
+  // past the tile's last row are out of range through their own offset.
+  const uint32_t w_lane = li * row_bytes + 16u * g;
+
+  auto load = [&](RawT& r) {
     // bias and scale pieces are only requested for the windows that carry
     // them (uniform branches; an out-of-range request would still occupy the
     // load pipeline for all 64 lanes)
-    if (p.j == 0) r.bias = buf_load_u16(biasr, 2u * li);
-    const int w = ks * nws + p.j;
+    if (lp.j == 0) r.bias = buf_load_u16(biasr, 2u * li);
+    const int w = ks * nws + lp.j;
     const bool ok = w < NW;
-    const bool piece = ok && p.j % SW == 0;
+    const bool piece = ok && lp.j % SW == 0;
     if constexpr (FP8) {
       const uint32_t off = ok ? li * row_bytes + 128u * w + 16u * g : kOutOfRange;
       r.w0 = buf_load_b128(br, off);
@@ -199,7 +211,9 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
         r.a[3] = buf_load_b128(a_rsrc, aoff + 144u);
       }
     } else {
-      r.w = buf_load_b128(br, ok ? li * row_bytes + 64u * w + 16u * g : kOutOfRange);
+      // windows past NW re-read window NW - 1 (inside the row) and are
+      // cancelled by zero scales when multiplied
+      r.w = buf_load_b128_so(br, w_lane, 64u * static_cast<uint32_t>(min(w, NW - 1)));
       // E4M3 scales of windows w .. w + 7 (bytes past the row are never used)
       if (piece) r.sc = buf_load_b128(sr, li * srow_bytes + 8u * w + 16u * g);
       if constexpr (ACT_REG) {
@@ -212,12 +226,16 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
         }
       }
     }
+    if (++lp.j == nws) {
+      lp.j = 0;
+      lp.tg += stride;
+      set_load_tile();
+    }
   };
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   uint32_t tbias = 0;  // bias bits of the lane's column, current tile
   RawT raw[S];
-  Pos lp{static_cast<int>(blockIdx.x), 0};  // next window to load
   Pos cp{static_cast<int>(blockIdx.x), 0};  // window being multiplied
 
   if constexpr (ACT_LDS) {
@@ -250,8 +268,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
     fill_load(threadIdx.x, v);
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      load(lp, raw[d]);
-      lp.advance(nws, stride);
+      load(raw[d]);
     }
     fill_store(threadIdx.x, v);
     for (uint32_t q0 = threadIdx.x + 8u * kStep; q0 < nload; q0 += 8u * kStep) {
@@ -264,8 +281,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
   } else {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      load(lp, raw[d]);
-      lp.advance(nws, stride);
+      load(raw[d]);
     }
   }
 
@@ -304,7 +320,9 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
     } else {
       typedef ActTraits<T> Tr;
       typedef typename Tr::vec8 V;
-      const u32x2 sb = *reinterpret_cast<const u32x2*>(slice + 64 * li + 8 * (j % SW));
+      // windows past NW (re-reads of window NW - 1) contribute nothing
+      const u32x2 sb = ks * nws + j < NW ? *reinterpret_cast<const u32x2*>(slice + 64 * li + 8 * (j % SW))
+                                          : u32x2{0u, 0u};
       // activations of the lane: 4 x 16 bytes per row half; chunk i = 2s + p
       // holds k 32g + 16s + 8p .. + 7 of the window (piece p of set s)
       u32x4 av[R][4];
@@ -390,8 +408,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
   for (int f0 = 0; f0 < total; f0 += S) {
 #pragma unroll
     for (int u = 0; u < S; ++u) {
-      load(lp, raw[(u + D) % S]);
-      lp.advance(nws, stride);
+      load(raw[(u + D) % S]);
       if (f0 + u < total) consume(raw[u]);
     }
   }
