@@ -36,6 +36,10 @@ FP4_CASES = [
     (9, 300, 128, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMM, fw.PATH_FP4_GENERIC]),
     (300, 700, 640, 16, "fp16", True, "ceil", [fw.PATH_FP4_GEMM]),  # ragged M and N
     (513, 256, 64, 16, "bf16", False, "ceil", [fw.PATH_FP4_GEMM]),
+    # 3 x 8 = 24 tiles of 256 x 256 (a multiple of 8: the XCD tile remap is
+    # active), ragged M and N, an odd number of K steps; the last column tile
+    # takes the element-wise epilogue, the others the 16-byte one
+    (700, 1800, 448, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMM]),
     (40, 96, 96, 16, "bf16", True, "ceil", [fw.PATH_FP4_GENERIC]),  # K % 64 != 0
     (6, 50, 40, 16, "fp16", True, "floor", [fw.PATH_FP4_GENERIC]),  # partial block, floor cols
     (4, 33, 30, 15, "bf16", True, "ceil", [fw.PATH_FP4_GENERIC]),   # odd block size
@@ -143,6 +147,7 @@ FP8_CASES = [
     (1, 1000, 1280, 256, "fp16", True, "ceil", [fw.PATH_FP8_GEMV]),
     (7, 64, 384, 256, "bf16", True, "floor", [fw.PATH_FP8_GEMV, fw.PATH_FP8_GENERIC]),  # partial block
     (300, 520, 640, 128, "bf16", True, "ceil", [fw.PATH_FP8_GEMM]),
+    (700, 1800, 448, 64, "fp16", False, "ceil", [fw.PATH_FP8_GEMM]),  # 24 tiles, ragged, odd K steps
     (64, 256, 448, 64, "fp16", False, "ceil", [fw.PATH_FP8_GEMM]),
     (33, 100, 320, 128, "bf16", True, "floor", [fw.PATH_FP8_GEMM, fw.PATH_FP8_GENERIC]),  # partial block
     (5, 40, 208, 128, "bf16", True, "ceil", [fw.PATH_FP8_GENERIC]),
