@@ -21,6 +21,13 @@ Formats:
 
 Decoding is a pure function of the code; the tables are those functions
 evaluated on every code.
+
+Encoding (FP32 -> E4M3 "fn", for the optional W8A8 activation path of
+[FP8 doc] §6): the nearest finite E4M3 value, ties to the code with an even
+mantissa, magnitudes beyond 448 saturated to 448, NaN to NaN.  The pages
+write fp8_e4m3(.) without naming a rounding or overflow rule; round to
+nearest even with saturation to the largest finite value is the reading
+taken (an "fn" format has no infinity to overflow to).
 """
 
 import math
@@ -59,6 +66,31 @@ def e4m3fn_value(byte: int) -> float:
 # Every code evaluated once; indexing these is the decode step.
 E2M1_TABLE = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
 E4M3FN_TABLE = np.array([e4m3fn_value(b) for b in range(256)], dtype=np.float64)
+
+
+# Finite positive E4M3 magnitudes in code order 0x00 .. 0x7E (increasing).
+_E4M3_POS = E4M3FN_TABLE[:0x7F]
+E4M3_MAX = 448.0
+
+
+def e4m3fn_encode(x) -> np.ndarray:
+    """float values -> E4M3 "fn" codes (uint8): nearest representable value,
+    ties to even code, |x| > 448 saturated to 448, NaN -> 0x7F, sign kept
+    (-0.0 -> 0x80).  A plain search over the 127 finite magnitudes."""
+    x = np.asarray(x, dtype=np.float64)
+    mag = np.abs(x)
+    nan = np.isnan(x)
+    m = np.where(nan, 0.0, np.minimum(mag, E4M3_MAX))
+    hi = np.searchsorted(_E4M3_POS, m, side="left")      # first magnitude >= m
+    hi = np.minimum(hi, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = m - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - m
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    sign = np.signbit(x).astype(np.int64) << 7
+    out = (code | sign).astype(np.uint8)
+    return np.where(nan, np.uint8(0x7F), out).astype(np.uint8)
 
 
 def f32_to_f16_bits(x) -> np.ndarray:

@@ -44,6 +44,7 @@ import numpy as np
 from .codecs import (
     E2M1_TABLE,
     E4M3FN_TABLE,
+    e4m3fn_encode,
     activation_to_f64,
     bits_to_f64,
     f32_to_bf16_bits,
@@ -118,6 +119,26 @@ def dequant_fp8_output_bits(B_fp8, b_scale, block_size: int, dtype: str) -> np.n
         return f32_to_f16_bits(as_f32)
     if dtype == "bf16":
         return f32_to_bf16_bits(as_f32)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def qdq_activation_fp8_bits(A_bits, dtype: str, a_scale) -> np.ndarray:
+    """The optional W8A8 activation of [FP8 doc] §6,
+        A_deq = fp8_e4m3(A / a_scale) * a_scale,
+    as uint16 bits of T, step by step: A (T) -> FP32; divide by the FP32
+    a_scale (one FP32 rounding); encode to E4M3 (e4m3fn_encode); decode and
+    multiply by a_scale (exact in float64, then one FP32 rounding); round the
+    FP32 value to T."""
+    a32 = activation_to_f64(A_bits, dtype).astype(np.float32)
+    s32 = np.float32(a_scale)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        q = (a32 / s32).astype(np.float32)
+    codes = e4m3fn_encode(q)
+    deq = (E4M3FN_TABLE[codes] * np.float64(s32)).astype(np.float32)
+    if dtype == "fp16":
+        return f32_to_f16_bits(deq)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(deq)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 

@@ -165,3 +165,61 @@ def test_bits_to_f64_matches_torch(dtype):
     nan = np.isnan(lib)
     assert np.array_equal(np.isnan(ours), nan)
     assert np.array_equal(ours[~nan], lib[~nan])
+
+
+# ---------------------------------------------------------------------------
+# E4M3 encoder (optional W8A8 activation path, [FP8 doc] §6)
+# ---------------------------------------------------------------------------
+
+def _finite_codes():
+    c = np.arange(256)
+    return c[~np.isnan(codecs.E4M3FN_TABLE)]
+
+
+def test_e4m3fn_encode_round_trips_every_finite_code():
+    c = _finite_codes()
+    got = codecs.e4m3fn_encode(codecs.E4M3FN_TABLE[c])
+    assert np.array_equal(got.astype(np.int64), c)
+
+
+def test_e4m3fn_encode_midpoints_go_to_even_code_and_neighbours_to_nearest():
+    pos = np.arange(0, 0x7E)                       # pairs (c, c+1) of finite positive codes
+    lo = codecs.E4M3FN_TABLE[pos]
+    hi = codecs.E4M3FN_TABLE[pos + 1]
+    mid = (lo + hi) / 2
+    want_mid = np.where(pos % 2 == 0, pos, pos + 1)
+    assert np.array_equal(codecs.e4m3fn_encode(mid).astype(np.int64), want_mid)
+    assert np.array_equal(codecs.e4m3fn_encode(-mid).astype(np.int64), want_mid | 0x80)
+    gap = hi - lo
+    assert np.array_equal(codecs.e4m3fn_encode(mid - gap / 8).astype(np.int64), pos)
+    assert np.array_equal(codecs.e4m3fn_encode(mid + gap / 8).astype(np.int64), pos + 1)
+
+
+def test_e4m3fn_encode_saturation_nan_zero_and_underflow():
+    lm = _landmarks()
+    top = float(lm["e4m3_max"][0])
+    tiny = float(lm["e4m3_min_positive"][0])
+    enc = lambda v: int(codecs.e4m3fn_encode(np.array([v]))[0])
+    for v in (top, top * (1 + 2 ** -20), 464.0, 480.0, 1e30, math.inf):
+        assert enc(v) == 0x7E and enc(-v) == 0xFE
+    assert enc(math.nan) == 0x7F
+    assert enc(0.0) == 0x00 and enc(-0.0) == 0x80
+    assert enc(tiny / 2) == 0x00                  # midpoint of 0 and 2^-9: even code 0
+    assert enc(tiny / 2 * (1 + 2 ** -20)) == 0x01
+    assert enc(-tiny / 4) == 0x80
+    assert enc(tiny * 1.5) == 0x02                # midpoint of codes 1 and 2: even code 2
+
+
+def test_e4m3fn_encode_matches_torch_conversion_in_range():
+    rng = np.random.default_rng(11)
+    u = rng.integers(0, 2 ** 32, size=1_000_000, dtype=np.uint64).astype(np.uint32)
+    e = rng.integers(110, 136, size=u.size, dtype=np.uint32)     # 2^-17 .. 2^8
+    x = ((u & np.uint32(0x807FFFFF)) | (e << np.uint32(23))).view(np.float32)
+    # exact E4M3 midpoints and their float32 neighbours
+    mids = ((codecs.E4M3FN_TABLE[0:0x7E] + codecs.E4M3FN_TABLE[1:0x7F]) / 2).astype(np.float32)
+    x = np.concatenate([x, mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9)),
+                        -mids]).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    ours = codecs.e4m3fn_encode(x)
+    lib = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, lib)

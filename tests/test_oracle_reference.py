@@ -374,3 +374,74 @@ def test_check_matmul_nan_reference():
     S = np.array([[1.0, 1.0]])
     assert ref.check_matmul(np.array([[0x7FC0, 0x3F80]], dtype=np.uint16), "bf16", Y, S)["ok"]
     assert not ref.check_matmul(np.array([[0x3F80, 0x3F80]], dtype=np.uint16), "bf16", Y, S)["ok"]
+
+
+# ---------------------------------------------------------------------------
+# Optional W8A8 activation quantize/dequantize ([FP8 doc] §6)
+# ---------------------------------------------------------------------------
+
+def _all_bits():
+    return np.arange(65536, dtype=np.uint32).astype(np.uint16)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("a_scale", [1.0, 0.0625, 0.37, 3.0e-3, 7.5])
+def test_qdq_matches_torch_fp8_round_trip(dtype, a_scale):
+    """Every T bit pattern through QDQ vs torch's own float8_e4m3fn casts,
+    on inputs whose quotient stays within +-448 (torch does not saturate)."""
+    bits = _all_bits()
+    x = ref.activation_to_f64(bits, dtype)
+    q = (x.astype(np.float32) / np.float32(a_scale)).astype(np.float32)
+    keep = np.isfinite(q) & (np.abs(q) <= 448)
+    ours = ref.qdq_activation_fp8_bits(bits[keep], dtype, a_scale)
+    tdt = torch.float16 if dtype == "fp16" else torch.bfloat16
+    t = torch.from_numpy(q[keep]).to(torch.float8_e4m3fn).to(torch.float32)
+    t = (t * torch.tensor(a_scale, dtype=torch.float32)).to(tdt)
+    lib = t.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, lib)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_qdq_saturates_and_keeps_nan(dtype):
+    a_scale = 0.5
+    vals = np.array([300.0, -300.0, 224.0, 240.0, 1e4], dtype=np.float32)
+    bits = codecs.f32_to_f16_bits(vals) if dtype == "fp16" else codecs.f32_to_bf16_bits(vals)
+    out = ref.activation_to_f64(ref.qdq_activation_fp8_bits(bits, dtype, a_scale), dtype)
+    assert np.array_equal(out, [224.0, -224.0, 224.0, 224.0, 224.0])   # 448 * 0.5
+    nan_bits = np.array([0x7E00 if dtype == "fp16" else 0x7FC0], dtype=np.uint16)
+    assert np.isnan(ref.activation_to_f64(
+        ref.qdq_activation_fp8_bits(nan_bits, dtype, a_scale), dtype)).all()
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_qdq_fixes_values_already_on_the_scaled_grid(dtype):
+    """A = code * a_scale with a power-of-two a_scale: QDQ is the identity;
+    and QDQ is idempotent for any power-of-two scale."""
+    a_scale = 2.0 ** -3
+    c = np.arange(256)
+    v = codecs.E4M3FN_TABLE[c]
+    v = v[np.isfinite(v)] * a_scale
+    bits = codecs.f32_to_f16_bits(v) if dtype == "fp16" else codecs.f32_to_bf16_bits(v)
+    assert np.array_equal(ref.activation_to_f64(bits, dtype), v)   # exact in T
+    out = ref.qdq_activation_fp8_bits(bits, dtype, a_scale)
+    assert np.array_equal(out, bits)
+    once = ref.qdq_activation_fp8_bits(_all_bits(), dtype, 4.0)
+    twice = ref.qdq_activation_fp8_bits(once, dtype, 4.0)
+    fin = np.isfinite(ref.activation_to_f64(once, dtype))
+    assert np.array_equal(once[fin], twice[fin])
+
+
+def test_qdq_error_within_e4m3_half_ulp():
+    """|QDQ(a) - a| <= 2^-4 |a| for normal-range quotients (3 mantissa bits),
+    <= 2^-10 * a_scale in the subnormal range; every output is code * a_scale."""
+    rng = np.random.default_rng(3)
+    a = rng.standard_normal(200_000).astype(np.float32)
+    bits = codecs.f32_to_bf16_bits(a)
+    x = ref.activation_to_f64(bits, "bf16")
+    for a_scale in (0.01, 0.05):
+        y = ref.activation_to_f64(ref.qdq_activation_fp8_bits(bits, "bf16", a_scale), "bf16")
+        q = np.abs(x) / a_scale
+        bound = np.where(q >= 2.0 ** -6, 2.0 ** -4 * np.abs(x), 2.0 ** -10 * a_scale)
+        # one more BF16 rounding of the result: half an ulp of |y| (2^-9 relative)
+        bound = bound + 2.0 ** -8 * np.abs(y)
+        assert np.all(np.abs(y - x) <= bound * (1 + 1e-12))
