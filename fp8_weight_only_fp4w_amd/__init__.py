@@ -16,6 +16,11 @@ The functions carry the C ABI's names (include/fp4w.h):
   Documentation" §2).
 * ``fp4w_dequant(B, weight_scale, weight_scale_2, block_size=16, dtype=...)``:
   the [N, K] FP16/BF16 expansion of B.
+* ``fp8w_qdq_activation(A, a_scale)``: fp8_e4m3(A / a_scale) * a_scale in A's
+  dtype, the activation step of the FP8 operator's optional W8A8 mode (FP8
+  document §6).
+* ``fp8w_matmul_w8a8(A, B, b_scale, a_scale, bias=None, block_size=128)``:
+  that step into a workspace, then ``fp8w_matmul`` on it.
 
 A keeps any leading dimensions; Y has A's leading dimensions, last dimension
 N and A's dtype.
@@ -36,14 +41,16 @@ PATH_AUTO, PATH_NONE = 0, 1
 PATH_FP4_GEMV, PATH_FP4_GEMM, PATH_FP4_GENERIC = 2, 3, 4
 PATH_FP8_GEMV, PATH_FP8_GEMM, PATH_FP8_GENERIC = 5, 6, 7
 PATH_DEQUANT_VEC, PATH_DEQUANT_GENERIC = 8, 9
+PATH_QDQ_VEC, PATH_QDQ_GENERIC = 10, 11
 # operations (fp4w_op)
-OP_FP4_MATMUL, OP_FP8_MATMUL, OP_FP4_DEQUANT = 0, 1, 2
+OP_FP4_MATMUL, OP_FP8_MATMUL, OP_FP4_DEQUANT, OP_FP8_QDQ = 0, 1, 2, 3
 # dtypes (fp4w_dtype)
 F16, BF16 = 0, 1
 
 EXPORTED = (
     "fp4w_matmul", "fp4w_matmul_ex", "fp8w_matmul", "fp8w_matmul_ex", "fp4w_dequant",
-    "fp4w_dequant_ex", "fp4w_select_path", "fp4w_status_string", "fp4w_path_name",
+    "fp4w_dequant_ex", "fp8w_qdq_activation", "fp8w_qdq_activation_ex", "fp8w_matmul_w8a8",
+    "fp4w_select_path", "fp4w_status_string", "fp4w_path_name",
 )
 
 
@@ -77,6 +84,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp4w_dequant_ex.restype = i32
     lib.fp4w_dequant.argtypes = [vp, i64, i64, vp, i64, i64, vp, vp, i32, vp]
     lib.fp4w_dequant.restype = i32
+    lib.fp8w_qdq_activation_ex.argtypes = [vp, i64, i64, vp, vp, i32, vp, i32]
+    lib.fp8w_qdq_activation_ex.restype = i32
+    lib.fp8w_qdq_activation.argtypes = [vp, i64, i64, vp, vp, i32, vp]
+    lib.fp8w_qdq_activation.restype = i32
+    lib.fp8w_matmul_w8a8.argtypes = [vp, i64, i64, vp, i64, vp, i64, i64, vp, vp, vp, vp, i32, vp]
+    lib.fp8w_matmul_w8a8.restype = i32
     lib.fp4w_select_path.argtypes = [i32, i64, i64, i64, i64, i64]
     lib.fp4w_select_path.restype = i32
     lib.fp4w_status_string.argtypes = [i32]
@@ -213,4 +226,68 @@ def fp4w_dequant(B: torch.Tensor, weight_scale: torch.Tensor, weight_scale_2: to
     st = lib.fp4w_dequant_ex(_ptr(B), N, K, _ptr(weight_scale), weight_scale.shape[1], block_size,
                              _ptr(weight_scale_2), _ptr(out), _dtype_code(out.dtype), _stream(dev), path)
     _check(st, "fp4w_dequant")
+    return out
+
+
+def _scalar_f32(t: torch.Tensor, name: str):
+    if t.dtype != torch.float32 or t.numel() != 1:
+        raise ValueError(f"{name} must be a 1-element float32 tensor")
+
+
+def fp8w_qdq_activation(A: torch.Tensor, a_scale: torch.Tensor, out: torch.Tensor = None,
+                        path: int = PATH_AUTO) -> torch.Tensor:
+    """fp8_e4m3(A / a_scale) * a_scale in A's dtype; ``out`` may be ``A``."""
+    lib = load_library()
+    dev = A.device
+    K = A.shape[-1] if A.dim() else 1
+    M = A.numel() // K if K else 0
+    _need(A, "A", dev)
+    _need(a_scale, "a_scale", dev)
+    _scalar_f32(a_scale, "a_scale")
+    if out is None:
+        out = torch.empty_like(A)
+    _need(out, "out", dev)
+    if out.shape != A.shape or out.dtype != A.dtype:
+        raise ValueError("out must have A's shape and dtype")
+    st = lib.fp8w_qdq_activation_ex(_ptr(A), M, K, _ptr(a_scale), _ptr(out),
+                                    _dtype_code(A.dtype), _stream(dev), path)
+    _check(st, "fp8w_qdq_activation")
+    return out
+
+
+def fp8w_matmul_w8a8(A: torch.Tensor, B: torch.Tensor, b_scale: torch.Tensor, a_scale: torch.Tensor,
+                     bias: torch.Tensor = None, block_size: int = 128, out: torch.Tensor = None,
+                     workspace: torch.Tensor = None) -> torch.Tensor:
+    """fp8w_matmul on fp8_e4m3(A / a_scale) * a_scale.  ``workspace`` (A's shape
+    and dtype, or ``A`` itself to quantize in place) receives the quantized
+    activation; it is allocated here when not given."""
+    lib = load_library()
+    dev = A.device
+    B = _bytes(B)
+    K = A.shape[-1]
+    M = A.numel() // K if K else int(torch.tensor(A.shape[:-1]).prod().item())
+    N = B.shape[0]
+    if B.dim() != 2 or B.shape[1] != K:
+        raise ValueError(f"B must be [N, K] = [N, {K}], got {tuple(B.shape)}")
+    if b_scale.dtype != torch.float32 or b_scale.dim() != 2 or b_scale.shape[0] != N:
+        raise ValueError("b_scale must be float32 [N, scale_cols]")
+    _scalar_f32(a_scale, "a_scale")
+    for t, name in ((A, "A"), (B, "B"), (b_scale, "b_scale"), (a_scale, "a_scale")):
+        _need(t, name, dev)
+    if bias is not None:
+        _need(bias, "bias", dev)
+        if bias.dtype != A.dtype or bias.numel() != N:
+            raise ValueError("bias must be [N] with A's dtype")
+    if workspace is None:
+        workspace = torch.empty_like(A)
+    _need(workspace, "workspace", dev)
+    if workspace.shape != A.shape or workspace.dtype != A.dtype:
+        raise ValueError("workspace must have A's shape and dtype")
+    if out is None:
+        out = torch.empty(*A.shape[:-1], N, dtype=A.dtype, device=dev)
+    _need(out, "out", dev)
+    st = lib.fp8w_matmul_w8a8(_ptr(A), M, K, _ptr(B), N, _ptr(b_scale), b_scale.shape[1], block_size,
+                              _ptr(a_scale), _ptr(bias), _ptr(workspace), _ptr(out),
+                              _dtype_code(A.dtype), _stream(dev))
+    _check(st, "fp8w_matmul_w8a8")
     return out

@@ -18,6 +18,7 @@ namespace {
 using fp4w::Act;
 using fp4w::DequantArgs;
 using fp4w::MatmulArgs;
+using fp4w::QdqArgs;
 
 constexpr int64_t kMaxElems = int64_t(1) << 62;
 
@@ -103,8 +104,10 @@ bool path_applies(int path, const MatmulArgs& a) {
   }
 }
 
-int run_matmul(int op, MatmulArgs& a, const void* scale_ptr_for_alias, int64_t scale_elem_bytes,
-               int path) {
+// Validates a matmul call and picks its kernel path.  Returns FP4W_OK with
+// *chosen set (FP4W_PATH_NONE when there is nothing to launch), or an error.
+int plan_matmul(int op, const MatmulArgs& a, const void* scale_ptr_for_alias,
+                int64_t scale_elem_bytes, int path, int* chosen_out) {
   const int dtype = static_cast<int>(a.act);
   if (dtype != FP4W_F16 && dtype != FP4W_BF16) return FP4W_ERR_DTYPE;
   int st = check_shape(op, a.M, a.N, a.K, a.block_size, a.scale_cols);
@@ -117,6 +120,7 @@ int run_matmul(int op, MatmulArgs& a, const void* scale_ptr_for_alias, int64_t s
                                   path == FP4W_PATH_FP8_GENERIC);
     if (!family_ok) return FP4W_ERR_PATH;
   }
+  *chosen_out = FP4W_PATH_NONE;
   if (a.M == 0 || a.N == 0) return FP4W_OK;  // empty output: nothing to do
   if (a.Y == nullptr) return FP4W_ERR_NULL;
   if (a.K > 0 && (a.A == nullptr || a.B == nullptr || a.scales == nullptr)) return FP4W_ERR_NULL;
@@ -136,8 +140,14 @@ int run_matmul(int op, MatmulArgs& a, const void* scale_ptr_for_alias, int64_t s
   } else if (!path_applies(path, a)) {
     return FP4W_ERR_PATH;
   }
+  *chosen_out = chosen;
+  return FP4W_OK;
+}
+
+int launch_matmul(int chosen, const MatmulArgs& a) {
   int rc = -1;
   switch (chosen) {
+    case FP4W_PATH_NONE: return FP4W_OK;
     case FP4W_PATH_FP4_GEMV: rc = fp4w::launch_fp4_gemv(a); break;
     case FP4W_PATH_FP4_GEMM: rc = fp4w::launch_fp4_gemm(a); break;
     case FP4W_PATH_FP4_GENERIC: rc = fp4w::launch_fp4_generic(a); break;
@@ -146,6 +156,42 @@ int run_matmul(int op, MatmulArgs& a, const void* scale_ptr_for_alias, int64_t s
     case FP4W_PATH_FP8_GENERIC: rc = fp4w::launch_fp8_generic(a); break;
     default: return FP4W_ERR_PATH;
   }
+  return rc == 0 ? FP4W_OK : FP4W_ERR_LAUNCH;
+}
+
+int run_matmul(int op, const MatmulArgs& a, const void* scale_ptr_for_alias,
+               int64_t scale_elem_bytes, int path) {
+  int chosen = FP4W_PATH_NONE;
+  const int st = plan_matmul(op, a, scale_ptr_for_alias, scale_elem_bytes, path, &chosen);
+  return st != FP4W_OK ? st : launch_matmul(chosen, a);
+}
+
+bool qdq_vec_ok(int64_t count) { return count > 0 && count % 8 == 0; }
+
+// Validates a QDQ call and picks its path (FP4W_PATH_NONE: nothing to do).
+int plan_qdq(const QdqArgs& q, int64_t M, int64_t K, int path, int* chosen_out) {
+  const int dtype = static_cast<int>(q.act);
+  if (dtype != FP4W_F16 && dtype != FP4W_BF16) return FP4W_ERR_DTYPE;
+  if (M < 0 || K < 0 || !mul_ok(M, K) || !mul_ok(M * K, 2)) return FP4W_ERR_SHAPE;
+  if (path != FP4W_PATH_AUTO && path != FP4W_PATH_QDQ_VEC && path != FP4W_PATH_QDQ_GENERIC)
+    return FP4W_ERR_PATH;
+  *chosen_out = FP4W_PATH_NONE;
+  if (M == 0 || K == 0) return FP4W_OK;
+  if (q.A == nullptr || q.a_scale == nullptr || q.out == nullptr) return FP4W_ERR_NULL;
+  const int64_t bytes = M * K * 2;
+  if (q.out != q.A && overlaps(q.out, bytes, q.A, bytes)) return FP4W_ERR_ALIAS;
+  if (overlaps(q.out, bytes, q.a_scale, 4)) return FP4W_ERR_ALIAS;
+  const bool vec = qdq_vec_ok(M * K) && aligned(q.A, 16) && aligned(q.out, 16);
+  int chosen = path;
+  if (path == FP4W_PATH_AUTO) chosen = vec ? FP4W_PATH_QDQ_VEC : FP4W_PATH_QDQ_GENERIC;
+  if (chosen == FP4W_PATH_QDQ_VEC && !vec) return FP4W_ERR_PATH;
+  *chosen_out = chosen;
+  return FP4W_OK;
+}
+
+int launch_qdq(int chosen, const QdqArgs& q) {
+  if (chosen == FP4W_PATH_NONE) return FP4W_OK;
+  const int rc = chosen == FP4W_PATH_QDQ_VEC ? fp4w::launch_qdq_vec(q) : fp4w::launch_qdq_generic(q);
   return rc == 0 ? FP4W_OK : FP4W_ERR_LAUNCH;
 }
 
@@ -184,6 +230,48 @@ int fp8w_matmul(const void* A, int64_t M, int64_t K, const uint8_t* B, int64_t N
                         FP4W_PATH_AUTO);
 }
 
+int fp8w_qdq_activation_ex(const void* A, int64_t M, int64_t K, const float* a_scale, void* out,
+                           int dtype, void* stream, int path) {
+  const int64_t count = (M >= 0 && K >= 0 && mul_ok(M, K)) ? M * K : 0;
+  QdqArgs q{A, a_scale, out, count, static_cast<Act>(dtype), stream};
+  int chosen = FP4W_PATH_NONE;
+  const int st = plan_qdq(q, M, K, path, &chosen);
+  return st != FP4W_OK ? st : launch_qdq(chosen, q);
+}
+
+int fp8w_qdq_activation(const void* A, int64_t M, int64_t K, const float* a_scale, void* out,
+                        int dtype, void* stream) {
+  return fp8w_qdq_activation_ex(A, M, K, a_scale, out, dtype, stream, FP4W_PATH_AUTO);
+}
+
+int fp8w_matmul_w8a8(const void* A, int64_t M, int64_t K, const uint8_t* B, int64_t N,
+                     const float* b_scale, int64_t scale_cols, int64_t block_size,
+                     const float* a_scale, const void* bias, void* A_work, void* Y, int dtype,
+                     void* stream) {
+  // The matmul reads A_work; validate it as the matmul's activation.
+  MatmulArgs a{A_work, B, b_scale, nullptr, bias, Y, M, N, K, block_size, scale_cols,
+               static_cast<Act>(dtype), stream};
+  int mm_path = FP4W_PATH_NONE;
+  int st = plan_matmul(FP4W_OP_FP8_MATMUL, a, b_scale, 4, FP4W_PATH_AUTO, &mm_path);
+  if (st != FP4W_OK) return st;
+  if (mm_path == FP4W_PATH_NONE) return FP4W_OK;  // empty output
+  QdqArgs q{A, a_scale, A_work, M * K, static_cast<Act>(dtype), stream};
+  int q_path = FP4W_PATH_NONE;
+  st = plan_qdq(q, M, K, FP4W_PATH_AUTO, &q_path);
+  if (st != FP4W_OK) return st;
+  // The weights, scales and bias are only read, but the QDQ step writes
+  // A_work: it must not overlap them or Y (checked against Y by plan_matmul).
+  // Y must not overlap the original activation or a_scale either.
+  const int64_t abytes = M * K * 2;
+  if (overlaps(Y, M * N * 2, A, abytes) || overlaps(Y, M * N * 2, a_scale, 4) ||
+      overlaps(A_work, abytes, B, N * K) ||
+      overlaps(A_work, abytes, b_scale, N * scale_cols * 4) || overlaps(A_work, abytes, bias, N * 2))
+    return FP4W_ERR_ALIAS;
+  st = launch_qdq(q_path, q);
+  if (st != FP4W_OK) return st;
+  return launch_matmul(mm_path, a);
+}
+
 int fp4w_dequant_ex(const uint8_t* B, int64_t N, int64_t K, const uint8_t* weight_scale,
                     int64_t scale_cols, int64_t block_size, const float* weight_scale_2, void* out,
                     int dtype, void* stream, int path) {
@@ -219,6 +307,11 @@ int fp4w_dequant(const uint8_t* B, int64_t N, int64_t K, const uint8_t* weight_s
 
 int fp4w_select_path(int op, int64_t M, int64_t N, int64_t K, int64_t block_size,
                      int64_t scale_cols) {
+  if (op == FP4W_OP_FP8_QDQ) {
+    if (M < 0 || K < 0 || !mul_ok(M, K) || !mul_ok(M * K, 2)) return FP4W_ERR_SHAPE;
+    if (M == 0 || K == 0) return FP4W_PATH_NONE;
+    return qdq_vec_ok(M * K) ? FP4W_PATH_QDQ_VEC : FP4W_PATH_QDQ_GENERIC;
+  }
   if (op != FP4W_OP_FP4_MATMUL && op != FP4W_OP_FP8_MATMUL && op != FP4W_OP_FP4_DEQUANT)
     return FP4W_ERR_PATH;
   int st = check_shape(op, op == FP4W_OP_FP4_DEQUANT ? 0 : M, N, K, block_size, scale_cols);
@@ -252,6 +345,8 @@ const char* fp4w_path_name(int path) {
     case FP4W_PATH_FP8_GENERIC: return "fp8_generic";
     case FP4W_PATH_DEQUANT_VEC: return "dequant_vec";
     case FP4W_PATH_DEQUANT_GENERIC: return "dequant_generic";
+    case FP4W_PATH_QDQ_VEC: return "qdq_vec";
+    case FP4W_PATH_QDQ_GENERIC: return "qdq_generic";
     default: return "unknown";
   }
 }

@@ -32,6 +32,16 @@ struct DequantArgs {
   void* stream;
 };
 
+// Activation quantize/dequantize (W8A8 mode): `count` elements of T.
+struct QdqArgs {
+  const void* A;
+  const float* a_scale;
+  void* out;
+  int64_t count;
+  Act act;
+  void* stream;
+};
+
 // Each launcher enqueues its kernel(s) and returns 0, or -1 when HIP reports
 // an error at enqueue time.  Preconditions (checked by the dispatcher, never
 // by the launcher) are stated next to each.
@@ -58,5 +68,10 @@ int launch_fp8_generic(const MatmulArgs& a);
 int launch_dequant_vec(const DequantArgs& a);
 // any validated arguments with N, K > 0
 int launch_dequant_generic(const DequantArgs& a);
+
+// count % 8 == 0, A and out 16-byte aligned; out == A allowed.
+int launch_qdq_vec(const QdqArgs& a);
+// any count > 0; out == A allowed.
+int launch_qdq_generic(const QdqArgs& a);
 
 }  // namespace fp4w

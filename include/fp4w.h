@@ -66,11 +66,18 @@ typedef enum {
   FP4W_PATH_FP8_GEMM = 6,        /* MFMA prefill GEMM: block_size % 64 == 0, K % 64 == 0 */
   FP4W_PATH_FP8_GENERIC = 7,     /* any legal FP8 arguments */
   FP4W_PATH_DEQUANT_VEC = 8,     /* vectorised dequant: K % 8 == 0, block_size % 8 == 0 */
-  FP4W_PATH_DEQUANT_GENERIC = 9  /* any legal dequant arguments */
+  FP4W_PATH_DEQUANT_GENERIC = 9, /* any legal dequant arguments */
+  FP4W_PATH_QDQ_VEC = 10,        /* vectorised activation QDQ: M*K % 8 == 0 */
+  FP4W_PATH_QDQ_GENERIC = 11     /* any legal QDQ arguments */
 } fp4w_path;
 
 /* Operation selector for fp4w_select_path. */
-typedef enum { FP4W_OP_FP4_MATMUL = 0, FP4W_OP_FP8_MATMUL = 1, FP4W_OP_FP4_DEQUANT = 2 } fp4w_op;
+typedef enum {
+  FP4W_OP_FP4_MATMUL = 0,
+  FP4W_OP_FP8_MATMUL = 1,
+  FP4W_OP_FP4_DEQUANT = 2,
+  FP4W_OP_FP8_QDQ = 3 /* fp8w_qdq_activation: only M and K are used */
+} fp4w_op;
 
 /*
  * fp4w_matmul - weight-only FP4 matmul, Y = A * dequant(B)^T (+ bias).
@@ -135,6 +142,49 @@ int fp4w_dequant(const uint8_t* B, int64_t N, int64_t K, const uint8_t* weight_s
 int fp4w_dequant_ex(const uint8_t* B, int64_t N, int64_t K, const uint8_t* weight_scale,
                     int64_t scale_cols, int64_t block_size, const float* weight_scale_2, void* out,
                     int dtype, void* stream, int path);
+
+/*
+ * fp8w_qdq_activation - the activation step of the FP8 operator's optional
+ * W8A8 mode ([FP8 doc] §6, Optional W8A8 Activation Path):
+ *   out[m, k] = RNE_T( RNE_f32( e4m3( sat( RNE_f32(A[m, k] / a_scale) ) ) * a_scale ) )
+ * The quotient is an IEEE FP32 division; e4m3() rounds to nearest even; sat()
+ * clamps magnitudes above 448 (the largest finite E4M3 "fn" value) to 448 and
+ * keeps NaN; the decoded value times a_scale is rounded once in FP32, then to
+ * T.  Bit-exact.
+ *
+ *   A        T[M, K]
+ *   a_scale  device float*: the per-tensor activation scale (expected > 0;
+ *            other values just follow the IEEE steps above).
+ *   out      T[M, K] (written).  out == A is allowed (in place); any other
+ *            overlap with A is FP4W_ERR_ALIAS.
+ * M == 0 or K == 0: FP4W_OK, nothing launched.  Errors: FP4W_ERR_NULL,
+ * FP4W_ERR_SHAPE, FP4W_ERR_DTYPE, FP4W_ERR_ALIAS, FP4W_ERR_LAUNCH.
+ */
+int fp8w_qdq_activation(const void* A, int64_t M, int64_t K, const float* a_scale, void* out,
+                        int dtype, void* stream);
+
+/* Path-forcing variant (FP4W_PATH_AUTO, _QDQ_VEC, _QDQ_GENERIC). */
+int fp8w_qdq_activation_ex(const void* A, int64_t M, int64_t K, const float* a_scale, void* out,
+                           int dtype, void* stream, int path);
+
+/*
+ * fp8w_matmul_w8a8 - the FP8 operator with its optional a_scale input
+ * ([FP8 doc] §3 dispatch chain, whose first step quantizes/dequantizes A when
+ * a_scale is present, and §6): A_work = fp8w_qdq_activation(A), then
+ * Y = fp8w_matmul(A_work, ...).  Both steps are enqueued on `stream`.
+ *
+ *   A_work   T[M, K] caller-owned workspace that receives the quantized
+ *            activation (the library allocates nothing).  A_work == A is
+ *            allowed and overwrites A; any other overlap with A is
+ *            FP4W_ERR_ALIAS, as is an overlap of Y with A_work.
+ *   a_scale  device float*, as fp8w_qdq_activation.
+ *   Other arguments and errors as fp8w_matmul.  Every argument is validated
+ *   before anything is launched.
+ */
+int fp8w_matmul_w8a8(const void* A, int64_t M, int64_t K, const uint8_t* B, int64_t N,
+                     const float* b_scale, int64_t scale_cols, int64_t block_size,
+                     const float* a_scale, const void* bias, void* A_work, void* Y, int dtype,
+                     void* stream);
 
 /*
  * fp4w_select_path - the path FP4W_PATH_AUTO takes for these sizes, assuming

@@ -169,3 +169,46 @@ def test_binding_fails_loudly_without_library(tmp_path):
             mod.load_library(str(tmp_path / "missing.so"))
     finally:
         importlib.reload(fw)
+
+
+def test_dispatch_and_validation_qdq():
+    Q = fw.OP_FP8_QDQ
+    assert fw.fp4w_select_path(Q, 4, 0, 5120, 1, 1) == fw.PATH_QDQ_VEC
+    assert fw.fp4w_select_path(Q, 3, 0, 7, 1, 1) == fw.PATH_QDQ_GENERIC      # 21 elements
+    assert fw.fp4w_select_path(Q, 0, 0, 64, 1, 1) == fw.PATH_NONE
+    assert fw.fp4w_select_path(Q, -1, 0, 64, 1, 1) == fw.ERR_SHAPE
+    assert fw.fp4w_path_name(fw.PATH_QDQ_VEC) == "qdq_vec"
+    lib = fw.load_library()
+    vp = ctypes.c_void_p
+    A, S, O = vp(0x100000), vp(0x300000), vp(0x500000)
+    q = lib.fp8w_qdq_activation_ex
+    assert q(A, 4, 64, S, O, 7, None, 0) == fw.ERR_DTYPE
+    assert q(A, -4, 64, S, O, fw.BF16, None, 0) == fw.ERR_SHAPE
+    assert q(None, 4, 64, S, O, fw.BF16, None, 0) == fw.ERR_NULL
+    assert q(A, 4, 64, None, O, fw.BF16, None, 0) == fw.ERR_NULL
+    assert q(A, 4, 64, S, None, fw.BF16, None, 0) == fw.ERR_NULL
+    assert q(A, 4, 64, S, vp(0x100000 + 16), fw.BF16, None, 0) == fw.ERR_ALIAS   # partial overlap
+    assert q(A, 4, 64, S, vp(0x300000 - 8), fw.BF16, None, 0) == fw.ERR_ALIAS    # out over a_scale
+    assert q(A, 3, 7, S, O, fw.BF16, None, fw.PATH_QDQ_VEC) == fw.ERR_PATH        # 21 % 8 != 0
+    assert q(vp(0x100002), 4, 64, S, O, fw.BF16, None, fw.PATH_QDQ_VEC) == fw.ERR_PATH  # unaligned
+    assert q(A, 4, 64, S, O, fw.BF16, None, fw.PATH_FP8_GEMV) == fw.ERR_PATH     # not a QDQ path
+    assert q(None, 0, 64, None, None, fw.BF16, None, 0) == fw.OK                  # empty: no launch
+    assert q(None, 4, 0, None, None, fw.F16, None, fw.PATH_QDQ_GENERIC) == fw.OK
+
+
+def test_w8a8_validation_before_any_launch():
+    lib = fw.load_library()
+    vp = ctypes.c_void_p
+    A, B, S, AS, W, Y = (vp(x) for x in (0x100000, 0x200000, 0x300000, 0x380000, 0x400000, 0x500000))
+    m = lib.fp8w_matmul_w8a8
+    # M=4, K=256, N=16, bs=128, cols=2
+    assert m(A, 4, 256, B, 16, S, 3, 128, AS, None, W, Y, fw.BF16, None) == fw.ERR_SHAPE
+    assert m(A, 4, 256, B, 16, S, 2, 128, None, None, W, Y, fw.BF16, None) == fw.ERR_NULL
+    assert m(A, 4, 256, B, 16, S, 2, 128, AS, None, None, Y, fw.BF16, None) == fw.ERR_NULL
+    assert m(None, 4, 256, B, 16, S, 2, 128, AS, None, W, Y, fw.BF16, None) == fw.ERR_NULL
+    assert m(A, 4, 256, B, 16, S, 2, 128, AS, None, vp(0x100000 + 32), Y, fw.BF16, None) == fw.ERR_ALIAS
+    assert m(A, 4, 256, B, 16, S, 2, 128, AS, None, W, vp(0x400000 + 64), fw.BF16, None) == fw.ERR_ALIAS
+    assert m(A, 4, 256, B, 16, S, 2, 128, AS, None, W, vp(0x100000 + 64), fw.BF16, None) == fw.ERR_ALIAS
+    assert m(A, 4, 256, B, 16, S, 2, 128, AS, None, vp(0x200000 + 64), Y, fw.BF16, None) == fw.ERR_ALIAS
+    assert m(A, 4, 256, B, 16, S, 2, 128, AS, None, W, Y, 9, None) == fw.ERR_DTYPE
+    assert m(None, 0, 256, None, 16, None, 2, 128, None, None, None, None, fw.BF16, None) == fw.OK
