@@ -321,6 +321,37 @@ def extra_wide(steps, warmup):
     return {"us": round(t * 1e6, 2), "weight_GBps": round(wb / t / 1e9, 1), "copies": R}
 
 
+def extra_w8a8(steps, warmup):
+    """Optional W8A8 mode ([FP8 doc] §6): the activation QDQ kernel alone, and
+    QDQ + FP8 matmul at the FP8 GEMV workload (M=4) and at the pages' W8A8
+    profiling shape (bf16, M=16, N=K=4096, block 128).  a_scale = amax/448."""
+    res = {}
+    w = workloads.WORKLOADS["fp8_gemv"]
+    for label, M, N, K in (("M4_N17408_K5120", 4, w.N, w.K), ("M16_N4096_K4096", 16, 4096, 4096)):
+        p = workloads.make_fp8(M, N, K, 128, "bf16", seed=M + 5)
+        wb = p.B.nbytes + p.b_scale.nbytes
+        R = copies_for(wb)
+        d = fp8_on_device(p, copies=R)
+        a = d["A"].float().abs().max() / 448.0
+        sc = a.reshape(1).to(torch.float32)
+        work = torch.empty_like(d["A"])
+        out = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        tq = time_rotating(lambda r: fw.fp8w_qdq_activation(d["A"], sc, out=work), 1, steps)
+        tw = time_rotating(lambda r: fw.fp8w_matmul_w8a8(d["A"], d["B"][r], d["bs"][r], sc, None, 128,
+                                                          out=out, workspace=work), R, steps)
+        t0 = time_rotating(lambda r: fw.fp8w_matmul(d["A"], d["B"][r], d["bs"][r], None, 128, out=out),
+                           R, steps)
+        res[label] = {"qdq_us": round(tq * 1e6, 2), "w8a8_us": round(tw * 1e6, 2),
+                      "weight_only_us": round(t0 * 1e6, 2), "weight_GBps_w8a8": round(wb / tw / 1e9, 1)}
+        del d
+    A = torch.randn(8192, 5120, device="cuda").to(torch.bfloat16)
+    work = torch.empty_like(A)
+    sc = (A.float().abs().max() / 448.0).reshape(1)
+    tq = time_calls([lambda: fw.fp8w_qdq_activation(A, sc, out=work)], 50, 5) / 50
+    res["qdq_M8192_K5120"] = {"us": round(tq * 1e6, 2), "GBps": round(4 * A.numel() / tq / 1e9, 1)}
+    return res
+
+
 # ------------------------------------------------------------------ profiling mode
 
 def profile_kernel(which, launches=50):
@@ -422,6 +453,7 @@ def main():
                          ("fp4_gemv_small", lambda: extra_small_gemv(args.steps, args.warmup)),
                          ("fp4_gemv_wide", lambda: extra_wide(args.steps, args.warmup)),
                          ("fp8", lambda: extra_fp8(args.steps, args.warmup)),
+                         ("fp8_w8a8", lambda: extra_w8a8(args.steps, args.warmup)),
                          ("fp4_prefill", extra_prefill_fp4)):
             t0 = time.perf_counter()
             extra[name] = fn()

@@ -42,6 +42,7 @@ PATH_FP4_GEMV, PATH_FP4_GEMM, PATH_FP4_GENERIC = 2, 3, 4
 PATH_FP8_GEMV, PATH_FP8_GEMM, PATH_FP8_GENERIC = 5, 6, 7
 PATH_DEQUANT_VEC, PATH_DEQUANT_GENERIC = 8, 9
 PATH_QDQ_VEC, PATH_QDQ_GENERIC = 10, 11
+PATH_FP4_SKINNY, PATH_FP8_SKINNY = 12, 13
 # operations (fp4w_op)
 OP_FP4_MATMUL, OP_FP8_MATMUL, OP_FP4_DEQUANT, OP_FP8_QDQ = 0, 1, 2, 3
 # dtypes (fp4w_dtype)

@@ -55,6 +55,12 @@ int check_shape(int op, int64_t M, int64_t N, int64_t K, int64_t bs, int64_t col
 bool fp4_gemv_ok(int64_t M, int64_t K, int64_t bs) {
   return M >= 1 && M <= 8 && bs == 16 && K % 128 == 0 && K > 0;
 }
+bool fp4_skinny_ok(int64_t M, int64_t K, int64_t bs) {
+  return M >= 1 && M <= 64 && bs == 16 && K % 128 == 0 && K > 0;
+}
+bool fp8_skinny_ok(int64_t M, int64_t K, int64_t bs) {
+  return M >= 1 && M <= 64 && bs % 128 == 0 && K % 128 == 0 && K > 0;
+}
 bool fp4_gemm_ok(int64_t M, int64_t K, int64_t bs) { return M >= 1 && bs == 16 && K % 64 == 0 && K > 0; }
 bool fp8_gemv_ok(int64_t M, int64_t K, int64_t bs) {
   return M >= 1 && M <= 8 && bs % 128 == 0 && K % 128 == 0 && K > 0;
@@ -73,10 +79,12 @@ int shape_path(int op, int64_t M, int64_t N, int64_t K, int64_t bs) {
   if (M == 0 || N == 0) return FP4W_PATH_NONE;
   if (op == FP4W_OP_FP4_MATMUL) {
     if (fp4_gemv_ok(M, K, bs)) return FP4W_PATH_FP4_GEMV;
+    if (M > 8 && fp4_skinny_ok(M, K, bs)) return FP4W_PATH_FP4_SKINNY;
     if (M > 8 && fp4_gemm_ok(M, K, bs)) return FP4W_PATH_FP4_GEMM;
     return FP4W_PATH_FP4_GENERIC;
   }
   if (fp8_gemv_ok(M, K, bs)) return FP4W_PATH_FP8_GEMV;
+  if (M > 8 && fp8_skinny_ok(M, K, bs)) return FP4W_PATH_FP8_SKINNY;
   if (M > 8 && fp8_gemm_ok(M, K, bs)) return FP4W_PATH_FP8_GEMM;
   return FP4W_PATH_FP8_GENERIC;
 }
@@ -87,6 +95,9 @@ bool path_applies(int path, const MatmulArgs& a) {
     case FP4W_PATH_FP4_GEMV:
       return fp4_gemv_ok(a.M, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 16) &&
              aligned(a.scales, 4) && aligned(a.bias, 2) && aligned(a.Y, 2);
+    case FP4W_PATH_FP4_SKINNY:
+      return fp4_skinny_ok(a.M, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 16) &&
+             aligned(a.scales, 4) && aligned(a.bias, 2) && aligned(a.Y, 2);
     case FP4W_PATH_FP4_GEMM:
       return fp4_gemm_ok(a.M, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 8) &&
              aligned(a.bias, 2) && aligned(a.Y, 2);
@@ -95,6 +106,9 @@ bool path_applies(int path, const MatmulArgs& a) {
       return true;
     case FP4W_PATH_FP8_GEMV:
       return fp8_gemv_ok(a.M, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 16) &&
+             aligned(a.scales, 4) && aligned(a.bias, 2) && aligned(a.Y, 2);
+    case FP4W_PATH_FP8_SKINNY:
+      return fp8_skinny_ok(a.M, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 16) &&
              aligned(a.scales, 4) && aligned(a.bias, 2) && aligned(a.Y, 2);
     case FP4W_PATH_FP8_GEMM:
       return fp8_gemm_ok(a.M, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 16) &&
@@ -114,10 +128,10 @@ int plan_matmul(int op, const MatmulArgs& a, const void* scale_ptr_for_alias,
   if (st != FP4W_OK) return st;
   const bool fp4 = op == FP4W_OP_FP4_MATMUL;
   if (path != FP4W_PATH_AUTO) {
-    const bool family_ok = fp4 ? (path == FP4W_PATH_FP4_GEMV || path == FP4W_PATH_FP4_GEMM ||
-                                  path == FP4W_PATH_FP4_GENERIC)
-                               : (path == FP4W_PATH_FP8_GEMV || path == FP4W_PATH_FP8_GEMM ||
-                                  path == FP4W_PATH_FP8_GENERIC);
+    const bool family_ok = fp4 ? (path == FP4W_PATH_FP4_GEMV || path == FP4W_PATH_FP4_SKINNY ||
+                                  path == FP4W_PATH_FP4_GEMM || path == FP4W_PATH_FP4_GENERIC)
+                               : (path == FP4W_PATH_FP8_GEMV || path == FP4W_PATH_FP8_SKINNY ||
+                                  path == FP4W_PATH_FP8_GEMM || path == FP4W_PATH_FP8_GENERIC);
     if (!family_ok) return FP4W_ERR_PATH;
   }
   *chosen_out = FP4W_PATH_NONE;
@@ -149,9 +163,11 @@ int launch_matmul(int chosen, const MatmulArgs& a) {
   switch (chosen) {
     case FP4W_PATH_NONE: return FP4W_OK;
     case FP4W_PATH_FP4_GEMV: rc = fp4w::launch_fp4_gemv(a); break;
+    case FP4W_PATH_FP4_SKINNY: rc = fp4w::launch_fp4_skinny(a); break;
     case FP4W_PATH_FP4_GEMM: rc = fp4w::launch_fp4_gemm(a); break;
     case FP4W_PATH_FP4_GENERIC: rc = fp4w::launch_fp4_generic(a); break;
     case FP4W_PATH_FP8_GEMV: rc = fp4w::launch_fp8_gemv(a); break;
+    case FP4W_PATH_FP8_SKINNY: rc = fp4w::launch_fp8_skinny(a); break;
     case FP4W_PATH_FP8_GEMM: rc = fp4w::launch_fp8_gemm(a); break;
     case FP4W_PATH_FP8_GENERIC: rc = fp4w::launch_fp8_generic(a); break;
     default: return FP4W_ERR_PATH;
@@ -347,6 +363,8 @@ const char* fp4w_path_name(int path) {
     case FP4W_PATH_DEQUANT_GENERIC: return "dequant_generic";
     case FP4W_PATH_QDQ_VEC: return "qdq_vec";
     case FP4W_PATH_QDQ_GENERIC: return "qdq_generic";
+    case FP4W_PATH_FP4_SKINNY: return "fp4_skinny";
+    case FP4W_PATH_FP8_SKINNY: return "fp8_skinny";
     default: return "unknown";
   }
 }

@@ -52,6 +52,9 @@ int launch_fp4_gemv(const MatmulArgs& a);
 // M >= 1, block_size == 16, K % 64 == 0, scale_cols == K / 16,
 // A 16-byte aligned, B 8-byte aligned.
 int launch_fp4_gemm(const MatmulArgs& a);
+// 1 <= M <= 64, block_size == 16, K % 128 == 0, scale_cols == K / 16,
+// A / B 16-byte aligned, scales 4-byte aligned, bias / Y 2-byte aligned.
+int launch_fp4_skinny(const MatmulArgs& a);
 // any validated FP4 arguments (K may be 0)
 int launch_fp4_generic(const MatmulArgs& a);
 
@@ -60,6 +63,9 @@ int launch_fp4_generic(const MatmulArgs& a);
 int launch_fp8_gemv(const MatmulArgs& a);
 // M >= 1, block_size % 64 == 0, K % 64 == 0, A / B 16-byte aligned.
 int launch_fp8_gemm(const MatmulArgs& a);
+// 1 <= M <= 64, block_size % 128 == 0, K % 128 == 0, A / B 16-byte aligned,
+// scales 4-byte aligned.
+int launch_fp8_skinny(const MatmulArgs& a);
 // any validated FP8 arguments (K may be 0)
 int launch_fp8_generic(const MatmulArgs& a);
 

@@ -68,7 +68,9 @@ typedef enum {
   FP4W_PATH_DEQUANT_VEC = 8,     /* vectorised dequant: K % 8 == 0, block_size % 8 == 0 */
   FP4W_PATH_DEQUANT_GENERIC = 9, /* any legal dequant arguments */
   FP4W_PATH_QDQ_VEC = 10,        /* vectorised activation QDQ: M*K % 8 == 0 */
-  FP4W_PATH_QDQ_GENERIC = 11     /* any legal QDQ arguments */
+  FP4W_PATH_QDQ_GENERIC = 11,    /* any legal QDQ arguments */
+  FP4W_PATH_FP4_SKINNY = 12,     /* MFMA skinny matmul: 1 <= M <= 64, block_size 16, K % 128 == 0 */
+  FP4W_PATH_FP8_SKINNY = 13      /* MFMA skinny matmul: 1 <= M <= 64, block_size % 128 == 0, K % 128 == 0 */
 } fp4w_path;
 
 /* Operation selector for fp4w_select_path. */
@@ -100,7 +102,8 @@ int fp4w_matmul(const void* A, int64_t M, int64_t K, const uint8_t* B, int64_t N
                 const float* weight_scale_2, const void* bias, void* Y, int dtype, void* stream);
 
 /* Same as fp4w_matmul, with the kernel path forced (FP4W_PATH_AUTO, _FP4_GEMV,
- * _FP4_GEMM or _FP4_GENERIC).  FP4W_ERR_PATH if the path does not apply. */
+ * _FP4_SKINNY, _FP4_GEMM or _FP4_GENERIC).  FP4W_ERR_PATH if the path does not
+ * apply. */
 int fp4w_matmul_ex(const void* A, int64_t M, int64_t K, const uint8_t* B, int64_t N,
                    const uint8_t* weight_scale, int64_t scale_cols, int64_t block_size,
                    const float* weight_scale_2, const void* bias, void* Y, int dtype, void* stream,
@@ -120,7 +123,8 @@ int fp8w_matmul(const void* A, int64_t M, int64_t K, const uint8_t* B, int64_t N
                 const float* b_scale, int64_t scale_cols, int64_t block_size, const void* bias,
                 void* Y, int dtype, void* stream);
 
-/* Path-forcing variant (FP4W_PATH_AUTO, _FP8_GEMV, _FP8_GEMM, _FP8_GENERIC). */
+/* Path-forcing variant (FP4W_PATH_AUTO, _FP8_GEMV, _FP8_SKINNY, _FP8_GEMM,
+ * _FP8_GENERIC). */
 int fp8w_matmul_ex(const void* A, int64_t M, int64_t K, const uint8_t* B, int64_t N,
                    const float* b_scale, int64_t scale_cols, int64_t block_size, const void* bias,
                    void* Y, int dtype, void* stream, int path);

@@ -58,8 +58,11 @@ def test_dispatch_fp4():
     for M in (1, 2, 4, 8):
         assert sel(F, M, 5120, 5120, 16) == fw.PATH_FP4_GEMV
     assert sel(F, 1, 256, 512, 16) == fw.PATH_FP4_GEMV
-    # prefill GEMM for M > 8
-    assert sel(F, 9, 5120, 5120, 16) == fw.PATH_FP4_GEMM
+    # skinny matmul for 8 < M <= 64, prefill GEMM above
+    assert sel(F, 9, 5120, 5120, 16) == fw.PATH_FP4_SKINNY
+    assert sel(F, 64, 5120, 5120, 16) == fw.PATH_FP4_SKINNY
+    assert sel(F, 65, 5120, 5120, 16) == fw.PATH_FP4_GEMM
+    assert sel(F, 16, 5120, 5184, 16) == fw.PATH_FP4_GEMM       # K % 128 != 0, K % 64 == 0
     assert sel(F, 8192, 17408, 5120, 16) == fw.PATH_FP4_GEMM
     # outside the fast predicates -> generic ([Blog] "Existing FP4 tests did not
     # reach the prefill kernel": every leaf must be reachable and tested)
@@ -78,6 +81,10 @@ def test_dispatch_fp8():
     F = fw.OP_FP8_MATMUL
     assert sel(F, 4, 17408, 5120, 128) == fw.PATH_FP8_GEMV
     assert sel(F, 8192, 17408, 5120, 128) == fw.PATH_FP8_GEMM
+    assert sel(F, 16, 4096, 4096, 128) == fw.PATH_FP8_SKINNY
+    assert sel(F, 32, 4096, 4096, 128) == fw.PATH_FP8_SKINNY
+    assert sel(F, 65, 4096, 4096, 128) == fw.PATH_FP8_GEMM
+    assert sel(F, 16, 4096, 4096, 64) == fw.PATH_FP8_GEMM         # skinny needs bs % 128
     assert sel(F, 64, 256, 256, 64) == fw.PATH_FP8_GEMM
     assert sel(F, 4, 256, 256, 64) == fw.PATH_FP8_GENERIC      # GEMV needs bs % 128
     assert sel(F, 4, 256, 208, 128) == fw.PATH_FP8_GENERIC     # K % 128 != 0

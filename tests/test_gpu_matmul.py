@@ -40,6 +40,15 @@ FP4_CASES = [
     # active), ragged M and N, an odd number of K steps; the last column tile
     # takes the element-wise epilogue, the others the 16-byte one
     (700, 1800, 448, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMM]),
+    # skinny kernel: 1, 2 and 4 row tiles, ragged M and N, one window per
+    # wave (K = 128), long K, the persistent loop over many tiles
+    (9, 300, 256, 16, "bf16", True, "ceil", [fw.PATH_FP4_SKINNY, fw.PATH_FP4_GEMM]),
+    (16, 1000, 1024, 16, "fp16", True, "ceil", [fw.PATH_FP4_SKINNY]),
+    (17, 777, 640, 16, "bf16", False, "ceil", [fw.PATH_FP4_SKINNY, fw.PATH_FP4_GENERIC]),
+    (33, 4100, 512, 16, "fp16", True, "ceil", [fw.PATH_FP4_SKINNY]),
+    (64, 256, 5120, 16, "bf16", True, "ceil", [fw.PATH_FP4_SKINNY, fw.PATH_FP4_GEMM]),
+    (1, 40, 128, 16, "bf16", True, "ceil", [fw.PATH_FP4_SKINNY]),
+    (5, 65590, 256, 16, "fp16", False, "ceil", [fw.PATH_FP4_SKINNY]),
     (40, 96, 96, 16, "bf16", True, "ceil", [fw.PATH_FP4_GENERIC]),  # K % 64 != 0
     (6, 50, 40, 16, "fp16", True, "floor", [fw.PATH_FP4_GENERIC]),  # partial block, floor cols
     (4, 33, 30, 15, "bf16", True, "ceil", [fw.PATH_FP4_GENERIC]),   # odd block size
@@ -76,6 +85,7 @@ def _one_hot_fp4(M, N, K, dtype, seed):
 @pytest.mark.parametrize("M,N,K,path", [
     (8, 64, 256, fw.PATH_FP4_GEMV), (5, 48, 128, fw.PATH_FP4_GEMV), (1, 32, 4096, fw.PATH_FP4_GEMV),
     (8, 300, 512, fw.PATH_FP4_GEMM), (64, 512, 1024, fw.PATH_FP4_GEMM), (16, 40, 96, fw.PATH_FP4_GENERIC),
+    (13, 80, 512, fw.PATH_FP4_SKINNY), (64, 48, 1024, fw.PATH_FP4_SKINNY),
 ])
 def test_fp4_one_hot_probe_bit_exact(M, N, K, path, dtype):
     require_gpu()
@@ -148,6 +158,11 @@ FP8_CASES = [
     (7, 64, 384, 256, "bf16", True, "floor", [fw.PATH_FP8_GEMV, fw.PATH_FP8_GENERIC]),  # partial block
     (300, 520, 640, 128, "bf16", True, "ceil", [fw.PATH_FP8_GEMM]),
     (700, 1800, 448, 64, "fp16", False, "ceil", [fw.PATH_FP8_GEMM]),  # 24 tiles, ragged, odd K steps
+    (12, 300, 512, 128, "bf16", True, "ceil", [fw.PATH_FP8_SKINNY, fw.PATH_FP8_GEMM]),
+    (40, 1000, 640, 256, "fp16", False, "floor", [fw.PATH_FP8_SKINNY]),  # partial block, 3 row tiles
+    (64, 100, 384, 384, "bf16", True, "ceil", [fw.PATH_FP8_SKINNY, fw.PATH_FP8_GENERIC]),
+    (3, 50, 256, 128, "fp16", True, "ceil", [fw.PATH_FP8_SKINNY]),
+    (20, 20000, 1024, 128, "bf16", False, "ceil", [fw.PATH_FP8_SKINNY]),
     (64, 256, 448, 64, "fp16", False, "ceil", [fw.PATH_FP8_GEMM]),
     (33, 100, 320, 128, "bf16", True, "floor", [fw.PATH_FP8_GEMM, fw.PATH_FP8_GENERIC]),  # partial block
     (5, 40, 208, 128, "bf16", True, "ceil", [fw.PATH_FP8_GENERIC]),
@@ -169,6 +184,7 @@ def test_fp8_matmul_parity(M, N, K, bs, dtype, bias, partial, paths):
 @pytest.mark.parametrize("M,N,K,bs,path", [
     (8, 64, 512, 128, fw.PATH_FP8_GEMV), (3, 40, 384, 256, fw.PATH_FP8_GEMV),
     (16, 300, 512, 128, fw.PATH_FP8_GEMM), (40, 64, 208, 128, fw.PATH_FP8_GENERIC),
+    (24, 64, 512, 128, fw.PATH_FP8_SKINNY), (50, 33, 640, 128, fw.PATH_FP8_SKINNY),
 ])
 def test_fp8_one_hot_probe_bit_exact(M, N, K, bs, path):
     require_gpu()
