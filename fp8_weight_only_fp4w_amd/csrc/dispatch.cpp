@@ -99,8 +99,8 @@ bool path_applies(int path, const MatmulArgs& a) {
       return fp4_skinny_ok(a.M, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 16) &&
              aligned(a.scales, 4) && aligned(a.bias, 2) && aligned(a.Y, 2);
     case FP4W_PATH_FP4_GEMM:
-      return fp4_gemm_ok(a.M, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 8) &&
-             aligned(a.bias, 2) && aligned(a.Y, 2);
+      return fp4_gemm_ok(a.M, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 16) &&
+             aligned(a.scales, 4) && aligned(a.bias, 2) && aligned(a.Y, 2);
     case FP4W_PATH_FP4_GENERIC:
     case FP4W_PATH_FP8_GENERIC:
       return true;

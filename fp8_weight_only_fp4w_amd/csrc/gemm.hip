@@ -228,45 +228,67 @@ __global__ __launch_bounds__(256 * WM) void gemm_kernel(
   }
 }
 
-// FP4 prefill GEMM, large tiles.  Workgroup 256 (M) x 256 (N) x 64 (K per
-// step), 8 waves in a 2 (M) x 4 (N) grid, each wave 128 x 64 = 8 x 4 tiles of
-// v_mfma_f32_16x16x32 (128 FP32 accumulators per lane), two waves per SIMD:
-// a wave's weight decode (vector ALU) runs while the other wave's MFMAs
-// occupy the matrix core (one wave alone does not overlap the two).
-//  * Every operand tile (activations, packed weights, scale bytes) moves
-//    global -> LDS by direct loads (global_load_lds: no registers), three
-//    stages deep: the tiles of step t + 2 are requested during step t, so a
-//    load has two steps of MFMA work to arrive.  The only wait is, at the end
-//    of each step, for the tiles of the next step (loads complete in order).
-//  * LDS layout per stage: activations [256 rows][64] of T with 16-byte chunks
-//    XOR-swizzled by row (the swizzle is applied to the global addresses,
-//    since one direct load writes 1 KiB contiguously), packed weights
-//    [256 columns][32 bytes], scale bytes [256 columns][4].
+// Prefill GEMM, large tiles (FP4 and FP8).  Workgroup 256 (M) x 256 (N) x
+// 64 (K per step), 8 waves in a 2 (M) x 4 (N) grid, each wave 128 x 64 = 8 x 4
+// tiles of v_mfma_f32_16x16x32 (128 FP32 accumulators per lane), two waves
+// per SIMD: a wave's weight decode (vector ALU) runs while the other wave's
+// MFMAs occupy the matrix core (one wave alone does not overlap the two).
+//  * Every operand tile moves global -> LDS by direct loads (no registers).
+//    What limits these loads is the number of L2 requests rather than their
+//    bytes: a request carries one piece of at most 64 bytes of a line, so a
+//    4- or 32-byte piece costs as much as a full one (measured: the 4-byte
+//    scale pieces and 32-byte weight pieces of the first version of this
+//    kernel took more load time than the activation tiles, which are 80 % of
+//    the bytes).  So each operand is loaded in the largest contiguous pieces
+//    its layout allows:
+//     - activations: ring of 3 one-step stages [256 rows][64] of T (rows of
+//       128 contiguous bytes);
+//     - FP4 weights: ring of 2 slots of two steps each, 64 contiguous bytes
+//       per column; FP8 weights: ring of 3 one-step stages, 64 bytes per
+//       column;
+//     - scales: ring of 2 slots of eight steps each, 32 contiguous bytes per
+//       column (32 E4M3 bytes, or 8 FP32 block scales starting at the first
+//       block of the slot).  Weight and scale slots are read through a
+//       buffer descriptor per tile, so pieces past the matrix read zeros.
+//    The tiles of step t + 2 are requested during step t; the only wait is,
+//    at the end of each step, for the tiles of step t + 1 (loads complete in
+//    order), then one barrier.  A slot is refilled only after the barrier
+//    that ends its last reader's step.
+//  * LDS layouts are XOR-swizzled in 16-byte pieces (applied on the global
+//    side, since one direct load writes its 64 lanes' data contiguously), so
+//    the operand reads of a 16-lane group hit distinct banks.
 //  * Lane (li, g) takes k 16g .. 16g + 15 of each step for both operands
 //    (one 16-element scale block), split in two 8-k halves over two MFMAs;
 //    the E4M3 scale is folded into the decoded BF16/FP16 operand (exact).
 //  * Tile order: workgroups are dispatched round-robin over the 8 XCDs, each
 //    with its own L2, so the workgroup index is remapped to give every XCD a
-//    contiguous range of tiles, walked in groups of 8 tile rows.
+//    contiguous range of tiles, walked in groups of 2 tile rows.
 constexpr int L_BM = 256, L_BN = 256;
+constexpr int kScaleSteps = 8;  // steps per scale slot
 
 template <typename T, bool FP8>
-struct LargeStage {
-  T a[L_BM * kLdsRow];               // 32 KiB
-  uint8_t b[L_BN * (FP8 ? 64 : 32)];  // 16 / 8 KiB of weight bytes
-  uint8_t s[L_BN * 4];               // 1 KiB: 4 E4M3 bytes or one FP32 scale per column
+struct LargeLds {
+  T a[3][L_BM * kLdsRow];              // 3 x 32 KiB
+  uint8_t b[FP8 ? 3 : 2][L_BN * 64];   // FP8: 3 steps; FP4: 2 slots of 2 steps (16 KiB each)
+  uint8_t s[2][L_BN * 32];             // 2 x 8 KiB
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// direct 16-byte (or 4-byte) global -> LDS load: lane l writes lds + l * size
+// direct 16-byte global -> LDS load: lane l writes lds + 16 l
+__device__ __forceinline__ void load_lds16(const void* gptr, void* lds) {
+  __builtin_amdgcn_global_load_lds(gptr, (lds_ptr_t)(lds), 16, 0, 0);
+}
+
+// direct buffer -> LDS load of SIZE bytes per lane (lane l writes lds + SIZE l);
+// offsets past the descriptor's range read zeros
 template <int SIZE>
-__device__ __forceinline__ void load_lds(const void* gptr, void* lds) {
+__device__ __forceinline__ void buf_load_lds(rsrc_t r, uint32_t voff, void* lds) {
   static_assert(SIZE == 16 || SIZE == 4, "direct load size");
   if constexpr (SIZE == 16)
-    __builtin_amdgcn_global_load_lds(gptr, (lds_ptr_t)(lds), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(lds), 16, vgpr(voff), 0, 0, 0);
   else
-    __builtin_amdgcn_global_load_lds(gptr, (lds_ptr_t)(lds), 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(lds), 4, vgpr(voff), 0, 0, 0);
 }
 
 // wait until at most N vector-memory loads are in flight and every LDS access
@@ -288,30 +310,29 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
     int K, int cols, int bs, int tiles_m, int tiles_n) {
   typedef ActTraits<T> Tr;
   typedef typename Tr::vec8 V;
-  typedef LargeStage<T, FP8> Stage;
-  __shared__ __attribute__((aligned(16))) Stage st[3];
+  __shared__ __attribute__((aligned(16))) LargeLds<T, FP8> L;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, g = lane >> 4;
   const int wm = wave >> 2, wn = wave & 3;
 
-  // tile index: contiguous range per XCD, then groups of 8 tile rows
+  // tile index: contiguous range per XCD, then groups of GM tile rows
   const int ntiles = tiles_m * tiles_n;
   int t = blockIdx.x;
   if (ntiles % 8 == 0) t = (t % 8) * (ntiles / 8) + t / 8;
-  constexpr int GM = 8;
+  constexpr int GM = 2;
   const int per_group = GM * tiles_n;
   const int first_m = (t / per_group) * GM;
   const int gsize = min(tiles_m - first_m, GM);
   const int tm = first_m + (t % per_group) % gsize;
   const int tn = (t % per_group) / gsize;
   const int m0 = tm * L_BM, n0 = tn * L_BN;
+  const int rows_n = min(L_BN, N - n0);  // weight / scale rows of this tile
 
-  // Direct-load sources of this lane (element / byte offsets, step 0).
   // Activations: instruction j of wave w writes rows 8q .. 8q + 7 of the
   // stage, q = 8j + w; lane l lands in row 8q + l / 8, LDS chunk l % 8, which
-  // holds global chunk (l % 8) ^ (l / 8) under the swizzle.
+  // holds global chunk (l % 8) ^ lds_swz(row).
   int a_off[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -319,49 +340,68 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
     const int chunk = (lane & 7) ^ lds_swz(row);
     a_off[j] = min(m0 + row, M - 1) * K + 8 * chunk;
   }
-  // Weights.  FP4 (32 bytes per column and step): instruction j of wave w
-  // covers columns 32q .. 32q + 31, q = w; lane l lands in column 32q + l / 2,
-  // 16-byte piece l % 2.  FP8 (64 bytes): q = 8j + w, 16 columns per
-  // instruction, lane l in column 16q + l / 4, piece l % 4.  Pieces are
-  // swizzled with the column (global piece = LDS piece ^ bit pattern of the
-  // column) so the 16 columns read by a 16-lane group fall in distinct banks.
-  constexpr int kBBytes = FP8 ? 64 : 32;            // per column and step
-  constexpr int kBLoads = FP8 ? 2 : 1;              // direct loads per wave and step
-  constexpr int kColsPerLoad = 1024 / kBBytes;      // columns per direct load
-  constexpr int kPieces = kBBytes / 16;
-  auto b_swz = [](int col) { return FP8 ? (col & 3) : ((col >> 3) & 1); };
-  const size_t b_row = FP8 ? static_cast<size_t>(K) : static_cast<size_t>(K / 2);
-  int b_off[kBLoads];
+  // Weights.  FP4 slot (two steps, 64 bytes per column, pieces 0-1 = the even
+  // step, 2-3 = the odd step): instruction j of wave w covers columns
+  // 16q .. 16q + 15, q = 8j + w; lane l lands in column 16q + l / 4, LDS piece
+  // l % 4, holding global piece (l % 4) ^ ((col >> 2) & 3).  FP8 stage (64
+  // bytes per column): same columns, LDS piece l % 4 holds global piece
+  // (l % 4) ^ (col & 3).
+  const uint32_t b_row = FP8 ? static_cast<uint32_t>(K) : static_cast<uint32_t>(K / 2);
+  auto b_swz = [](int col) { return FP8 ? (col & 3) : ((col >> 2) & 3); };
+  uint32_t b_off[2];  // FP4: byte offset in the tile's descriptor; FP8: global byte offset
 #pragma unroll
-  for (int j = 0; j < kBLoads; ++j) {
-    const int col = kColsPerLoad * (8 * j + wave) + lane / kPieces;
-    const int piece = (lane % kPieces) ^ b_swz(col);
-    b_off[j] = min(n0 + col, N - 1) * static_cast<int>(b_row) + 16 * piece;
+  for (int j = 0; j < 2; ++j) {
+    const int col = 16 * (8 * j + wave) + (lane >> 2);
+    const int piece = (lane & 3) ^ b_swz(col);
+    b_off[j] = FP8 ? static_cast<uint32_t>(min(n0 + col, N - 1)) * b_row + 16u * piece
+                   : static_cast<uint32_t>(col) * b_row + 16u * piece;
   }
-  // scales: wave w covers columns 64 (w % 4) .. + 63, 4 bytes each: the 4
-  // E4M3 bytes of the step (FP4) or the FP32 scale of the step's block (FP8;
-  // block_size % 64 == 0, so a step lies in one block).  Waves 4..7 repeat
-  // waves 0..3: identical data to identical addresses, which keeps the number
-  // of loads per wave uniform.
-  const int s_col = 64 * (wave & 3) + lane;
-  const int s_off = min(n0 + s_col, N - 1) * cols;  // elements (bytes FP4, floats FP8)
+  const rsrc_t b_rsrc = make_rsrc(B + static_cast<size_t>(n0) * b_row, static_cast<uint32_t>(rows_n) * b_row);
+  // Scales: slot of 8 steps, 32 bytes per column.  Instruction j of wave w
+  // (4-byte pieces) covers columns 8q .. 8q + 7, q = 4w + j; lane l lands in
+  // column 8q + l / 8, LDS piece (l % 8) / 4 (16-byte), holding global piece
+  // ((l % 8) / 4) ^ ((col >> 3) & 1).
+  const uint32_t s_row = FP8 ? static_cast<uint32_t>(cols) * 4u : static_cast<uint32_t>(cols);
+  uint32_t s_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int col = 8 * (4 * wave + j) + (lane >> 3);
+    const int d = lane & 7;
+    const int piece = (d >> 2) ^ ((col >> 3) & 1);
+    s_off[j] = static_cast<uint32_t>(col) * s_row + 16u * piece + 4u * (d & 3);
+  }
+  const rsrc_t s_rsrc = make_rsrc(scales + static_cast<size_t>(n0) * s_row, static_cast<uint32_t>(rows_n) * s_row);
+  const int spb = FP8 ? bs / BK : 1;  // steps per FP8 scale block (block_size % 64 == 0)
+  // FP8: first scale column of the slot holding steps 8c .. 8c + 7
+  auto slot_col = [&](int c) { return min(kScaleSteps * c / spb, cols - 1); };
 
   const int nsteps = K / BK;
-  auto issue = [&](int step, Stage& st) {
+  // loads a wave issues for step u: activations, weights (FP4: at even steps,
+  // for the pair), scales (at the first step of each slot)
+  auto loads_for = [](int u) { return 4 + (FP8 ? 2 : ((u & 1) ? 0 : 2)) + (u % kScaleSteps == 0 ? 4 : 0); };
+  auto issue = [&](int u) {
+    T* a_dst = L.a[u % 3];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      load_lds<16>(A + a_off[j] + step * BK, &st.a[(8 * j + wave) * 8 * kLdsRow]);
-#pragma unroll
-    for (int j = 0; j < kBLoads; ++j)
-      load_lds<16>(B + b_off[j] + static_cast<size_t>(step) * (FP8 ? BK : BK / 2), &st.b[(8 * j + wave) * 1024]);
+    for (int j = 0; j < 4; ++j) load_lds16(A + a_off[j] + u * BK, &a_dst[(8 * j + wave) * 8 * kLdsRow]);
     if constexpr (FP8) {
-      const int col = min(step * BK / bs, cols - 1);
-      load_lds<4>(reinterpret_cast<const float*>(scales) + s_off + col, &st.s[64 * (wave & 3) * 4]);
+      uint8_t* b_dst = L.b[u % 3];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) load_lds16(B + b_off[j] + static_cast<size_t>(u) * BK, &b_dst[(8 * j + wave) * 1024]);
     } else {
-      load_lds<4>(scales + s_off + step * (BK / 16), &st.s[64 * (wave & 3) * 4]);
+      if ((u & 1) == 0) {
+        uint8_t* b_dst = L.b[(u >> 1) & 1];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) buf_load_lds<16>(b_rsrc, b_off[j] + 32u * u, &b_dst[(8 * j + wave) * 1024]);
+      }
+    }
+    if (u % kScaleSteps == 0) {
+      const int c = u / kScaleSteps;
+      uint8_t* s_dst = L.s[c & 1];
+      const uint32_t base = FP8 ? 4u * static_cast<uint32_t>(slot_col(c)) : 32u * static_cast<uint32_t>(c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) buf_load_lds<4>(s_rsrc, s_off[j] + base, &s_dst[(4 * wave + j) * 256]);
     }
   };
-  constexpr int kLoadsPerStep = 4 + kBLoads + 1;  // direct loads per wave and step
 
   f32x4 acc[8][4];
 #pragma unroll
@@ -369,21 +409,28 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const Stage& st) {
+  auto compute = [&](int u) {
+    const T* a_src = L.a[u % 3];
+    const uint8_t* s_src = L.s[(u / kScaleSteps) & 1];
     // lane (li, g): k 16g .. 16g + 15 of its 4 columns (FP4 8 bytes, FP8 16)
     u32x4 bw[4];
     float sc[4];
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) {
       const int col = 64 * wn + 16 * ns + li;
+      const int ss = (col >> 3) & 1;
       if constexpr (FP8) {
-        bw[ns] = *reinterpret_cast<const u32x4*>(&st.b[col * 64 + 16 * (g ^ b_swz(col))]);
-        sc[ns] = *reinterpret_cast<const float*>(&st.s[col * 4]);
+        bw[ns] = *reinterpret_cast<const u32x4*>(&L.b[u % 3][col * 64 + 16 * (g ^ b_swz(col))]);
+        const int idx = min(u / spb, cols - 1) - slot_col(u / kScaleSteps);  // 0 .. 7
+        sc[ns] = *reinterpret_cast<const float*>(&s_src[col * 32 + 16 * ((idx >> 2) ^ ss) + 4 * (idx & 3)]);
       } else {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(&st.b[col * 32 + 16 * ((g >> 1) ^ b_swz(col)) + 8 * (g & 1)]);
+        const int gp = 2 * (u & 1) + (g >> 1);
+        const u32x2 v = *reinterpret_cast<const u32x2*>(
+            &L.b[(u >> 1) & 1][col * 64 + 16 * (gp ^ b_swz(col)) + 8 * (g & 1)]);
         bw[ns].x = v.x;
         bw[ns].y = v.y;
-        sc[ns] = e4m3_to_f32<0>(st.s[col * 4 + g]);
+        const int st8 = u % kScaleSteps;
+        sc[ns] = e4m3_to_f32<0>(s_src[col * 32 + 16 * ((st8 >> 2) ^ ss) + 4 * (st8 & 3) + g]);
       }
     }
 #pragma unroll
@@ -391,7 +438,7 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
       V aop[8];
 #pragma unroll
       for (int ms = 0; ms < 8; ++ms)
-        aop[ms] = *reinterpret_cast<const V*>(&st.a[lds_index(128 * wm + 16 * ms + li, 2 * g + s)]);
+        aop[ms] = *reinterpret_cast<const V*>(&a_src[lds_index(128 * wm + 16 * ms + li, 2 * g + s)]);
       V bop[4];
 #pragma unroll
       for (int ns = 0; ns < 4; ++ns) {
@@ -407,26 +454,32 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
     }
   };
 
-  auto do_step = [&](int step, const Stage& cur, Stage& ahead2) {
-    const bool issue2 = step + 2 < nsteps;
-    if (issue2) issue(step + 2, ahead2);
-    compute(cur);
-    if (issue2)
-      wait_barrier<kLoadsPerStep>();  // the tiles of step + 1 have landed
-    else
-      wait_barrier<0>();
+  // wait for everything but the n loads of the newest step, then barrier
+  auto wait_all_but = [](int n) {
+    switch (n) {
+      case 4: wait_barrier<4>(); break;
+      case 6: wait_barrier<6>(); break;
+      case 8: wait_barrier<8>(); break;
+      case 10: wait_barrier<10>(); break;
+      default: wait_barrier<0>(); break;
+    }
   };
 
-  issue(0, st[0]);
-  if (nsteps > 1) issue(1, st[1]);
-  if (nsteps > 1)
-    wait_barrier<kLoadsPerStep>();
-  else
+  issue(0);
+  if (nsteps > 1) {
+    issue(1);
+    wait_all_but(loads_for(1));
+  } else {
     wait_barrier<0>();
-  for (int step = 0; step < nsteps; step += 3) {
-    do_step(step, st[0], st[2]);
-    if (step + 1 < nsteps) do_step(step + 1, st[1], st[0]);
-    if (step + 2 < nsteps) do_step(step + 2, st[2], st[1]);
+  }
+  for (int step = 0; step < nsteps; ++step) {
+    const bool ahead = step + 2 < nsteps;
+    if (ahead) issue(step + 2);
+    compute(step);
+    if (ahead)
+      wait_all_but(loads_for(step + 2));  // the tiles of step + 1 have landed
+    else
+      wait_barrier<0>();
   }
 
   // Epilogue: lane (li, g) holds columns 64 wn + 16 ns + li and rows
@@ -436,7 +489,7 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
   // ragged edge, or outputs that are not 16-byte aligned, store element-wise.
   const float ws2 = FP8 ? 1.0f : *ws2p;
   constexpr int kOutPitch = L_BN + 8;  // elements per staged row (breaks bank aliasing)
-  T* out = reinterpret_cast<T*>(&st[0]);
+  T* out = reinterpret_cast<T*>(&L.a[0][0]);
   const bool wide = (N % 8 == 0) && (reinterpret_cast<uintptr_t>(Y) % 16 == 0) && n0 + L_BN <= N;
   float bsum[4];
 #pragma unroll

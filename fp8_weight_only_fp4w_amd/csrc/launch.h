@@ -50,7 +50,7 @@ struct QdqArgs {
 // A / B 16-byte aligned, scales 4-byte aligned, bias 2-byte aligned.
 int launch_fp4_gemv(const MatmulArgs& a);
 // M >= 1, block_size == 16, K % 64 == 0, scale_cols == K / 16,
-// A 16-byte aligned, B 8-byte aligned.
+// A / B 16-byte aligned, scales 4-byte aligned.
 int launch_fp4_gemm(const MatmulArgs& a);
 // 1 <= M <= 64, block_size == 16, K % 128 == 0, scale_cols == K / 16,
 // A / B 16-byte aligned, scales 4-byte aligned, bias / Y 2-byte aligned.
