@@ -306,6 +306,20 @@ def extra_fp8(steps, warmup, reps=10):
     flops = 2.0 * p8.M * p8.N * p8.K
     tp = time_calls([lambda: fw.fp8w_matmul(d["A"], d["B"][0], d["bs"][0], None, 128, out=out)], reps, 3) / reps
     res.update({"prefill_ms": round(tp * 1e3, 3), "prefill_TFLOPs": round(flops / tp / 1e12, 1)})
+    # the pages' default path: dequant to an [N, K] scratch, then hipBLASLt (torch.matmul)
+    scratch = torch.empty(p8.N, p8.K, dtype=torch.bfloat16, device="cuda")
+
+    def base():
+        fw.fp8w_dequant(d["B"][0], d["bs"][0], 128, out=scratch)
+        torch.matmul(d["A"], scratch.t(), out=out)
+
+    tb = time_calls([base], reps, 3) / reps
+    td = time_calls([lambda: fw.fp8w_dequant(d["B"][0], d["bs"][0], 128, out=scratch)], reps * 5, 3) / (reps * 5)
+    dq_bytes = p8.B.nbytes + p8.b_scale.nbytes + scratch.numel() * 2
+    res.update({"prefill_baseline_dequant_plus_hipblaslt_ms": round(tb * 1e3, 3),
+                "prefill_baseline_TFLOPs": round(flops / tb / 1e12, 1),
+                "dequant_ms": round(td * 1e3, 4), "dequant_GBps": round(dq_bytes / td / 1e9, 1)})
+    del scratch
     return res
 
 
@@ -319,6 +333,33 @@ def extra_wide(steps, warmup):
     t = time_rotating(lambda r: fw.fp4w_matmul(d["A"], d["B"][r], d["ws"][r], d["ws2"], None, 16, out=out),
                       R, min(steps, 64))
     return {"us": round(t * 1e6, 2), "weight_GBps": round(wb / t / 1e9, 1), "copies": R}
+
+
+def extra_skinny(steps, warmup):
+    """8 < M <= 64 (batched decode / short prefill chunks): the skinny MFMA
+    kernel, weights rotated past the last-level cache."""
+    res = {}
+    for N, K in ((4096, 4096), (17408, 5120)):
+        for M in (16, 32, 64):
+            p = workloads.make_fp4(M, N, K, 16, "bf16", seed=M)
+            wb = p.B.nbytes + p.weight_scale.nbytes
+            R = copies_for(wb)
+            d = fp4_on_device(p, copies=R)
+            out = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+            t = time_rotating(lambda r: fw.fp4w_matmul(d["A"], d["B"][r], d["ws"][r], d["ws2"], None, 16,
+                                                       out=out), R, min(steps, 64))
+            del d
+            p8 = workloads.make_fp8(M, N, K, 128, "bf16", seed=M)
+            wb8 = p8.B.nbytes + p8.b_scale.nbytes
+            R8 = copies_for(wb8)
+            d8 = fp8_on_device(p8, copies=R8)
+            t8 = time_rotating(lambda r: fw.fp8w_matmul(d8["A"], d8["B"][r], d8["bs"][r], None, 128, out=out),
+                               R8, min(steps, 64))
+            del d8
+            torch.cuda.empty_cache()
+            res[f"M{M}_N{N}_K{K}"] = {"fp4_us": round(t * 1e6, 2), "fp4_weight_GBps": round(wb / t / 1e9, 1),
+                                      "fp8_us": round(t8 * 1e6, 2), "fp8_weight_GBps": round(wb8 / t8 / 1e9, 1)}
+    return res
 
 
 def extra_w8a8(steps, warmup):
@@ -454,6 +495,7 @@ def main():
                          ("fp4_gemv_wide", lambda: extra_wide(args.steps, args.warmup)),
                          ("fp8", lambda: extra_fp8(args.steps, args.warmup)),
                          ("fp8_w8a8", lambda: extra_w8a8(args.steps, args.warmup)),
+                         ("skinny", lambda: extra_skinny(args.steps, args.warmup)),
                          ("fp4_prefill", extra_prefill_fp4)):
             t0 = time.perf_counter()
             extra[name] = fn()

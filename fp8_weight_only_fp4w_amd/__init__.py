@@ -16,6 +16,8 @@ The functions carry the C ABI's names (include/fp4w.h):
   Documentation" §2).
 * ``fp4w_dequant(B, weight_scale, weight_scale_2, block_size=16, dtype=...)``:
   the [N, K] FP16/BF16 expansion of B.
+* ``fp8w_dequant(B, b_scale, block_size=128, dtype=...)``: the [N, K]
+  FP16/BF16 expansion of FP8 weights (FP8 document §5, step 1).
 * ``fp8w_qdq_activation(A, a_scale)``: fp8_e4m3(A / a_scale) * a_scale in A's
   dtype, the activation step of the FP8 operator's optional W8A8 mode (FP8
   document §6).
@@ -43,14 +45,15 @@ PATH_FP8_GEMV, PATH_FP8_GEMM, PATH_FP8_GENERIC = 5, 6, 7
 PATH_DEQUANT_VEC, PATH_DEQUANT_GENERIC = 8, 9
 PATH_QDQ_VEC, PATH_QDQ_GENERIC = 10, 11
 PATH_FP4_SKINNY, PATH_FP8_SKINNY = 12, 13
+PATH_FP8_DEQUANT_VEC, PATH_FP8_DEQUANT_GENERIC = 14, 15
 # operations (fp4w_op)
-OP_FP4_MATMUL, OP_FP8_MATMUL, OP_FP4_DEQUANT, OP_FP8_QDQ = 0, 1, 2, 3
+OP_FP4_MATMUL, OP_FP8_MATMUL, OP_FP4_DEQUANT, OP_FP8_QDQ, OP_FP8_DEQUANT = 0, 1, 2, 3, 4
 # dtypes (fp4w_dtype)
 F16, BF16 = 0, 1
 
 EXPORTED = (
     "fp4w_matmul", "fp4w_matmul_ex", "fp8w_matmul", "fp8w_matmul_ex", "fp4w_dequant",
-    "fp4w_dequant_ex", "fp8w_qdq_activation", "fp8w_qdq_activation_ex", "fp8w_matmul_w8a8",
+    "fp4w_dequant_ex", "fp8w_dequant", "fp8w_dequant_ex", "fp8w_qdq_activation", "fp8w_qdq_activation_ex", "fp8w_matmul_w8a8",
     "fp4w_select_path", "fp4w_status_string", "fp4w_path_name",
 )
 
@@ -85,6 +88,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp4w_dequant_ex.restype = i32
     lib.fp4w_dequant.argtypes = [vp, i64, i64, vp, i64, i64, vp, vp, i32, vp]
     lib.fp4w_dequant.restype = i32
+    lib.fp8w_dequant_ex.argtypes = [vp, i64, i64, vp, i64, i64, vp, i32, vp, i32]
+    lib.fp8w_dequant_ex.restype = i32
+    lib.fp8w_dequant.argtypes = [vp, i64, i64, vp, i64, i64, vp, i32, vp]
+    lib.fp8w_dequant.restype = i32
     lib.fp8w_qdq_activation_ex.argtypes = [vp, i64, i64, vp, vp, i32, vp, i32]
     lib.fp8w_qdq_activation_ex.restype = i32
     lib.fp8w_qdq_activation.argtypes = [vp, i64, i64, vp, vp, i32, vp]
@@ -291,4 +298,24 @@ def fp8w_matmul_w8a8(A: torch.Tensor, B: torch.Tensor, b_scale: torch.Tensor, a_
                               _ptr(a_scale), _ptr(bias), _ptr(workspace), _ptr(out),
                               _dtype_code(A.dtype), _stream(dev))
     _check(st, "fp8w_matmul_w8a8")
+    return out
+
+
+def fp8w_dequant(B: torch.Tensor, b_scale: torch.Tensor, block_size: int = 128,
+                 dtype: torch.dtype = torch.bfloat16, out: torch.Tensor = None,
+                 path: int = PATH_AUTO) -> torch.Tensor:
+    lib = load_library()
+    dev = B.device
+    B = _bytes(B)
+    N, K = B.shape
+    for t, name in ((B, "B"), (b_scale, "b_scale")):
+        _need(t, name, dev)
+    if b_scale.dtype != torch.float32 or b_scale.dim() != 2 or b_scale.shape[0] != N:
+        raise ValueError("b_scale must be float32 [N, scale_cols]")
+    if out is None:
+        out = torch.empty(N, K, dtype=dtype, device=dev)
+    _need(out, "out", dev)
+    st = lib.fp8w_dequant_ex(_ptr(B), N, K, _ptr(b_scale), b_scale.shape[1], block_size, _ptr(out),
+                             _dtype_code(out.dtype), _stream(dev), path)
+    _check(st, "fp8w_dequant")
     return out

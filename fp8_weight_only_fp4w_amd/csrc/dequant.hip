@@ -1,4 +1,5 @@
-// FP4 -> FP16/BF16 dequant kernels (the library's fp4w_dequant).
+// FP4 and FP8 -> FP16/BF16 dequant kernels (the library's fp4w_dequant and
+// fp8w_dequant).
 //
 // out[n, k] = RNE_T( RNE_f32( e2m1(B[n,k]) * e4m3(ws[n, col(k)]) * ws2 ) )
 // ([FP4 doc] §2 Weight Format; [FP4 doc] §5 step 1; the vectorised kernel of
@@ -16,7 +17,15 @@
 //    order of the formula, then one rounding to T;
 //  * the tensor scale ws2 is one scalar load per thread, kept in a register.
 //
+// FP8: out[n, k] = RNE_T( RNE_f32( e4m3(B[n, k]) * b_scale[n, col(k)] ) ),
+// the expansion of the FP8 operator's default path ([FP8 doc] §5, step 1,
+// whose fast kernel gives each thread one aligned 16-element K chunk).  Here
+// too a 16-element chunk (one 16-byte load, two 16-byte stores) stays inside
+// one scale block when block_size % 16 == 0, so one FP32 scale is read per
+// chunk; the chunks form one flat grid-stride stream as for FP4.
+//
 // [FP4 doc] = "MatMulBlockQuantizedFp4Weight - CUDA Operator Documentation"
+// [FP8 doc] = "MatMulBlockQuantizedFp8Weight - CUDA Operator Documentation"
 // [Blog]    = "ONNX Runtime #32128 - Why Dequantizing 4-Bit Weights Became the
 //             Most Expensive Kernel in H200 Prefill"
 
@@ -117,6 +126,56 @@ __global__ __launch_bounds__(256) void dequant_generic_kernel(
   }
 }
 
+// FP8, 16 elements per chunk: one 16-byte weight load, one scale, two
+// 16-byte stores.
+template <typename T>
+__global__ __launch_bounds__(kDqThreads) void fp8_dequant_vec_kernel(
+    const u32x4* __restrict__ Bv, const float* __restrict__ scales, u32x4* __restrict__ out,
+    uint32_t total_chunks, FastDiv chunks_per_row, FastDiv chunks_per_block, uint32_t cols) {
+  const uint32_t stride = gridDim.x * kDqThreads * kDqUnroll;
+  for (uint32_t base = blockIdx.x * kDqThreads * kDqUnroll + threadIdx.x; base < total_chunks;
+       base += stride) {
+    u32x4 w[kDqUnroll];
+    float sc[kDqUnroll];
+#pragma unroll
+    for (int u = 0; u < kDqUnroll; ++u) {
+      const uint32_t c = base + u * kDqThreads;
+      if (c < total_chunks) {
+        const uint32_t row = fdiv(c, chunks_per_row);
+        const uint32_t cc = c - row * chunks_per_row.d;
+        const uint32_t col = min(fdiv(cc, chunks_per_block), cols - 1);
+        w[u] = Bv[c];
+        sc[u] = scales[static_cast<uint64_t>(row) * cols + col];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kDqUnroll; ++u) {
+      const uint32_t c = base + u * kDqThreads;
+      if (c < total_chunks) {
+        out[2 * static_cast<uint64_t>(c)] = __builtin_bit_cast(u32x4, decode8_fp8_scaled<T>(w[u].x, w[u].y, sc[u]));
+        out[2 * static_cast<uint64_t>(c) + 1] =
+            __builtin_bit_cast(u32x4, decode8_fp8_scaled<T>(w[u].z, w[u].w, sc[u]));
+      }
+    }
+  }
+}
+
+// FP8, any shape: one element per iteration.
+template <typename T>
+__global__ __launch_bounds__(256) void fp8_dequant_generic_kernel(
+    const uint8_t* __restrict__ B, const float* __restrict__ scales, T* __restrict__ out, int64_t N,
+    int64_t K, int64_t bs, int64_t cols) {
+  const int64_t total = N * K;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t row = e / K;
+    const int64_t k = e - row * K;
+    const float q = e4m3_to_f32<0>(B[e]);
+    const float s = scales[row * cols + min(k / bs, cols - 1)];
+    out[e] = round_to<T>(q * s);
+  }
+}
+
 int grid_for(int64_t work_items, int per_block) {
   int64_t g = (work_items + per_block - 1) / per_block;
   const int64_t cap = 256 * 16;  // 256 CUs, enough waves in flight to cover HBM latency
@@ -156,6 +215,36 @@ int launch_dequant_generic(const DequantArgs& a) {
   else
     hipLaunchKernelGGL(dequant_generic_kernel<_Float16>, dim3(grid), dim3(256), 0, s, a.B, a.scales,
                        a.ws2, static_cast<_Float16*>(a.out), a.N, a.K, a.block_size, a.scale_cols);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_fp8_dequant_vec(const Fp8DequantArgs& a) {
+  const uint32_t cpr = static_cast<uint32_t>(a.K / 16);
+  const uint32_t total = static_cast<uint32_t>(a.N * (a.K / 16));
+  const FastDiv f_row = make_fastdiv(cpr);
+  const FastDiv f_blk = make_fastdiv(static_cast<uint32_t>(a.block_size / 16));
+  const int grid = grid_for(total, kDqThreads * kDqUnroll);
+  hipStream_t s = static_cast<hipStream_t>(a.stream);
+  if (a.act == Act::BF16)
+    hipLaunchKernelGGL(fp8_dequant_vec_kernel<__bf16>, dim3(grid), dim3(kDqThreads), 0, s,
+                       reinterpret_cast<const u32x4*>(a.B), a.scales, static_cast<u32x4*>(a.out), total,
+                       f_row, f_blk, static_cast<uint32_t>(a.scale_cols));
+  else
+    hipLaunchKernelGGL(fp8_dequant_vec_kernel<_Float16>, dim3(grid), dim3(kDqThreads), 0, s,
+                       reinterpret_cast<const u32x4*>(a.B), a.scales, static_cast<u32x4*>(a.out), total,
+                       f_row, f_blk, static_cast<uint32_t>(a.scale_cols));
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_fp8_dequant_generic(const Fp8DequantArgs& a) {
+  const int grid = grid_for(a.N * a.K, 256);
+  hipStream_t s = static_cast<hipStream_t>(a.stream);
+  if (a.act == Act::BF16)
+    hipLaunchKernelGGL(fp8_dequant_generic_kernel<__bf16>, dim3(grid), dim3(256), 0, s, a.B, a.scales,
+                       static_cast<__bf16*>(a.out), a.N, a.K, a.block_size, a.scale_cols);
+  else
+    hipLaunchKernelGGL(fp8_dequant_generic_kernel<_Float16>, dim3(grid), dim3(256), 0, s, a.B, a.scales,
+                       static_cast<_Float16*>(a.out), a.N, a.K, a.block_size, a.scale_cols);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

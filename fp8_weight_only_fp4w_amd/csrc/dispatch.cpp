@@ -17,6 +17,7 @@ namespace {
 
 using fp4w::Act;
 using fp4w::DequantArgs;
+using fp4w::Fp8DequantArgs;
 using fp4w::MatmulArgs;
 using fp4w::QdqArgs;
 
@@ -69,12 +70,19 @@ bool fp8_gemm_ok(int64_t M, int64_t K, int64_t bs) { return M >= 1 && bs % 64 ==
 bool dequant_vec_ok(int64_t N, int64_t K, int64_t bs) {
   return K % 8 == 0 && bs % 8 == 0 && K > 0 && N > 0 && (N * (K / 8)) < (int64_t(1) << 32);
 }
+bool fp8_dequant_vec_ok(int64_t N, int64_t K, int64_t bs) {
+  return K % 16 == 0 && bs % 16 == 0 && K > 0 && N > 0 && (N * (K / 16)) < (int64_t(1) << 32);
+}
 
 // Path choice from sizes alone (pointers assumed 16-byte aligned).
 int shape_path(int op, int64_t M, int64_t N, int64_t K, int64_t bs) {
   if (op == FP4W_OP_FP4_DEQUANT) {
     if (N == 0 || K == 0) return FP4W_PATH_NONE;
     return dequant_vec_ok(N, K, bs) ? FP4W_PATH_DEQUANT_VEC : FP4W_PATH_DEQUANT_GENERIC;
+  }
+  if (op == FP4W_OP_FP8_DEQUANT) {
+    if (N == 0 || K == 0) return FP4W_PATH_NONE;
+    return fp8_dequant_vec_ok(N, K, bs) ? FP4W_PATH_FP8_DEQUANT_VEC : FP4W_PATH_FP8_DEQUANT_GENERIC;
   }
   if (M == 0 || N == 0) return FP4W_PATH_NONE;
   if (op == FP4W_OP_FP4_MATMUL) {
@@ -314,6 +322,34 @@ int fp4w_dequant_ex(const uint8_t* B, int64_t N, int64_t K, const uint8_t* weigh
   return rc == 0 ? FP4W_OK : FP4W_ERR_LAUNCH;
 }
 
+int fp8w_dequant_ex(const uint8_t* B, int64_t N, int64_t K, const float* b_scale, int64_t scale_cols,
+                    int64_t block_size, void* out, int dtype, void* stream, int path) {
+  if (dtype != FP4W_F16 && dtype != FP4W_BF16) return FP4W_ERR_DTYPE;
+  int st = check_shape(FP4W_OP_FP8_DEQUANT, 0, N, K, block_size, scale_cols);
+  if (st != FP4W_OK) return st;
+  if (path != FP4W_PATH_AUTO && path != FP4W_PATH_FP8_DEQUANT_VEC && path != FP4W_PATH_FP8_DEQUANT_GENERIC)
+    return FP4W_ERR_PATH;
+  if (N == 0 || K == 0) return FP4W_OK;
+  if (B == nullptr || b_scale == nullptr || out == nullptr) return FP4W_ERR_NULL;
+  const int64_t obytes = N * K * 2;
+  if (overlaps(out, obytes, B, N * K) || overlaps(out, obytes, b_scale, N * scale_cols * 4))
+    return FP4W_ERR_ALIAS;
+  Fp8DequantArgs a{B, b_scale, out, N, K, block_size, scale_cols, static_cast<Act>(dtype), stream};
+  const bool vec_ok = fp8_dequant_vec_ok(N, K, block_size) && aligned(B, 16) && aligned(out, 16) &&
+                      aligned(b_scale, 4);
+  int chosen = path;
+  if (path == FP4W_PATH_AUTO) chosen = vec_ok ? FP4W_PATH_FP8_DEQUANT_VEC : FP4W_PATH_FP8_DEQUANT_GENERIC;
+  if (chosen == FP4W_PATH_FP8_DEQUANT_VEC && !vec_ok) return FP4W_ERR_PATH;
+  const int rc = chosen == FP4W_PATH_FP8_DEQUANT_VEC ? fp4w::launch_fp8_dequant_vec(a)
+                                                     : fp4w::launch_fp8_dequant_generic(a);
+  return rc == 0 ? FP4W_OK : FP4W_ERR_LAUNCH;
+}
+
+int fp8w_dequant(const uint8_t* B, int64_t N, int64_t K, const float* b_scale, int64_t scale_cols,
+                 int64_t block_size, void* out, int dtype, void* stream) {
+  return fp8w_dequant_ex(B, N, K, b_scale, scale_cols, block_size, out, dtype, stream, FP4W_PATH_AUTO);
+}
+
 int fp4w_dequant(const uint8_t* B, int64_t N, int64_t K, const uint8_t* weight_scale,
                  int64_t scale_cols, int64_t block_size, const float* weight_scale_2, void* out,
                  int dtype, void* stream) {
@@ -328,9 +364,11 @@ int fp4w_select_path(int op, int64_t M, int64_t N, int64_t K, int64_t block_size
     if (M == 0 || K == 0) return FP4W_PATH_NONE;
     return qdq_vec_ok(M * K) ? FP4W_PATH_QDQ_VEC : FP4W_PATH_QDQ_GENERIC;
   }
-  if (op != FP4W_OP_FP4_MATMUL && op != FP4W_OP_FP8_MATMUL && op != FP4W_OP_FP4_DEQUANT)
+  if (op != FP4W_OP_FP4_MATMUL && op != FP4W_OP_FP8_MATMUL && op != FP4W_OP_FP4_DEQUANT &&
+      op != FP4W_OP_FP8_DEQUANT)
     return FP4W_ERR_PATH;
-  int st = check_shape(op, op == FP4W_OP_FP4_DEQUANT ? 0 : M, N, K, block_size, scale_cols);
+  const bool dq = op == FP4W_OP_FP4_DEQUANT || op == FP4W_OP_FP8_DEQUANT;
+  int st = check_shape(op, dq ? 0 : M, N, K, block_size, scale_cols);
   if (st != FP4W_OK) return st;
   return shape_path(op, M, N, K, block_size);
 }
@@ -365,6 +403,8 @@ const char* fp4w_path_name(int path) {
     case FP4W_PATH_QDQ_GENERIC: return "qdq_generic";
     case FP4W_PATH_FP4_SKINNY: return "fp4_skinny";
     case FP4W_PATH_FP8_SKINNY: return "fp8_skinny";
+    case FP4W_PATH_FP8_DEQUANT_VEC: return "fp8_dequant_vec";
+    case FP4W_PATH_FP8_DEQUANT_GENERIC: return "fp8_dequant_generic";
     default: return "unknown";
   }
 }

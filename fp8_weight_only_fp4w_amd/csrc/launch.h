@@ -32,6 +32,15 @@ struct DequantArgs {
   void* stream;
 };
 
+struct Fp8DequantArgs {
+  const uint8_t* B;
+  const float* scales;
+  void* out;
+  int64_t N, K, block_size, scale_cols;
+  Act act;
+  void* stream;
+};
+
 // Activation quantize/dequantize (W8A8 mode): `count` elements of T.
 struct QdqArgs {
   const void* A;
@@ -74,6 +83,12 @@ int launch_fp8_generic(const MatmulArgs& a);
 int launch_dequant_vec(const DequantArgs& a);
 // any validated arguments with N, K > 0
 int launch_dequant_generic(const DequantArgs& a);
+
+// FP8 dequant: K % 16 == 0, block_size % 16 == 0, B / out 16-byte aligned,
+// N * K / 16 < 2^32.
+int launch_fp8_dequant_vec(const Fp8DequantArgs& a);
+// any validated arguments with N, K > 0
+int launch_fp8_dequant_generic(const Fp8DequantArgs& a);
 
 // count % 8 == 0, A and out 16-byte aligned; out == A allowed.
 int launch_qdq_vec(const QdqArgs& a);

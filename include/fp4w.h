@@ -70,7 +70,9 @@ typedef enum {
   FP4W_PATH_QDQ_VEC = 10,        /* vectorised activation QDQ: M*K % 8 == 0 */
   FP4W_PATH_QDQ_GENERIC = 11,    /* any legal QDQ arguments */
   FP4W_PATH_FP4_SKINNY = 12,     /* MFMA skinny matmul: 1 <= M <= 64, block_size 16, K % 128 == 0 */
-  FP4W_PATH_FP8_SKINNY = 13      /* MFMA skinny matmul: 1 <= M <= 64, block_size % 128 == 0, K % 128 == 0 */
+  FP4W_PATH_FP8_SKINNY = 13,     /* MFMA skinny matmul: 1 <= M <= 64, block_size % 128 == 0, K % 128 == 0 */
+  FP4W_PATH_FP8_DEQUANT_VEC = 14,    /* vectorised FP8 dequant: K % 16 == 0, block_size % 16 == 0 */
+  FP4W_PATH_FP8_DEQUANT_GENERIC = 15 /* any legal FP8 dequant arguments */
 } fp4w_path;
 
 /* Operation selector for fp4w_select_path. */
@@ -78,7 +80,8 @@ typedef enum {
   FP4W_OP_FP4_MATMUL = 0,
   FP4W_OP_FP8_MATMUL = 1,
   FP4W_OP_FP4_DEQUANT = 2,
-  FP4W_OP_FP8_QDQ = 3 /* fp8w_qdq_activation: only M and K are used */
+  FP4W_OP_FP8_QDQ = 3, /* fp8w_qdq_activation: only M and K are used */
+  FP4W_OP_FP8_DEQUANT = 4 /* fp8w_dequant: M is ignored */
 } fp4w_op;
 
 /*
@@ -146,6 +149,24 @@ int fp4w_dequant(const uint8_t* B, int64_t N, int64_t K, const uint8_t* weight_s
 int fp4w_dequant_ex(const uint8_t* B, int64_t N, int64_t K, const uint8_t* weight_scale,
                     int64_t scale_cols, int64_t block_size, const float* weight_scale_2, void* out,
                     int dtype, void* stream, int path);
+
+/*
+ * fp8w_dequant - expand FP8 weights to T[N, K], the first step of the FP8
+ * operator's default path ([FP8 doc] §5 Default Path, step 1).
+ *   out[n, k] = RNE_T(RNE_f32(e4m3(B[n, k]) * b_scale[n, min(k / block_size, scale_cols - 1)]))
+ * The E4M3 value is exact in FP32; the product with the FP32 block scale
+ * rounds once, then the FP32 value is rounded to T.  Bit-exact; no FTZ.
+ *
+ *   B, b_scale, scale_cols, block_size: as fp8w_matmul.   out: T[N, K] (written).
+ * N == 0 or K == 0: FP4W_OK, nothing launched.  Errors: FP4W_ERR_NULL,
+ * FP4W_ERR_SHAPE, FP4W_ERR_BLOCK, FP4W_ERR_DTYPE, FP4W_ERR_ALIAS, FP4W_ERR_LAUNCH.
+ */
+int fp8w_dequant(const uint8_t* B, int64_t N, int64_t K, const float* b_scale, int64_t scale_cols,
+                 int64_t block_size, void* out, int dtype, void* stream);
+
+/* Path-forcing variant (FP4W_PATH_AUTO, _FP8_DEQUANT_VEC, _FP8_DEQUANT_GENERIC). */
+int fp8w_dequant_ex(const uint8_t* B, int64_t N, int64_t K, const float* b_scale, int64_t scale_cols,
+                    int64_t block_size, void* out, int dtype, void* stream, int path);
 
 /*
  * fp8w_qdq_activation - the activation step of the FP8 operator's optional

@@ -219,3 +219,24 @@ def test_w8a8_validation_before_any_launch():
     assert m(A, 4, 256, B, 16, S, 2, 128, AS, None, vp(0x200000 + 64), Y, fw.BF16, None) == fw.ERR_ALIAS
     assert m(A, 4, 256, B, 16, S, 2, 128, AS, None, W, Y, 9, None) == fw.ERR_DTYPE
     assert m(None, 0, 256, None, 16, None, 2, 128, None, None, None, None, fw.BF16, None) == fw.OK
+
+
+def test_dispatch_and_validation_fp8_dequant():
+    F = fw.OP_FP8_DEQUANT
+    assert sel(F, 0, 17408, 5120, 128) == fw.PATH_FP8_DEQUANT_VEC
+    assert sel(F, 0, 64, 208, 16) == fw.PATH_FP8_DEQUANT_VEC
+    assert sel(F, 0, 64, 37, 16) == fw.PATH_FP8_DEQUANT_GENERIC      # K % 16 != 0 (odd K is legal)
+    assert sel(F, 0, 64, 256, 24) == fw.PATH_FP8_DEQUANT_GENERIC     # block_size % 16 != 0
+    assert sel(F, 0, 0, 256, 128) == fw.PATH_NONE
+    lib = fw.load_library()
+    vp = ctypes.c_void_p
+    B, S, O = vp(0x100000), vp(0x300000), vp(0x500000)
+    d = lib.fp8w_dequant_ex
+    assert d(B, 16, 256, S, 3, 128, O, fw.BF16, None, 0) == fw.ERR_SHAPE
+    assert d(B, 16, 256, S, 2, 0, O, fw.BF16, None, 0) == fw.ERR_BLOCK
+    assert d(B, 16, 256, None, 2, 128, O, fw.BF16, None, 0) == fw.ERR_NULL
+    assert d(B, 16, 256, S, 2, 128, vp(0x100000 + 64), fw.BF16, None, 0) == fw.ERR_ALIAS
+    assert d(B, 16, 256, S, 2, 128, O, 5, None, 0) == fw.ERR_DTYPE
+    assert d(B, 16, 37, S, 3, 16, O, fw.BF16, None, fw.PATH_FP8_DEQUANT_VEC) == fw.ERR_PATH
+    assert d(B, 16, 256, S, 2, 128, O, fw.BF16, None, fw.PATH_DEQUANT_VEC) == fw.ERR_PATH
+    assert d(None, 0, 256, None, 2, 128, None, fw.BF16, None, 0) == fw.OK

@@ -109,3 +109,59 @@ def test_dequant_empty_is_noop():
                     torch.zeros((0, 2), dtype=torch.uint8, device="cuda"),
                     torch.ones(1, device="cuda"), 16, out=out)
     torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------- FP8 ([FP8 doc] §5, step 1)
+
+def _fp8_dequant(B, bsc, bs, dtype, path=fw.PATH_AUTO):
+    out = fw.fp8w_dequant(u8(B), torch.from_numpy(np.ascontiguousarray(bsc, dtype=np.float32)).to("cuda"),
+                          bs, TORCH_DT[dtype], path=path)
+    torch.cuda.synchronize()
+    return dev_to_bits(out)
+
+
+FP8_SCALES = np.array([1.0, 2.0 ** -9, 1e-3, 7.3e-3, 3.0, 300.0, 2.0 ** -140, 6.5e4], dtype=np.float32)
+
+
+@pytest.mark.parametrize("path", [fw.PATH_FP8_DEQUANT_VEC, fw.PATH_FP8_DEQUANT_GENERIC])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_fp8_dequant_every_code_and_scale(dtype, path):
+    """All 256 E4M3 codes (NaN included) x a spread of FP32 scales (fp16
+    overflow and subnormals, FP32 subnormal products), bit for bit."""
+    require_gpu()
+    B = np.tile(np.arange(256, dtype=np.uint8), (len(FP8_SCALES), 1))   # K = 256, one block
+    bsc = FP8_SCALES[:, None]
+    want = ref.dequant_fp8_output_bits(B, bsc, 256, dtype)
+    assert_dequant_equal(_fp8_dequant(B, bsc, 256, dtype, path), want, dtype, f"fp8 dequant path {path}")
+
+
+FP8_SHAPES = [
+    # N, K, block_size, partial
+    (64, 512, 128, "ceil"), (33, 640, 256, "floor"), (7, 208, 16, "ceil"),
+    (5, 37, 16, "ceil"), (9, 300, 7, "floor"), (128, 5120, 128, "ceil"),
+]
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("N,K,bs,partial", FP8_SHAPES)
+def test_fp8_dequant_shape_matrix(N, K, bs, partial, dtype):
+    """Vectorised and generic kernels over K % 16 != 0, odd block sizes and
+    partial final blocks with floor or ceil scale columns."""
+    require_gpu()
+    p = workloads.make_fp8(1, N, K, bs, dtype, seed=N + K + bs, partial=partial)
+    want = ref.dequant_fp8_output_bits(p.B, p.b_scale, bs, dtype)
+    auto = _fp8_dequant(p.B, p.b_scale, bs, dtype)
+    assert_dequant_equal(auto, want, dtype, f"fp8 dequant N{N} K{K} bs{bs}")
+    assert_dequant_equal(_fp8_dequant(p.B, p.b_scale, bs, dtype, fw.PATH_FP8_DEQUANT_GENERIC), want, dtype,
+                         "fp8 dequant generic")
+    vec = K % 16 == 0 and bs % 16 == 0
+    assert fw.fp4w_select_path(fw.OP_FP8_DEQUANT, 0, N, K, bs, p.b_scale.shape[1]) == (
+        fw.PATH_FP8_DEQUANT_VEC if vec else fw.PATH_FP8_DEQUANT_GENERIC)
+
+
+def test_fp8_dequant_prefill_weight_shape():
+    """The FP8 workload's weight [17408, 5120], block 128, every element."""
+    require_gpu()
+    p = workloads.WORKLOADS["fp8_gemv"].make(M=4)
+    want = ref.dequant_fp8_output_bits(p.B, p.b_scale, p.block_size, p.dtype)
+    assert_dequant_equal(_fp8_dequant(p.B, p.b_scale, p.block_size, p.dtype), want, p.dtype, "fp8 prefill weight")
