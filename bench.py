@@ -393,6 +393,55 @@ def extra_w8a8(steps, warmup):
     return res
 
 
+def decode_step_setup():
+    """Device inputs of the decode-step sequence: one weight set per launch,
+    one activation per K, one output per shape (FP16, M = 4, no bias)."""
+    M = workloads.DECODE_STEP_M
+    shapes = workloads.DECODE_STEP_SHAPES
+    ws2 = torch.tensor([2.0 ** -8], dtype=torch.float32, device="cuda")
+    W = [workloads.fp4_weights_on_device(N, K, 16, seed=7000 + i) for i, (N, K) in enumerate(shapes)]
+    A = {}
+    for K in sorted({K for _, K in shapes}):
+        A[K] = dev_bits(workloads.activations(np.random.default_rng(K), M, K, "fp16", "uniform"), "fp16")
+    out = {s: torch.empty(M, s[0], dtype=torch.float16, device="cuda") for s in set(shapes)}
+
+    def step():
+        for (N, K), (B, ws) in zip(shapes, W):
+            fw.fp4w_matmul(A[K], B, ws, ws2, None, 16, out=out[(N, K)])
+
+    return dict(M=M, shapes=shapes, W=W, A=A, out=out, ws2=ws2, step=step)
+
+
+def extra_decode_step(steps, warmup):
+    """A decode step as 121 back-to-back FP4 GEMV launches (M = 4, FP16): the
+    step replayed from one HIP graph, the same launches issued one by one from
+    Python, and the sum of the launches timed in isolation (graphs of one
+    shape), whose difference to the graph step is the cost of the sequence."""
+    st = decode_step_setup()
+    shapes, W = st["shapes"], st["W"]
+    wbytes = sum(B.numel() + ws.numel() for B, ws in W)
+    g = capture(st["step"])
+    n = max(4, min(steps, 40))
+    _, tg = time_graphs([g], n, max(2, min(warmup, 5)))
+    tg /= n
+    te = time_calls([st["step"]], max(2, n // 4), 2) / max(2, n // 4)
+    del g
+    iso = 0.0
+    per_shape = {}
+    for shp in sorted(set(shapes)):
+        idx = [i for i, s in enumerate(shapes) if s == shp]
+        N, K = shp
+        t = time_rotating(lambda r: fw.fp4w_matmul(st["A"][K], W[idx[r]][0], W[idx[r]][1], st["ws2"], None, 16,
+                                                   out=st["out"][shp]), len(idx), 4 * len(idx))
+        per_shape[f"N{N}_K{K}"] = {"launches": len(idx), "us": round(t * 1e6, 2)}
+        iso += t * len(idx)
+    return {"launches": len(shapes), "M": st["M"], "weight_MB_per_step": round(wbytes / 1e6, 1),
+            "graph_ms": round(tg * 1e3, 4), "eager_ms": round(te * 1e3, 4),
+            "isolated_sum_ms": round(iso * 1e3, 4),
+            "weight_GBps_graph": round(wbytes / tg / 1e9, 1),
+            "gap_us_per_launch": round((tg - iso) / len(shapes) * 1e6, 3), "per_shape": per_shape}
+
+
 # ------------------------------------------------------------------ profiling mode
 
 def profile_kernel(which, launches=50):
@@ -437,6 +486,42 @@ def profile_kernel(which, launches=50):
         out = torch.empty(p.M, p.N, dtype=torch.bfloat16, device="cuda")
         for _ in range(min(launches, 10)):
             fw.fp4w_matmul(d["A"], d["B"][0], d["ws"][0], d["ws2"], None, 16, out=out)
+    elif which == "skinny":
+        # batched decode, M = 16, 32, 64 at N = 17408, K = 5120 (FP4 then FP8)
+        for M in (16, 32, 64):
+            p = workloads.make_fp4(M, 17408, 5120, 16, "bf16", seed=M)
+            R = copies_for(p.B.nbytes + p.weight_scale.nbytes)
+            d = fp4_on_device(p, copies=R)
+            out = torch.empty(M, p.N, dtype=torch.bfloat16, device="cuda")
+            for i in range(launches):
+                fw.fp4w_matmul(d["A"], d["B"][i % R], d["ws"][i % R], d["ws2"], None, 16, out=out)
+            del d
+            p8 = workloads.make_fp8(M, 17408, 5120, 128, "bf16", seed=M)
+            R8 = copies_for(p8.B.nbytes + p8.b_scale.nbytes)
+            d8 = fp8_on_device(p8, copies=R8)
+            for i in range(launches):
+                fw.fp8w_matmul(d8["A"], d8["B"][i % R8], d8["bs"][i % R8], None, 128, out=out)
+            del d8
+    elif which == "qdq":
+        A = torch.randn(8192, 5120, device="cuda").to(torch.bfloat16)
+        work = torch.empty_like(A)
+        sc = (A.float().abs().max() / 448.0).reshape(1)
+        for _ in range(launches):
+            fw.fp8w_qdq_activation(A, sc, out=work)
+    elif which == "fp8_dequant":
+        p = workloads.WORKLOADS["fp8_gemv"].make(M=1)
+        d = fp8_on_device(p)
+        out = torch.empty(p.N, p.K, dtype=torch.bfloat16, device="cuda")
+        for _ in range(launches):
+            fw.fp8w_dequant(d["B"][0], d["bs"][0], 128, out=out)
+    elif which == "decode_step":
+        # the decode-step sequence, replayed from its graph
+        st = decode_step_setup()
+        g = capture(st["step"])
+        for _ in range(max(1, launches // 5)):
+            g.replay()
+        torch.cuda.synchronize()
+        del g
     elif which == "dequant":
         p = workloads.WORKLOADS["fp4_prefill"].make(M=1)
         d = fp4_on_device(p)
@@ -456,7 +541,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--profile-kernel", choices=["fp4_gemv", "fp4_gemv_wide", "fp8_gemv", "fp4_gemm", "dequant", "copy"])
+    ap.add_argument("--extra", default="", help="comma-separated subset of the extra workloads to run")
+    ap.add_argument("--profile-kernel", choices=["fp4_gemv", "fp4_gemv_wide", "fp8_gemv", "fp4_gemm", "dequant", "copy",
+                                                          "decode_step", "skinny", "qdq", "fp8_dequant"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library runs on a single MI355X and has no "
@@ -496,7 +583,10 @@ def main():
                          ("fp8", lambda: extra_fp8(args.steps, args.warmup)),
                          ("fp8_w8a8", lambda: extra_w8a8(args.steps, args.warmup)),
                          ("skinny", lambda: extra_skinny(args.steps, args.warmup)),
+                         ("decode_step", lambda: extra_decode_step(args.steps, args.warmup)),
                          ("fp4_prefill", extra_prefill_fp4)):
+            if args.extra and name not in args.extra.split(","):
+                continue
             t0 = time.perf_counter()
             extra[name] = fn()
             torch.cuda.empty_cache()

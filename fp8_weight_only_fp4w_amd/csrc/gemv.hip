@@ -100,8 +100,9 @@ struct Pos {
 // Activations, two ways (ACT_LDS):
 //  * false: loaded from L2 with the weights, at the same pipeline depth;
 //  * true: copied once into LDS by the persistent workgroup (rows zero-padded
-//    to whole 128-k windows; for FP4 one all-zero row follows the M rows), so
-//    the loop issues weight loads only.
+//    to whole 128-k windows; for FP4 a 256-byte zero block follows the M rows
+//    and serves the lanes that carry no row), so the loop issues weight loads
+//    only.
 // Either way the load consumed next is always the oldest one in flight.
 // R: FP4 - row halves (1: M <= 4, 2: M <= 8); FP8 - result rows a lane
 // scales (1, 2 or 4).  D: windows in flight ahead of the multiply.
@@ -139,14 +140,16 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
   unsigned char* slice = smem + 1024 * wave;          // this wave's 1 KiB
   unsigned char* a_lds = smem + kWaves * 1024;
   const uint32_t lds_pitch = static_cast<uint32_t>(NW) * 256u + 16u;  // bytes per LDS row of A
+  const uint32_t zero_off = static_cast<uint32_t>(M) * lds_pitch;       // FP4: the zero block
   const uint32_t a_bytes = static_cast<uint32_t>(M) * static_cast<uint32_t>(K) * 2u;
   const rsrc_t a_rsrc = make_rsrc(A, a_bytes);
 
   // Per-lane activation offsets (bytes, window 0).  FP4: lane (li = 4m' + q,
   // g) carries row m = m' + 4h of half h when q == g, else zeros (the zero
-  // LDS row, or an out-of-range offset).  FP8: row li (rows >= M are never
-  // stored, so lanes li >= M may read any valid row).
+  // block in LDS, or an out-of-range offset).  FP8: row li (rows >= M are
+  // never stored, so lanes li >= M may read any valid row).
   uint32_t a_off[FP8 ? 1 : R];
+  bool a_valid[FP8 ? 1 : R];
   if constexpr (FP8) {
     a_off[0] = ACT_LDS ? static_cast<uint32_t>(li % M) * lds_pitch
                        : static_cast<uint32_t>(li) * static_cast<uint32_t>(K) * 2u;
@@ -155,8 +158,9 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
     for (int h = 0; h < R; ++h) {
       const int m = (li >> 2) + 4 * h;
       const bool valid = (li & 3) == g && m < M;
+      a_valid[h] = valid;
       if constexpr (ACT_LDS)
-        a_off[h] = static_cast<uint32_t>(valid ? m : M) * lds_pitch + 64u * g;
+        a_off[h] = static_cast<uint32_t>(valid ? m : 0) * lds_pitch + 64u * g;
       else
         a_off[h] = valid ? static_cast<uint32_t>(m) * static_cast<uint32_t>(K) * 2u + 64u * g : kOutOfRange;
     }
@@ -247,7 +251,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
     // load is consumed by a store and none stays in flight into the main loop.
     const uint32_t cpr = chunks_per_row.d;  // lds_pitch / 16
     const uint32_t nload = static_cast<uint32_t>(M) * cpr;
-    const uint32_t nall = FP8 ? nload : nload + cpr;
+    const uint32_t nall = FP8 ? nload : nload + 16u;  // FP4: the 256-byte zero block
     constexpr uint32_t kStep = 64u * kWaves;
     auto fill_load = [&](uint32_t q0, u32x4 (&v)[8]) {
 #pragma unroll
@@ -329,7 +333,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
 #pragma unroll
       for (int h = 0; h < R; ++h) {
         if constexpr (ACT_LDS) {
-          const unsigned char* q = a_lds + a_off[h] + 256u * w;
+          const unsigned char* q = a_lds + (a_valid[h] ? a_off[h] + 256u * w : zero_off);
 #pragma unroll
           for (int i = 0; i < 4; ++i) av[h][i] = *reinterpret_cast<const u32x4*>(q + 16u * i);
         } else {
@@ -427,8 +431,9 @@ constexpr int depth() {
 }
 
 size_t lds_bytes(bool act_lds, bool fp8, int M, int NW) {
-  const size_t rows = static_cast<size_t>(M) + (fp8 ? 0 : 1);  // FP4: plus the zero row
-  return kWaves * 1024 + (act_lds ? rows * (static_cast<size_t>(NW) * 256 + 16) : 0);
+  // FP4: the M rows plus the 256-byte zero block
+  return kWaves * 1024 +
+         (act_lds ? static_cast<size_t>(M) * (static_cast<size_t>(NW) * 256 + 16) + (fp8 ? 0 : 256) : 0);
 }
 
 int num_cus() {

@@ -22,6 +22,12 @@ A -> B -> scales -> bias):
   than the two NaN codes 0x7F and 0xFF.
 * FP8 b_scale: float32 U[1e-3, 1e-2].
 * bias "N(0, 0.1)": standard deviation 0.1, rounded to T.
+
+Large weight sets that are only timed (the decode-step sequence) are drawn on
+the device instead (``fp4_weights_on_device``): torch's seeded device
+generator, uniform bytes for B and float32 U[a, b) encoded to E4M3 for the
+scales.  Same distributions, different streams of numbers; nothing checks
+their products against the oracle.
 """
 
 from dataclasses import dataclass, field
@@ -189,3 +195,27 @@ WORKLOADS = {
     "fp4_gemv_wide": Workload("fp4_gemv_wide", "fp4", (4,), 152064, 5120, 16, "bf16", "normal",
                               (2.0 ** -6, 4.0), with_bias=False, index=4),
 }
+
+
+def fp4_weights_on_device(N: int, K: int, block_size: int = 16, seed: int = 0,
+                          scale_range=(2.0 ** -6, 4.0), device="cuda"):
+    """(B uint8 [N, K/2], E4M3 scale bytes uint8 [N, ceil(K/bs)]) drawn on the
+    device with a seeded torch generator (see the module docstring)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    B = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=device, generator=g)
+    cols = scale_cols_for(K, block_size)
+    x = torch.empty(N, cols, dtype=torch.float32, device=device).uniform_(*scale_range, generator=g)
+    return B, x.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+# A decode step as a sequence of back-to-back FP4 GEMV launches: 121 launches
+# at M = 4 with FP16 activations, the launch count and batch of the pages'
+# per-step figure ("MatMulBlockQuantizedFp4Weight - CUDA Operator
+# Documentation", §4, tensor-core sub-path).  The pages do not give the
+# shapes of those launches.  Taken here: 40 repetitions of three projections
+# over the widths of the workloads above (5120 -> 5120, 5120 -> 17408,
+# 17408 -> 5120), then one more 5120 -> 5120, each launch with weights of its
+# own (about 4.6 GB per step, far beyond the last-level cache).
+DECODE_STEP_M = 4
+DECODE_STEP_SHAPES = tuple([(5120, 5120), (17408, 5120), (5120, 17408)] * 40 + [(5120, 5120)])  # (N, K)
