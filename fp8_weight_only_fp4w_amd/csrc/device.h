@@ -261,6 +261,21 @@ __device__ __forceinline__ uint32_t buf_load_u16(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, vgpr(off), 0, 0);
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Direct buffer -> LDS load of SIZE bytes per lane: lane l writes lds +
+// SIZE l (lds must be wave-uniform); offsets past the descriptor's range
+// write zeros.  The compiler does not track the LDS write: the caller waits
+// for it (vmcnt) before reading the data.
+template <int SIZE>
+__device__ __forceinline__ void buf_load_lds(rsrc_t r, uint32_t voff, void* lds) {
+  static_assert(SIZE == 16 || SIZE == 4, "direct load size");
+  if constexpr (SIZE == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(lds), 16, vgpr(voff), 0, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(lds), 4, vgpr(voff), 0, 0, 0);
+}
+
 // 16-byte global load of 8 T values, reinterpreted as the MFMA operand type.
 template <typename V>
 __device__ __forceinline__ V load16(const void* p) {

@@ -273,22 +273,9 @@ struct LargeLds {
   uint8_t s[2][L_BN * 32];             // 2 x 8 KiB
 };
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 // direct 16-byte global -> LDS load: lane l writes lds + 16 l
 __device__ __forceinline__ void load_lds16(const void* gptr, void* lds) {
   __builtin_amdgcn_global_load_lds(gptr, (lds_ptr_t)(lds), 16, 0, 0);
-}
-
-// direct buffer -> LDS load of SIZE bytes per lane (lane l writes lds + SIZE l);
-// offsets past the descriptor's range read zeros
-template <int SIZE>
-__device__ __forceinline__ void buf_load_lds(rsrc_t r, uint32_t voff, void* lds) {
-  static_assert(SIZE == 16 || SIZE == 4, "direct load size");
-  if constexpr (SIZE == 16)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(lds), 16, vgpr(voff), 0, 0, 0);
-  else
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(lds), 4, vgpr(voff), 0, 0, 0);
 }
 
 // wait until at most N vector-memory loads are in flight and every LDS access

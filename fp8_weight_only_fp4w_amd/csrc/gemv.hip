@@ -56,41 +56,95 @@ namespace {
 
 constexpr int kWaves = 8;  // waves per workgroup (KS x TPW)
 
-// Raw data of one window for one lane.  FP4: 16 weight bytes; FP8: 32.  The
-// block scales of a tile are read in 64-byte pieces per column (one request
-// per row instead of one per row and window): the piece rides along with the
-// first window of each group of kScaleWin windows and is parked in a per-wave
-// LDS slice, from which every window of the group reads its scales.  The bias
-// bits of the lane's column ride along with the first window of a tile.
-// Activations ride along only when they come from L2 (ACT_REG).
+// Weights travel global -> LDS by direct loads (no registers).  A unit (FP4:
+// two 128-k windows, FP8: one) is 128 contiguous bytes of each of the wave's
+// 16 rows, fetched by two instructions of 8 rows x 128 bytes.  HBM streams at
+// full rate only when an instruction requests whole 128-byte lines; 16 rows
+// x 64 bytes per instruction (half lines) reaches about two thirds of it.
+// Each row's eight 16-byte chunks are loaded by 8 adjacent lanes in the order
+// chunk ^ (row & 7), so the LDS copy comes out XOR-swizzled and the fragment
+// reads (lane (li, g): one chunk of row li) are free of bank conflicts.  A
+// wave has a private ring of D + 1 unit slots of 2 KiB and waits for its own
+// loads only, with no barrier.
+constexpr uint32_t kUnitBytes = 2048;  // one unit slot: 16 rows x 128 bytes
+constexpr int kSlicePitch = 144;       // FP4 scale slice: bytes per row (128 + 16 against bank conflicts)
+
+template <bool FP8>
+constexpr uint32_t slice_bytes() {
+  return FP8 ? 1024u : 16u * kSlicePitch;
+}
+
+// Units per scale piece.  FP4: 8 E4M3 bytes per window, 128 bytes per row =
+// 16 windows = 8 units, loaded like the weights (8 rows x 128 bytes per
+// instruction).  FP8: one FP32 scale per 128-k window (or per several:
+// block_size % 128 == 0), 16 scales of a row = 64 bytes per piece.
+template <bool FP8>
+constexpr int kScaleUnits = FP8 ? 16 : 8;
+
+// Activations streamed from L2 (ACT_REG): each unit brings the activation
+// bytes of its K range, row-major (rows of 512 bytes for FP4's two windows,
+// 256 bytes for FP8's one), so that every load instruction requests whole
+// lines: FP4 2R instructions of 2 rows, FP8 two of 4 rows.  The multiply
+// stores them in a wave-private LDS staging area and reads them back in the
+// MFMA layout.
+template <bool FP8, int R>
+constexpr int kActLoads = FP8 ? 2 : 2 * R;
+constexpr uint32_t kStagePitch4 = 528;  // FP4: bytes per staged row (512 + 16)
+constexpr uint32_t kStagePitch8 = 272;  // FP8: bytes per staged row (256 + 16)
+
+// Staging bytes per wave: FP4 4R rows and a 64-byte zero block for the lanes
+// that carry no row; FP8 8 rows.
+template <bool FP8, int R>
+constexpr uint32_t stage_bytes() {
+  return FP8 ? 8u * kStagePitch8 : 4u * R * kStagePitch4 + 64u;
+}
+
+// Register part of one unit for one lane: the scale piece (first unit of
+// each piece), the bias bits of the lane's column (first unit of a tile) and,
+// when they come from L2 (ACT_REG), the activations.
 template <bool FP8, bool ACT_REG, int R>
 struct Raw;
 template <bool ACT_REG, int R>
 struct Raw<false, ACT_REG, R> {
-  u32x4 w;
-  u32x4 sc;
+  u32x4 sc[2];  // rows lr and 8 + lr, 16 bytes each
   uint32_t bias;
-  u32x4 a[ACT_REG ? 4 * R : 1];  // 64 activation bytes per row half
+  u32x4 a[ACT_REG ? kActLoads<false, R> : 1];
 };
 template <bool ACT_REG, int R>
 struct Raw<true, ACT_REG, R> {
-  u32x4 w0, w1;
   u32x4 sc;
   uint32_t bias;
-  u32x4 a[ACT_REG ? 4 : 1];  // 4 x 8 activations
+  u32x4 a[ACT_REG ? kActLoads<true, R> : 1];
 };
 
-// Windows per 64-byte scale piece: FP4 has 8 E4M3 bytes per window, FP8 one
-// FP32 scale per 128-k window (or per several windows: block_size % 128 == 0,
-// and 16 consecutive columns always cover 16 consecutive windows).
-template <bool FP8>
-constexpr int kScaleWin = FP8 ? 16 : 8;
+// Loads every unit issues, whatever else it carries: the two direct weight
+// loads (issued last) and the activations from L2.
+template <bool FP8, bool ACT_REG, int R>
+constexpr int kLoadsPerUnit = 2 + (ACT_REG ? kActLoads<FP8, R> : 0);
 
-// Position of a wave in its flat window sequence: tile group and window.
+// Wait until at most N vector-memory loads of this wave are in flight.  The
+// compiler does not track the LDS side of direct loads, so the fences keep
+// the LDS reads that follow after the wait.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));  // vmcnt(N) only
+  __asm__ volatile("" ::: "memory");
+}
+
+// Workgroup barrier for data exchanged through LDS by ds_write / ds_read
+// only.  __syncthreads would also wait for every direct load in flight (the
+// compiler cannot tell which LDS bytes they write), draining the pipeline.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Position of a wave in its flat unit sequence: tile group and unit.
 struct Pos {
   int tg, j;
-  __device__ __forceinline__ void advance(int nws, int stride) {
-    if (++j == nws) {
+  __device__ __forceinline__ void advance(int nus, int stride) {
+    if (++j == nus) {
       j = 0;
       tg += stride;
     }
@@ -98,47 +152,53 @@ struct Pos {
 };
 
 // Activations, two ways (ACT_LDS):
-//  * false: loaded from L2 with the weights, at the same pipeline depth;
+//  * false: loaded from L2 with each unit, at the same pipeline depth;
 //  * true: copied once into LDS by the persistent workgroup (rows zero-padded
 //    to whole 128-k windows; for FP4 a 256-byte zero block follows the M rows
 //    and serves the lanes that carry no row), so the loop issues weight loads
 //    only.
-// Either way the load consumed next is always the oldest one in flight.
 // R: FP4 - row halves (1: M <= 4, 2: M <= 8); FP8 - result rows a lane
-// scales (1, 2 or 4).  D: windows in flight ahead of the multiply.
+// scales (1, 2 or 4).  D: units in flight ahead of the multiply.
 //
-// LDS: [kWaves][1 KiB] per-wave slices (scale pieces, and the K-split
-// reduction at the end of a tile), then the activation rows.
+// LDS: [kWaves][D + 1] unit slots, [kWaves] scale slices (a wave's slice also
+// takes its part of the K-split reduction at the end of a tile), then the
+// activation rows (ACT_LDS) or [kWaves] activation staging areas (ACT_REG).
 template <typename T, int KS, bool FP8, bool ACT_LDS, int R, int D>
 __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
     const T* __restrict__ A, const uint8_t* __restrict__ B, const void* __restrict__ scales,
     const float* __restrict__ ws2p, const T* __restrict__ bias, T* __restrict__ Y, int M, int N,
-    int K, int cols, FastDiv win_per_block, FastDiv chunks_per_row, int num_tiles, int nws) {
+    int K, int cols, FastDiv win_per_block, FastDiv chunks_per_row, int num_tiles, int nus) {
   constexpr bool ACT_REG = !ACT_LDS;
   constexpr int TPW = kWaves / KS;
-  constexpr int S = D + 1;  // register slots of the pipeline
-  constexpr int SW = kScaleWin<FP8>;
+  constexpr int S = D + 1;          // unit slots (LDS ring and registers)
+  constexpr int UW = FP8 ? 1 : 2;   // windows per unit
+  constexpr int SU = kScaleUnits<FP8>;
+  constexpr int LPU = kLoadsPerUnit<FP8, ACT_REG, R>;
+  constexpr uint32_t kSlice = slice_bytes<FP8>();
   typedef Raw<FP8, ACT_REG, R> RawT;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int li = lane & 15, g = lane >> 4;
+  const int li = lane & 15, g = lane >> 4;    // fragment side: row li, chunk group g
+  const int lr = lane >> 3, lc = lane & 7;    // load side: row lr of an 8-row half, position lc
   const int ks = wave % KS, tw = wave / KS;
-  const int NW = K >> 7;  // 128-k windows (K % 128 == 0)
+  const int NW = K >> 7;                      // 128-k windows (K % 128 == 0)
+  const int NU = (NW + UW - 1) / UW;          // units per row
   const int ntg = (num_tiles + TPW - 1) / TPW;
   const int iters = (ntg - static_cast<int>(blockIdx.x) + static_cast<int>(gridDim.x) - 1) /
                     static_cast<int>(gridDim.x);
   // every wave of the workgroup runs the same sequence, so the barriers of
   // the K-split reduction are uniform
-  const int total = iters * nws;
+  const int total = iters * nus;
   const int stride = gridDim.x;
   const uint32_t row_bytes = FP8 ? static_cast<uint32_t>(K) : static_cast<uint32_t>(K >> 1);
   const uint32_t srow_bytes = FP8 ? static_cast<uint32_t>(cols) * 4u : static_cast<uint32_t>(cols);
   const float ws2 = FP8 ? 1.0f : *ws2p;  // one scalar load, kept in a register
 
-  f32x4* red = reinterpret_cast<f32x4*>(smem);       // [kWaves][64]
-  unsigned char* slice = smem + 1024 * wave;          // this wave's 1 KiB
-  unsigned char* a_lds = smem + kWaves * 1024;
+  unsigned char* ring = smem + static_cast<uint32_t>(wave) * (S * kUnitBytes);
+  unsigned char* slices = smem + kWaves * S * kUnitBytes;
+  unsigned char* slice = slices + wave * kSlice;
+  unsigned char* a_lds = slices + kWaves * kSlice;
   const uint32_t lds_pitch = static_cast<uint32_t>(NW) * 256u + 16u;  // bytes per LDS row of A
   const uint32_t zero_off = static_cast<uint32_t>(M) * lds_pitch;       // FP4: the zero block
   const uint32_t a_bytes = static_cast<uint32_t>(M) * static_cast<uint32_t>(K) * 2u;
@@ -148,36 +208,43 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
   // g) carries row m = m' + 4h of half h when q == g, else zeros (the zero
   // block in LDS, or an out-of-range offset).  FP8: row li (rows >= M are
   // never stored, so lanes li >= M may read any valid row).
+  // In the staging area (ACT_REG) the same holds with the staged row pitch.
   uint32_t a_off[FP8 ? 1 : R];
   bool a_valid[FP8 ? 1 : R];
   if constexpr (FP8) {
-    a_off[0] = ACT_LDS ? static_cast<uint32_t>(li % M) * lds_pitch
-                       : static_cast<uint32_t>(li) * static_cast<uint32_t>(K) * 2u;
+    a_off[0] = static_cast<uint32_t>(li % M) * (ACT_LDS ? lds_pitch : kStagePitch8);
+    a_valid[0] = true;
   } else {
 #pragma unroll
     for (int h = 0; h < R; ++h) {
       const int m = (li >> 2) + 4 * h;
       const bool valid = (li & 3) == g && m < M;
       a_valid[h] = valid;
-      if constexpr (ACT_LDS)
-        a_off[h] = static_cast<uint32_t>(valid ? m : 0) * lds_pitch + 64u * g;
-      else
-        a_off[h] = valid ? static_cast<uint32_t>(m) * static_cast<uint32_t>(K) * 2u + 64u * g : kOutOfRange;
+      a_off[h] = static_cast<uint32_t>(valid ? m : 0) * (ACT_LDS ? lds_pitch : kStagePitch4) + 64u * g;
     }
   }
+  // ACT_REG: this wave's staging area, the lane's global offset (unit 0) in
+  // the row-major loads and its place in the staging area.  FP4 load b:
+  // rows 2b + (lane >> 5), 16 bytes at 16 (lane & 31) of the row's 512;
+  // FP8 load b: rows 4b + (lane >> 4), 16 bytes at 16 (lane & 15) of 256.
+  unsigned char* stage = a_lds + wave * stage_bytes<FP8, R>();
+  constexpr int kRowsPerLoad = FP8 ? 4 : 2;
+  const int st_row = FP8 ? (lane >> 4) : (lane >> 5);
+  const uint32_t st_pos = 16u * static_cast<uint32_t>(FP8 ? (lane & 15) : (lane & 31));
+  const uint32_t st_pitch = FP8 ? kStagePitch8 : kStagePitch4;
+  const uint32_t unit_act = FP8 ? 256u : 512u;  // activation bytes of a row per unit
   // scale column of window w (FP8; windows past NW are clamped)
   auto scol = [&](int w) {
     return min(fdiv(static_cast<uint32_t>(min(w, NW - 1)), win_per_block), static_cast<uint32_t>(cols - 1));
   };
 
-  // Window mapping.  FP4: lane group g loads the 32 k of chunk c = 4w + g
-  // (bytes 64w + 16g of its column: one wave instruction reads 64 contiguous
-  // bytes of each of 16 rows).  FP8: lane group g loads k 128w + 16g .. + 15
-  // and 128w + 64 + 16g .. + 15 (two instructions, each 64 contiguous bytes
-  // per row).
+  // Window mapping.  Unit u covers bytes 128u .. 128u + 127 of every row.
+  // FP4: window 2u + s is bytes 64s .. 64s + 63 of the unit, and lane group g
+  // takes chunk 4s + g of it (32 k); FP8: lane group g takes chunks g and
+  // 4 + g (k 16g .. + 15 and 64 + 16g .. + 15 of the window).
   // Load side of the pipeline: position and the (wave-uniform) descriptors
   // of its tile, recomputed only when the position enters a new tile.
-  Pos lp{static_cast<int>(blockIdx.x), 0};  // next window to load
+  Pos lp{static_cast<int>(blockIdx.x), 0};  // next unit to load
   rsrc_t br, sr, biasr;
   auto set_load_tile = [&]() {
     const int t = lp.tg * TPW + tw;
@@ -188,49 +255,51 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
     biasr = make_rsrc(bias + n0, bias ? rows * 2u : 0u);
   };
   set_load_tile();
-  // per-lane byte offsets of the lane's column (window 0); the window's own
-  // offset is wave-uniform and rides in the scalar offset of the load.  Lanes
-  // past the tile's last row are out of range through their own offset.
-  const uint32_t w_lane = li * row_bytes + 16u * g;
+  // direct-load offsets of the lane (unit 0): row lr (+ 8), chunk lc ^ lr
+  // (lr == row & 7).  Rows past the tile's last row are out of range through
+  // the descriptor.
+  const uint32_t wl = lr * row_bytes + 16u * (lc ^ lr);
+  const uint32_t wl8 = wl + 8u * row_bytes;
+  // FP4 scale pieces: row lr (+ 8), bytes 16 lc of the 128-byte piece
+  const uint32_t sl = lr * srow_bytes + 16u * lc;
+  const uint32_t sl8 = sl + 8u * srow_bytes;
 
-  auto load = [&](RawT& r) {
-    // bias and scale pieces are only requested for the windows that carry
+  auto load = [&](RawT& r, unsigned char* slot) {
+    // bias and scale pieces are only requested for the units that carry
     // them (uniform branches; an out-of-range request would still occupy the
     // load pipeline for all 64 lanes)
     if (lp.j == 0) r.bias = buf_load_u16(biasr, 2u * li);
-    const int w = ks * nws + lp.j;
-    const bool ok = w < NW;
-    const bool piece = ok && lp.j % SW == 0;
+    const int u = ks * nus + lp.j;  // unit of the row
+    const bool ok = u < NU;
+    const bool piece = ok && lp.j % SU == 0;
     if constexpr (FP8) {
-      const uint32_t off = ok ? li * row_bytes + 128u * w + 16u * g : kOutOfRange;
-      r.w0 = buf_load_b128(br, off);
-      r.w1 = buf_load_b128(br, off + 64u);
+      const int w = u;
       // FP32 scales of columns scol(w) .. + 15 (bytes past the row are never used)
       if (piece) r.sc = buf_load_b128(sr, li * srow_bytes + 4u * scol(w) + 16u * g);
-      if constexpr (ACT_REG) {
-        const uint32_t aoff = ok ? a_off[0] + 256u * w + 32u * g : kOutOfRange;
-        r.a[0] = buf_load_b128(a_rsrc, aoff);
-        r.a[1] = buf_load_b128(a_rsrc, aoff + 16u);
-        r.a[2] = buf_load_b128(a_rsrc, aoff + 128u);
-        r.a[3] = buf_load_b128(a_rsrc, aoff + 144u);
-      }
     } else {
-      // windows past NW re-read window NW - 1 (inside the row) and are
-      // cancelled by zero scales when multiplied
-      r.w = buf_load_b128_so(br, w_lane, 64u * static_cast<uint32_t>(min(w, NW - 1)));
-      // E4M3 scales of windows w .. w + 7 (bytes past the row are never used)
-      if (piece) r.sc = buf_load_b128(sr, li * srow_bytes + 8u * w + 16u * g);
-      if constexpr (ACT_REG) {
-#pragma unroll
-        for (int h = 0; h < R; ++h) {
-          // out-of-range lanes stay out of range: a_off < 2^31 or >= 2^31
-          const uint32_t aoff = ok ? a_off[h] + 256u * w : kOutOfRange;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) r.a[4 * h + i] = buf_load_b128(a_rsrc, aoff + 16u * i);
-        }
+      // E4M3 scales of windows 2u .. 2u + 15 (bytes past the row are never used)
+      if (piece) {
+        r.sc[0] = buf_load_b128(sr, sl + 16u * u);
+        r.sc[1] = buf_load_b128(sr, sl8 + 16u * u);
       }
     }
-    if (++lp.j == nws) {
+    if constexpr (ACT_REG) {
+      // row-major activations of the unit's K range; bytes past the end of a
+      // row (a last unit with one window) or rows past M read zeros
+      const uint32_t kpos = unit_act * static_cast<uint32_t>(u) + st_pos;
+#pragma unroll
+      for (int b = 0; b < kActLoads<FP8, R>; ++b) {
+        const int m = kRowsPerLoad * b + st_row;
+        const bool in = m < M && kpos < static_cast<uint32_t>(K) * 2u;
+        r.a[b] = buf_load_b128(a_rsrc, in ? static_cast<uint32_t>(m) * static_cast<uint32_t>(K) * 2u + kpos
+                                          : kOutOfRange);
+      }
+    }
+    // the unit's weights, last: whatever else is in flight is older
+    const uint32_t ub = 128u * static_cast<uint32_t>(u);
+    buf_load_lds<16>(br, ok ? wl + ub : kOutOfRange, slot);
+    buf_load_lds<16>(br, ok ? wl8 + ub : kOutOfRange, slot + 1024);
+    if (++lp.j == nus) {
       lp.j = 0;
       lp.tg += stride;
       set_load_tile();
@@ -240,15 +309,16 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   uint32_t tbias = 0;  // bias bits of the lane's column, current tile
   RawT raw[S];
-  Pos cp{static_cast<int>(blockIdx.x), 0};  // window being multiplied
+  Pos cp{static_cast<int>(blockIdx.x), 0};  // unit being multiplied
 
   if constexpr (ACT_LDS) {
-    // Rows 0 .. M-1 of A, zero beyond K, then (FP4) the zero row.  The first
-    // eight 16-byte chunks per thread are requested before the weights, so
-    // their stores wait for them alone (loads complete in order); any further
-    // chunks (large M x K) follow the weight requests.  Chunk indices past the
-    // end are clamped to the last chunk (same data, same address), so every
-    // load is consumed by a store and none stays in flight into the main loop.
+    // Rows 0 .. M-1 of A, zero beyond K, then (FP4) the zero block.  The
+    // first eight 16-byte chunks per thread are requested before the weights,
+    // so their stores wait for them alone (loads complete in order); any
+    // further chunks (large M x K) follow the weight requests.  Chunk indices
+    // past the end are clamped to the last chunk (same data, same address),
+    // so every load is consumed by a store and none stays in flight into the
+    // main loop.
     const uint32_t cpr = chunks_per_row.d;  // lds_pitch / 16
     const uint32_t nload = static_cast<uint32_t>(M) * cpr;
     const uint32_t nall = FP8 ? nload : nload + 16u;  // FP4: the 256-byte zero block
@@ -272,7 +342,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
     fill_load(threadIdx.x, v);
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      load(raw[d]);
+      load(raw[d], ring + d * kUnitBytes);
     }
     fill_store(threadIdx.x, v);
     for (uint32_t q0 = threadIdx.x + 8u * kStep; q0 < nload; q0 += 8u * kStep) {
@@ -281,104 +351,123 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
     }
     for (uint32_t q = nload + threadIdx.x; q < nall; q += kStep)
       *reinterpret_cast<u32x4*>(a_lds + 16u * q) = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
+    lds_barrier();
   } else {
+    // FP4: the staging area's zero block (wave-private: no barrier)
+    if constexpr (!FP8)
+      if (lane < 4) *reinterpret_cast<u32x4*>(stage + 4u * R * kStagePitch4 + 16u * lane) = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      load(raw[d]);
+      load(raw[d], ring + d * kUnitBytes);
     }
   }
 
-  // multiply one window (and finish its tile group after the last window)
-  auto consume = [&](const RawT& r) {
+  // multiply one unit (and finish its tile group after the last unit)
+  auto consume = [&](const RawT& r, const unsigned char* slot) {
     const int j = cp.j;
-    const int w = min(ks * nws + j, NW - 1);  // windows past NW meet zero weights
-    if (j % SW == 0) *reinterpret_cast<u32x4*>(slice + 64 * li + 16 * g) = r.sc;
+    const int u = ks * nus + j;
     if (j == 0) tbias = r.bias;
+    typedef ActTraits<T> Tr;
+    typedef typename Tr::vec8 V;
+    const int sw = li & 7;  // swizzle of the lane's row in the slot
     if constexpr (FP8) {
-      typedef ActTraits<T> Tr;
-      typedef typename Tr::vec8 V;
+      if (j % SU == 0) *reinterpret_cast<u32x4*>(slice + 64 * li + 16 * g) = r.sc;
+      const int w = min(u, NW - 1);  // windows past NW meet zero weights
       // the scale of this window's column, from the piece of the first
       // window of its group (the column offset is at most 15)
-      const uint32_t c0 = scol(ks * nws + (j - j % SW));
+      const uint32_t c0 = scol(ks * nus + (j - j % SU));
       const float sc = *reinterpret_cast<const float*>(slice + 64 * li + 4 * (scol(w) - c0));
-      V a[4];
-      if constexpr (ACT_LDS) {
-        const unsigned char* q = a_lds + a_off[0] + 256u * w + 32u * g;
-        a[0] = *reinterpret_cast<const V*>(q);
-        a[1] = *reinterpret_cast<const V*>(q + 16u);
-        a[2] = *reinterpret_cast<const V*>(q + 128u);
-        a[3] = *reinterpret_cast<const V*>(q + 144u);
-      } else {
+      if constexpr (ACT_REG) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = __builtin_bit_cast(V, r.a[i]);
+        for (int b = 0; b < kActLoads<FP8, R>; ++b)
+          *reinterpret_cast<u32x4*>(stage + (kRowsPerLoad * b + st_row) * st_pitch + st_pos) = r.a[b];
       }
+      const unsigned char* q = (ACT_LDS ? a_lds + 256u * w : stage) + a_off[0] + 32u * g;
+      V a[4];
+      a[0] = *reinterpret_cast<const V*>(q);
+      a[1] = *reinterpret_cast<const V*>(q + 16u);
+      a[2] = *reinterpret_cast<const V*>(q + 128u);
+      a[3] = *reinterpret_cast<const V*>(q + 144u);
+      wait_vm<D * LPU>();  // this unit's weights have landed
+      const u32x4 w0 = *reinterpret_cast<const u32x4*>(slot + 128 * li + 16 * (g ^ sw));
+      const u32x4 w1 = *reinterpret_cast<const u32x4*>(slot + 128 * li + 16 * ((4 + g) ^ sw));
       f32x4 blk = f32x4{0.f, 0.f, 0.f, 0.f};
-      blk = Tr::mfma(a[0], Tr::decode8_fp8(r.w0.x, r.w0.y), blk);
-      blk = Tr::mfma(a[1], Tr::decode8_fp8(r.w0.z, r.w0.w), blk);
-      blk = Tr::mfma(a[2], Tr::decode8_fp8(r.w1.x, r.w1.y), blk);
-      blk = Tr::mfma(a[3], Tr::decode8_fp8(r.w1.z, r.w1.w), blk);
+      blk = Tr::mfma(a[0], Tr::decode8_fp8(w0.x, w0.y), blk);
+      blk = Tr::mfma(a[1], Tr::decode8_fp8(w0.z, w0.w), blk);
+      blk = Tr::mfma(a[2], Tr::decode8_fp8(w1.x, w1.y), blk);
+      blk = Tr::mfma(a[3], Tr::decode8_fp8(w1.z, w1.w), blk);
       // lane holds column n (one scale) and rows 4g .. 4g + 3
 #pragma unroll
       for (int i = 0; i < R; ++i) acc[i] = fmaf(blk[i], sc, acc[i]);
     } else {
-      typedef ActTraits<T> Tr;
-      typedef typename Tr::vec8 V;
-      // windows past NW (re-reads of window NW - 1) contribute nothing
-      const u32x2 sb = ks * nws + j < NW ? *reinterpret_cast<const u32x2*>(slice + 64 * li + 8 * (j % SW))
-                                          : u32x2{0u, 0u};
-      // activations of the lane: 4 x 16 bytes per row half; chunk i = 2s + p
-      // holds k 32g + 16s + 8p .. + 7 of the window (piece p of set s)
-      u32x4 av[R][4];
+      if (j % SU == 0) {
+        *reinterpret_cast<u32x4*>(slice + kSlicePitch * lr + 16 * lc) = r.sc[0];
+        *reinterpret_cast<u32x4*>(slice + kSlicePitch * (8 + lr) + 16 * lc) = r.sc[1];
+      }
+      if constexpr (ACT_REG) {
 #pragma unroll
-      for (int h = 0; h < R; ++h) {
-        if constexpr (ACT_LDS) {
-          const unsigned char* q = a_lds + (a_valid[h] ? a_off[h] + 256u * w : zero_off);
+        for (int b = 0; b < kActLoads<FP8, R>; ++b)
+          *reinterpret_cast<u32x4*>(stage + (kRowsPerLoad * b + st_row) * st_pitch + st_pos) = r.a[b];
+      }
+      wait_vm<D * LPU>();  // this unit's weights have landed
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int w = 2 * u + s2;
+        const int wa = min(w, NW - 1);  // windows past NW meet zero scales
+        const u32x2 sb = w < NW ? *reinterpret_cast<const u32x2*>(slice + kSlicePitch * li + 8 * (2 * (j % SU) + s2))
+                                : u32x2{0u, 0u};
+        // activations of the lane: 4 x 16 bytes per row half; chunk i = 2s + p
+        // holds k 32g + 16s + 8p .. + 7 of the window (piece p of set s)
+        u32x4 av[R][4];
+#pragma unroll
+        for (int h = 0; h < R; ++h) {
+          const unsigned char* q =
+              ACT_LDS ? a_lds + (a_valid[h] ? a_off[h] + 256u * wa : zero_off)
+                      : stage + (a_valid[h] ? a_off[h] + 256u * s2 : 4u * R * kStagePitch4);
 #pragma unroll
           for (int i = 0; i < 4; ++i) av[h][i] = *reinterpret_cast<const u32x4*>(q + 16u * i);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) av[h][i] = r.a[4 * h + i];
         }
+        // weights of the lane: chunk 4 s2 + g of row li (32 codes); dword
+        // 2s + p holds piece p of set s (block 2g + s)
+        const u32x4 wv = *reinterpret_cast<const u32x4*>(slot + 128 * li + 16 * ((4 * s2 + g) ^ sw));
+        V bw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bw[i] = Tr::decode8_fp4(wv[i]);
+        const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 d[R][2];
+#pragma unroll
+        for (int h = 0; h < R; ++h)
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            d[h][s] = Tr::mfma(__builtin_bit_cast(V, av[h][2 * s]), bw[2 * s], zero);
+            d[h][s] = Tr::mfma(__builtin_bit_cast(V, av[h][2 * s + 1]), bw[2 * s + 1], d[h][s]);
+          }
+        // result row r of set s is block 2r + s: scale byte 2r + s
+        const f32x2 s01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb.x), false);
+        const f32x2 s23 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb.x), true);
+        const f32x2 s45 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb.y), false);
+        const f32x2 s67 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb.y), true);
+        const float sc[8] = {s01.x, s01.y, s23.x, s23.y, s45.x, s45.y, s67.x, s67.y};
+#pragma unroll
+        for (int h = 0; h < R; ++h)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) acc[h] = fmaf(d[h][s][rr], sc[2 * rr + s], acc[h]);
       }
-      // weights of piece p of set s (block 2g + s): dword 2s + p (8 codes)
-      V bw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bw[i] = Tr::decode8_fp4(r.w[i]);
-      const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
-      f32x4 d[R][2];
-#pragma unroll
-      for (int h = 0; h < R; ++h)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          d[h][s] = Tr::mfma(__builtin_bit_cast(V, av[h][2 * s]), bw[2 * s], zero);
-          d[h][s] = Tr::mfma(__builtin_bit_cast(V, av[h][2 * s + 1]), bw[2 * s + 1], d[h][s]);
-        }
-      // result row r of set s is block 2r + s: scale byte 2r + s
-      const f32x2 s01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb.x), false);
-      const f32x2 s23 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb.x), true);
-      const f32x2 s45 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb.y), false);
-      const f32x2 s67 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb.y), true);
-      const float sc[8] = {s01.x, s01.y, s23.x, s23.y, s45.x, s45.y, s67.x, s67.y};
-#pragma unroll
-      for (int h = 0; h < R; ++h)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-          for (int s = 0; s < 2; ++s) acc[h] = fmaf(d[h][s][rr], sc[2 * rr + s], acc[h]);
     }
-    if (j == nws - 1) {
-      // end of this tile group: reduce the K split (the slices are free: every
-      // wave has read its scales for this window), then the epilogue (uniform
+    if (j == nus - 1) {
+      // end of this tile group: reduce the K split through the slices (every
+      // wave has read its scales for this unit), then the epilogue (uniform
       // across the workgroup: every wave has the same sequence)
       if (KS > 1) {
-        red[wave * 64 + lane] = acc;
-        __syncthreads();
+        *reinterpret_cast<f32x4*>(slice + 16 * lane) = acc;
+        lds_barrier();
         if (ks == 0) {
 #pragma unroll
-          for (int v = 1; v < KS; ++v) acc += red[(wave + v) * 64 + lane];
+          for (int v = 1; v < KS; ++v) acc += *reinterpret_cast<const f32x4*>(slices + (wave + v) * kSlice + 16 * lane);
         }
-        __syncthreads();
+        lds_barrier();
       }
       if (ks == 0) {
         const int n = 16 * (cp.tg * TPW + tw) + li;
@@ -402,18 +491,18 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
       }
       acc = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    cp.advance(nws, stride);
+    cp.advance(nus, stride);
   };
 
-  // Window f sits in slot f % S.  Loads run ahead unconditionally (past the
-  // end they are out of range), so every step waits only for its own, oldest,
+  // Unit f sits in slot f % S.  Loads run ahead unconditionally (past the end
+  // they are out of range), so every step waits only for its own, oldest,
   // loads; steps past the end of the sequence skip the multiply (the
   // condition is uniform across the workgroup).
   for (int f0 = 0; f0 < total; f0 += S) {
 #pragma unroll
     for (int u = 0; u < S; ++u) {
-      load(raw[(u + D) % S]);
-      if (f0 + u < total) consume(raw[u]);
+      load(raw[(u + D) % S], ring + ((u + D) % S) * kUnitBytes);
+      if (f0 + u < total) consume(raw[u], ring + u * kUnitBytes);
     }
   }
 }
@@ -422,18 +511,24 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
 
 constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 
-// Pipeline depth (windows in flight per wave), from measurement: FP4 with
-// activations in LDS gains up to 5; FP8 loads twice the bytes per window and
-// is best at 3.
-template <bool FP8, bool ACT_LDS>
+// Kernel variants by where the activations live and the pipeline depth
+// (units in flight per wave): MODE 0 - streamed from L2 with each unit, 4
+// units; 1 - in LDS, 2 units; 2 - in LDS, 4 units (the deepest ring that
+// leaves room for them).
+template <bool FP8, int MODE, int R>
 constexpr int depth() {
-  return ACT_LDS && !FP8 ? 5 : 3;
+  return MODE == 1 ? 2 : 4;
 }
 
-size_t lds_bytes(bool act_lds, bool fp8, int M, int NW) {
-  // FP4: the M rows plus the 256-byte zero block
-  return kWaves * 1024 +
-         (act_lds ? static_cast<size_t>(M) * (static_cast<size_t>(NW) * 256 + 16) + (fp8 ? 0 : 256) : 0);
+size_t lds_bytes(int mode, bool fp8, int M, int NW) {
+  const size_t ring = kWaves * (static_cast<size_t>(mode == 1 ? 2 : 4) + 1) * kUnitBytes;
+  const size_t slices = kWaves * static_cast<size_t>(fp8 ? slice_bytes<true>() : slice_bytes<false>());
+  // ACT_LDS: the M rows (FP4: plus the 256-byte zero block); ACT_REG: the
+  // staging areas
+  const size_t stage = fp8 ? stage_bytes<true, 1>() : M > 4 ? stage_bytes<false, 2>() : stage_bytes<false, 1>();
+  const size_t act = mode > 0 ? static_cast<size_t>(M) * (static_cast<size_t>(NW) * 256 + 16) + (fp8 ? 0 : 256)
+                              : kWaves * stage;
+  return ring + slices + act;
 }
 
 int num_cus() {
@@ -448,76 +543,96 @@ int num_cus() {
   return cus;
 }
 
-template <typename T, int KS, bool FP8, bool ACT_LDS, int R>
+template <typename T, int KS, bool FP8, int MODE, int R>
 constexpr auto kernel_ptr() {
-  return &gemv_kernel<T, KS, FP8, ACT_LDS, R, depth<FP8, ACT_LDS>()>;
+  return &gemv_kernel<T, KS, FP8, (MODE > 0), R, depth<FP8, MODE, R>()>;
 }
 
 // Dynamic LDS above 64 KiB must be allowed per kernel, once.
-template <typename T, int KS, bool FP8, bool ACT_LDS, int R>
+template <typename T, int KS, bool FP8, int MODE, int R>
 void allow_lds() {
   static bool done = false;
   if (!done) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel_ptr<T, KS, FP8, ACT_LDS, R>()),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel_ptr<T, KS, FP8, MODE, R>()),
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kMaxLds));
     done = true;
   }
 }
 
 // Resident workgroups per CU for a kernel variant and LDS size.
-template <typename T, int KS, bool FP8, bool ACT_LDS, int R>
+template <typename T, int KS, bool FP8, int MODE, int R>
 int wg_per_cu(size_t lds) {
-  allow_lds<T, KS, FP8, ACT_LDS, R>();
+  allow_lds<T, KS, FP8, MODE, R>();
   int v = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kernel_ptr<T, KS, FP8, ACT_LDS, R>(), 64 * kWaves,
-                                                   lds) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kernel_ptr<T, KS, FP8, MODE, R>(), 64 * kWaves, lds) !=
+          hipSuccess ||
       v < 1)
     v = 1;
   return v;
 }
 
-template <typename T, int KS, bool FP8, bool ACT_LDS>
+template <typename T, int KS, bool FP8, int MODE>
 int wg_per_cu_r(int R, size_t lds) {
-  if (R == 1) return wg_per_cu<T, KS, FP8, ACT_LDS, 1>(lds);
-  if (R == 2 || !FP8) return wg_per_cu<T, KS, FP8, ACT_LDS, 2>(lds);
-  return wg_per_cu<T, KS, FP8, ACT_LDS, (FP8 ? 4 : 2)>(lds);
+  if (R == 1) return wg_per_cu<T, KS, FP8, MODE, 1>(lds);
+  if (R == 2 || !FP8) return wg_per_cu<T, KS, FP8, MODE, 2>(lds);
+  return wg_per_cu<T, KS, FP8, MODE, (FP8 ? 4 : 2)>(lds);
 }
 
-template <typename T, bool FP8, bool ACT_LDS>
+template <typename T, bool FP8, int MODE>
 int slots_for(int KS, int R, int M, int NW) {
-  const size_t lds = lds_bytes(ACT_LDS, FP8, M, NW);
+  const size_t lds = lds_bytes(MODE, FP8, M, NW);
   int per = 1;
   switch (KS) {
-    case 1: per = wg_per_cu_r<T, 1, FP8, ACT_LDS>(R, lds); break;
-    case 2: per = wg_per_cu_r<T, 2, FP8, ACT_LDS>(R, lds); break;
-    case 4: per = wg_per_cu_r<T, 4, FP8, ACT_LDS>(R, lds); break;
-    default: per = wg_per_cu_r<T, 8, FP8, ACT_LDS>(R, lds); break;
+    case 1: per = wg_per_cu_r<T, 1, FP8, MODE>(R, lds); break;
+    case 2: per = wg_per_cu_r<T, 2, FP8, MODE>(R, lds); break;
+    case 4: per = wg_per_cu_r<T, 4, FP8, MODE>(R, lds); break;
+    default: per = wg_per_cu_r<T, 8, FP8, MODE>(R, lds); break;
   }
   return num_cus() * per;
 }
 
 struct Plan {
-  int KS, grid, nws;
-  bool act_lds;
+  int KS, grid, nus, mode;
 };
 
-// Launch plan (rules from measurements on the decode, FP8 and wide-output
-// shapes).  Activations go to LDS whenever they fit (reading them from L2 per
-// window costs more load instructions than the weights themselves).  Few
-// tiles (fewer than two per CU): 4 waves split K and a workgroup owns two
-// tiles, which halves the activation fill per tile; many tiles: 8 waves split
-// K of one tile.  Each wave keeps at least two windows.  The grid is the
-// number of tile groups, capped at the resident workgroups (persistent).
+// Launch plan.  Activations go to LDS whenever they fit (reading them from
+// L2 per window costs more load instructions than the weights themselves),
+// with the deep ring when it fits beside them.  The K split KS (and with it
+// TPW = 8 / KS tiles side by side) is the one with the least work on the
+// busiest wave: rounds of tile groups per workgroup (the grid is the number
+// of tile groups, capped at the resident workgroups: persistent) times units
+// per wave, counting the units a wave pads with when KS does not divide the
+// row.  Ties go to the split with fewer padded units, then to the larger
+// split; every wave keeps at least one unit.
+template <typename T, bool FP8>
+int slots_mode(int mode, int ks, int R, int M, int NW) {
+  return mode == 2 ? slots_for<T, FP8, 2>(ks, R, M, NW)
+                   : mode == 1 ? slots_for<T, FP8, 1>(ks, R, M, NW) : slots_for<T, FP8, 0>(ks, R, M, NW);
+}
+
 template <typename T, bool FP8>
 Plan plan(int64_t N, int M, int R, int NW) {
   const int64_t tiles = (N + 15) / 16;
-  const int cus = num_cus();
-  const bool lds = lds_bytes(true, FP8, M, NW) <= kMaxLds;
-  int ks = tiles < 2 * static_cast<int64_t>(cus) ? 4 : 8;
-  while (ks > 1 && NW < 2 * ks) ks >>= 1;
-  const int64_t ntg = (tiles + kWaves / ks - 1) / (kWaves / ks);
-  const int64_t slots = lds ? slots_for<T, FP8, true>(ks, R, M, NW) : slots_for<T, FP8, false>(ks, R, M, NW);
-  return Plan{ks, static_cast<int>(ntg < slots ? ntg : slots), (NW + ks - 1) / ks, lds};
+  const int NU = FP8 ? NW : (NW + 1) / 2;
+  const int mode = lds_bytes(2, FP8, M, NW) <= kMaxLds ? 2 : lds_bytes(1, FP8, M, NW) <= kMaxLds ? 1 : 0;
+  Plan best{1, 1, NU, mode};
+  int64_t best_cost = -1;
+  int best_pad = 0;
+  for (int ks = 8; ks >= 1; ks >>= 1) {
+    if (NU < ks) continue;
+    const int64_t ntg = (tiles + kWaves / ks - 1) / (kWaves / ks);
+    const int64_t slots = slots_mode<T, FP8>(mode, ks, R, M, NW);
+    const int64_t grid = ntg < slots ? ntg : slots;
+    const int nus = (NU + ks - 1) / ks;
+    const int64_t cost = (ntg + grid - 1) / grid * nus;
+    const int pad = nus * ks - NU;
+    if (best_cost < 0 || cost < best_cost || (cost == best_cost && pad < best_pad)) {
+      best_cost = cost;
+      best_pad = pad;
+      best = Plan{ks, static_cast<int>(grid), nus, mode};
+    }
+  }
+  return best;
 }
 
 // The plan depends only on the sizes, the device and the variant's resource
@@ -553,16 +668,15 @@ Plan cached_plan(int64_t N, int M, int R, int NW) {
   return p;
 }
 
-template <typename T, int KS, bool FP8, bool LDS>
+template <typename T, int KS, bool FP8, int MODE>
 void launch_v(const MatmulArgs& a, const Plan& p, int R, size_t lds, FastDiv wpb, FastDiv cpr, int tiles) {
   hipStream_t s = static_cast<hipStream_t>(a.stream);
-#define FP4W_GEMV_LAUNCH(R_)                                                                           \
-  allow_lds<T, KS, FP8, LDS, R_>();                                                                    \
-  hipLaunchKernelGGL((gemv_kernel<T, KS, FP8, LDS, R_, depth<FP8, LDS>()>), dim3(p.grid),              \
-                     dim3(64 * kWaves), lds, s, static_cast<const T*>(a.A), a.B, a.scales, a.ws2,      \
-                     static_cast<const T*>(a.bias), static_cast<T*>(a.Y), static_cast<int>(a.M),       \
-                     static_cast<int>(a.N), static_cast<int>(a.K), static_cast<int>(a.scale_cols), wpb, \
-                     cpr, tiles, p.nws)
+#define FP4W_GEMV_LAUNCH(R_)                                                                            \
+  allow_lds<T, KS, FP8, MODE, R_>();                                                                    \
+  hipLaunchKernelGGL((kernel_ptr<T, KS, FP8, MODE, R_>()), dim3(p.grid), dim3(64 * kWaves), lds, s,     \
+                     static_cast<const T*>(a.A), a.B, a.scales, a.ws2, static_cast<const T*>(a.bias),   \
+                     static_cast<T*>(a.Y), static_cast<int>(a.M), static_cast<int>(a.N),                \
+                     static_cast<int>(a.K), static_cast<int>(a.scale_cols), wpb, cpr, tiles, p.nus)
   if (R == 1) {
     FP4W_GEMV_LAUNCH(1);
   } else if (R == 2) {
@@ -571,6 +685,16 @@ void launch_v(const MatmulArgs& a, const Plan& p, int R, size_t lds, FastDiv wpb
     FP4W_GEMV_LAUNCH(4);
   }
 #undef FP4W_GEMV_LAUNCH
+}
+
+template <typename T, bool FP8, int MODE>
+void launch_mode(const MatmulArgs& a, const Plan& p, int R, size_t lds, FastDiv wpb, FastDiv cpr, int tiles) {
+  switch (p.KS) {
+    case 1: launch_v<T, 1, FP8, MODE>(a, p, R, lds, wpb, cpr, tiles); break;
+    case 2: launch_v<T, 2, FP8, MODE>(a, p, R, lds, wpb, cpr, tiles); break;
+    case 4: launch_v<T, 4, FP8, MODE>(a, p, R, lds, wpb, cpr, tiles); break;
+    default: launch_v<T, 8, FP8, MODE>(a, p, R, lds, wpb, cpr, tiles); break;
+  }
 }
 
 template <typename T, bool FP8>
@@ -584,22 +708,15 @@ int launch_t(const MatmulArgs& a) {
   const int R = FP8 ? (M >= 3 ? 4 : M) : (M > 4 ? 2 : 1);
   const Plan p = cached_plan<T, FP8>(a.N, M, R, NW);
   const int tiles = static_cast<int>((a.N + 15) / 16);
-  const size_t lds = lds_bytes(p.act_lds, FP8, M, NW);
+  const size_t lds = lds_bytes(p.mode, FP8, M, NW);
   const FastDiv wpb = make_fastdiv(FP8 ? static_cast<uint32_t>(a.block_size / 128) : 1u);
   const FastDiv cpr = make_fastdiv(static_cast<uint32_t>(NW) * 16u + 1u);  // 16-byte chunks per LDS row
-#define FP4W_GEMV_KS(LDS_)                                                   \
-  switch (p.KS) {                                                            \
-    case 1: launch_v<T, 1, FP8, LDS_>(a, p, R, lds, wpb, cpr, tiles); break;  \
-    case 2: launch_v<T, 2, FP8, LDS_>(a, p, R, lds, wpb, cpr, tiles); break;  \
-    case 4: launch_v<T, 4, FP8, LDS_>(a, p, R, lds, wpb, cpr, tiles); break;  \
-    default: launch_v<T, 8, FP8, LDS_>(a, p, R, lds, wpb, cpr, tiles); break; \
-  }
-  if (p.act_lds) {
-    FP4W_GEMV_KS(true)
-  } else {
-    FP4W_GEMV_KS(false)
-  }
-#undef FP4W_GEMV_KS
+  if (p.mode == 2)
+    launch_mode<T, FP8, 2>(a, p, R, lds, wpb, cpr, tiles);
+  else if (p.mode == 1)
+    launch_mode<T, FP8, 1>(a, p, R, lds, wpb, cpr, tiles);
+  else
+    launch_mode<T, FP8, 0>(a, p, R, lds, wpb, cpr, tiles);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
