@@ -54,6 +54,12 @@ FP4_CASES = [
     (4, 33, 30, 15, "bf16", True, "ceil", [fw.PATH_FP4_GENERIC]),   # odd block size
     (12, 20, 18, 5, "fp16", False, "floor", [fw.PATH_FP4_GENERIC]),
     (2, 64, 64, 32, "bf16", True, "ceil", [fw.PATH_FP4_GENERIC]),   # block size 32
+    # GEMV activation modes: K = 17536 (137 windows, odd: the last unit has one
+    # window) does not fit in LDS, so the activations stream from L2; two row
+    # halves streamed; 6 rows x 41 windows fit only beside the shallow ring
+    (4, 300, 17536, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMV]),
+    (8, 100, 17408, 16, "fp16", True, "ceil", [fw.PATH_FP4_GEMV]),
+    (6, 200, 5248, 16, "bf16", False, "ceil", [fw.PATH_FP4_GEMV]),
 ]
 
 
@@ -168,6 +174,9 @@ FP8_CASES = [
     (5, 40, 208, 128, "bf16", True, "ceil", [fw.PATH_FP8_GENERIC]),
     (5, 40, 208, 128, "fp16", True, "floor", [fw.PATH_FP8_GENERIC]),
     (3, 21, 37, 16, "bf16", True, "ceil", [fw.PATH_FP8_GENERIC]),
+    # GEMV activation modes: streamed from L2 (K = 17408), shallow ring (8 rows)
+    (4, 300, 17408, 128, "bf16", True, "ceil", [fw.PATH_FP8_GEMV]),
+    (8, 200, 5120, 128, "fp16", False, "ceil", [fw.PATH_FP8_GEMV]),
 ]
 
 
