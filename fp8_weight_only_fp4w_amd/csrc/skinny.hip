@@ -24,23 +24,21 @@
 // The decode cost is shared by all row tiles.
 //
 // K mapping (a reduction axis: both operands only have to agree).  Window w
-// covers k = 128 w .. 128 w + 127; MFMA step i of it takes the 32 k at
-// 128 w + 32 i, lane group g = lane / 16 supplying 8 of them (the natural
-// MFMA order).  The weights keep their 16-byte contiguous loads (64
-// contiguous bytes per column and load instruction) and are moved between
-// lane groups in registers, with v_permlane32_swap / v_permlane16_swap:
-// each swaps one bit of the lane-group index with one bit of the register
-// index.
-//  * FP4: lane group s loads the 32 k at 128 w + 32 s, dwords d = 8-k units
-//    4 s + d; swapping both lane-group bits with both register bits leaves
-//    register i of group g holding unit 4 i + g, i.e. k 128 w + 32 i + 8 g.
-//    That lane needs the scales of blocks 8 w + 2 i + g / 2, read as the
-//    window's 8 scale bytes.
-//  * FP8: lane group s loads k 128 w + 16 s .. + 15 and 128 w + 64 + 16 s ..
-//    + 15 (8-k units 2 s, 2 s + 1, 8 + 2 s, 9 + 2 s); one swap of the high
-//    lane-group bit with the low unit-slot bit leaves step i of group g with
-//    unit 4 i + tau(g), tau(g) = 2 (g & 1) + (g >> 1).  The activations are
-//    loaded with the same tau.
+// covers k = 128 w .. 128 w + 127; in MFMA step i lane group g supplies the
+// 8-k unit 4 g + i of it (k 128 w + 32 g + 8 i .. + 7), for the weights and
+// the activations alike, so a lane's four steps take one contiguous 32-k
+// chunk of its column: one 16-byte fragment (FP4) or two (FP8).
+//  * FP4 steps 0, 1 lie in block 8 w + 2 g, steps 2, 3 in block 8 w + 2 g + 1.
+//  * Weights travel global -> LDS by direct loads: a unit is 128 contiguous
+//    bytes of each of the wave's 16 rows (two FP4 windows, one FP8 window),
+//    fetched by two instructions of 8 rows x 128 bytes.  HBM streams at full
+//    rate only for whole 128-byte lines per instruction; 16 rows x 64 bytes
+//    (the register-direct MFMA layout) reaches about two thirds of it.  Each
+//    row's chunks are loaded in the order chunk ^ (row & 7), so the fragment
+//    reads are free of bank conflicts.  A wave has a private ring and waits
+//    for its own loads only.
+//  * FP4 scale bytes travel in 128-byte pieces per row (16 windows), parked in
+//    a per-wave LDS slice.
 //
 // Activations come from L2 (at most M x K x 2 bytes, read by every
 // workgroup) in the same pipeline slot as the weights: loads retire in
@@ -51,9 +49,9 @@
 // instead (4 rows x 256 contiguous bytes per instruction) the same bytes
 // cost about half the time.  So a window's activations are loaded
 // row-major and moved into the MFMA layout through a wave-private LDS
-// scratch (16-byte chunks XOR-swizzled by row, conflict-free on both the
-// write and the read side), which also holds the K-split reduction at the
-// end of a tile.
+// staging area, one row tile at a time (16-byte chunks XOR-swizzled by row,
+// conflict-free on both the write and the read side), which also holds the
+// K-split reduction at the end of a tile.
 //
 // [FP4 doc] = "MatMulBlockQuantizedFp4Weight - CUDA Operator Documentation"
 // [FP8 doc] = "MatMulBlockQuantizedFp8Weight - CUDA Operator Documentation"
@@ -70,38 +68,59 @@ namespace {
 
 constexpr int kSkWaves = 8;  // waves per workgroup (KS x TPW)
 
-// One window of one lane: weights, the block scale(s) of the lane's column,
-// the bias bits (first window of a tile only) and 4 x 16 activation bytes per
-// row tile (row-major: load q of tile t holds rows 16 t + 4 q .. + 3).
+// One window of one lane, in registers: the block scales (FP4: the piece of
+// 16 windows, first window of each piece; FP8: the window's FP32 scale), the
+// bias bits (first window of a tile) and 4 x 16 activation bytes per row
+// tile (row-major: load q of tile t holds rows 16 t + 4 q .. + 3).  The
+// weights go to LDS by direct loads.
 template <bool FP8, int MT>
 struct SkRaw;
 template <int MT>
 struct SkRaw<false, MT> {
-  u32x4 w;
-  u32x2 sc;  // the 8 E4M3 scale bytes of the window
+  u32x4 sc[2];  // scale rows lr and 8 + lr, 16 bytes each
   uint32_t bias;
   u32x4 a[4 * MT];
 };
 template <int MT>
 struct SkRaw<true, MT> {
-  u32x4 w0, w1;
   uint32_t sc;  // FP32 block scale bits
   uint32_t bias;
   u32x4 a[4 * MT];
 };
 
-// v_permlane32_swap: the upper 32 lanes of a trade places with the lower 32
-// lanes of b.  v_permlane16_swap: the odd 16-lane rows of a trade places
-// with the even rows of b.
-__device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
-  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
-  a = r[0];
-  b = r[1];
+constexpr uint32_t kSkUnit = 2048;      // weight slot: 16 rows x 128 bytes
+constexpr uint32_t kSkScratch = 4096;   // activation staging: 16 rows x 256 bytes
+constexpr int kSkSlicePitch = 144;      // FP4 scale slice: bytes per row (128 + 16)
+constexpr uint32_t kSkSlice = 16 * kSkSlicePitch;
+
+// Weight slots of a wave's ring.  A unit is 128 contiguous bytes of each of
+// the wave's 16 rows: two windows for FP4 (loaded every second step), one
+// for FP8.  A slot is refilled only after the last step that reads it.
+template <bool FP8, int D>
+constexpr int sk_ring() {
+  return FP8 ? D + 1 : (D + 1) / 2 + 1;
 }
-__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
-  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
-  a = r[0];
-  b = r[1];
+
+template <bool FP8, int D>
+constexpr uint32_t sk_lds_per_wave() {
+  return static_cast<uint32_t>(sk_ring<FP8, D>()) * kSkUnit + kSkScratch + (FP8 ? 0u : kSkSlice);
+}
+
+// Wait until at most N vector-memory loads of this wave are in flight.  The
+// compiler does not track the LDS side of direct loads, so the fences keep
+// the LDS reads that follow after the wait.
+template <int N>
+__device__ __forceinline__ void sk_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));  // vmcnt(N) only
+  __asm__ volatile("" ::: "memory");
+}
+
+// Workgroup barrier for data exchanged through LDS by ds_write / ds_read only
+// (__syncthreads would also wait for the direct loads in flight).
+__device__ __forceinline__ void sk_lds_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 struct SkPos {
@@ -121,17 +140,22 @@ __global__ __launch_bounds__(64 * kSkWaves) void skinny_kernel(
     int cols, FastDiv win_per_block, int num_tiles, int nws) {
   constexpr int TPW = kSkWaves / KS;
   constexpr int S = D + 1;
+  constexpr int NS = sk_ring<FP8, D>();
+  constexpr uint32_t kWaveLds = sk_lds_per_wave<FP8, D>();
   typedef SkRaw<FP8, MT> RawT;
   typedef ActTraits<T> Tr;
   typedef typename Tr::vec8 V;
-  // per wave: MT x 16 rows x 256 bytes of activations (one window), reused
-  // for the K-split partial sums at the end of a tile
+  // per wave: the weight ring, the activation staging area (also the K-split
+  // partial sums at the end of a tile) and (FP4) the scale slice
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int li = lane & 15, g = lane >> 4;
+  const int lr = lane >> 3, lc = lane & 7;  // direct loads: row lr of an 8-row half, position lc
   const int ks = wave % KS, tw = wave / KS;
-  unsigned char* scr = smem + wave * (MT * 4096);
+  unsigned char* ring = smem + wave * kWaveLds;
+  unsigned char* scr = ring + NS * kSkUnit;
+  unsigned char* slice = scr + kSkScratch;
   const int NW = K >> 7;
   const int ntg = (num_tiles + TPW - 1) / TPW;
   const int iters = (ntg - static_cast<int>(blockIdx.x) + static_cast<int>(gridDim.x) - 1) /
@@ -147,15 +171,26 @@ __global__ __launch_bounds__(64 * kSkWaves) void skinny_kernel(
   // window) of row 16 t + 4 q + l / 16; rows past M read zeros
   const uint32_t row_pitch = static_cast<uint32_t>(K) * 2u;
   const uint32_t a_lane = static_cast<uint32_t>(g) * row_pitch + 16u * static_cast<uint32_t>(li);
-  // LDS byte offsets: row-major chunk written by this lane (load q adds
-  // 1024 q and XORs the chunk with 4 q), and the chunk this lane reads for
-  // MFMA step i (row li, chunk 4 i + tau(g); step i XORs with 4 i)
-  const uint32_t tau = FP8 ? static_cast<uint32_t>(2 * (g & 1) + (g >> 1)) : static_cast<uint32_t>(g);
+  // LDS byte offsets of the staging area: the chunk this lane writes (load q
+  // adds 1024 q and XORs the chunk with 4 q: chunk c of row r sits at
+  // position c ^ r), and the chunk it reads for MFMA step i: row li, chunk
+  // 4 g + i, i.e. r_lds ^ 16 i
   const uint32_t w_lds = static_cast<uint32_t>(g) * 256u + 16u * static_cast<uint32_t>(li ^ g);
-  const uint32_t r_lds = static_cast<uint32_t>(li) * 256u + 16u * (tau ^ static_cast<uint32_t>(li));
-  // FP4: bit offset of the scale bytes of blocks 2 i + g / 2 in the window's
-  // scale dwords (byte g / 2 for steps 0 and 2, byte 2 + g / 2 for 1 and 3)
-  const uint32_t sc_shift = 8u * static_cast<uint32_t>(g >> 1);
+  const uint32_t r_lds = static_cast<uint32_t>(li) * 256u + 16u * static_cast<uint32_t>((4 * g) ^ li);
+  // Weights: direct loads of row lr (+ 8), chunk lc ^ lr (lr == row & 7), so
+  // chunk c of row r sits at position c ^ (r & 7) of its 128-byte row.  The
+  // lane's fragment: FP4 window s of the unit, chunk 4 s + g (dword i = 8-k
+  // unit 4 g + i of the window, MFMA step i); FP8 chunks 2 g and 2 g + 1
+  // (step i: chunk 2 g + i / 2, dwords 2 (i & 1) and 2 (i & 1) + 1).
+  const int sw = li & 7;
+  const uint32_t wf0 = 128u * li + 16u * static_cast<uint32_t>(FP8 ? ((2 * g) ^ sw) : (g ^ sw));
+  const uint32_t wf1 = 128u * li + 16u * static_cast<uint32_t>(FP8 ? ((2 * g + 1) ^ sw) : ((4 + g) ^ sw));
+  const uint32_t wl = lr * row_bytes + 16u * static_cast<uint32_t>(lc ^ lr);
+  const uint32_t wl8 = wl + 8u * row_bytes;
+  // FP4 scale pieces (16 windows = 128 bytes of a row): rows lr (+ 8), bytes
+  // 16 lc of the piece
+  const uint32_t sl = lr * srow_bytes + 16u * lc;
+  const uint32_t sl8 = sl + 8u * srow_bytes;
   auto scol = [&](int w) {  // FP8 scale column of window w
     return min(fdiv(static_cast<uint32_t>(w), win_per_block), static_cast<uint32_t>(cols - 1));
   };
@@ -172,18 +207,18 @@ __global__ __launch_bounds__(64 * kSkWaves) void skinny_kernel(
   };
   set_load_tile();
 
+  int lslot = 0;  // ring slot of the next unit to load
   auto load = [&](RawT& r) {
     if (lp.j == 0) r.bias = buf_load_u16(biasr, 2u * li);
     const int w = ks * nws + lp.j;
     const bool ok = w < NW;  // windows past K read zeros (weights, scales, activations)
     if constexpr (FP8) {
-      const uint32_t off = ok ? li * row_bytes + 128u * w + 16u * g : kOutOfRange;
-      r.w0 = buf_load_b128(br, off);
-      r.w1 = buf_load_b128(br, off + 64u);
       r.sc = buf_load_b32(sr, ok ? li * srow_bytes + 4u * scol(w) : kOutOfRange);
     } else {
-      r.w = buf_load_b128(br, ok ? li * row_bytes + 64u * w + 16u * g : kOutOfRange);
-      r.sc = buf_load_b64(sr, ok ? li * srow_bytes + 8u * w : kOutOfRange);
+      if (lp.j % 16 == 0) {  // E4M3 scales of windows w .. w + 15 (bytes past the row are never used)
+        r.sc[0] = buf_load_b128(sr, ok ? sl + 8u * w : kOutOfRange);
+        r.sc[1] = buf_load_b128(sr, ok ? sl8 + 8u * w : kOutOfRange);
+      }
     }
 #pragma unroll
     for (int t = 0; t < MT; ++t)
@@ -194,6 +229,14 @@ __global__ __launch_bounds__(64 * kSkWaves) void skinny_kernel(
         r.a[4 * t + q] = buf_load_b128(
             a_rsrc, valid ? a_lane + static_cast<uint32_t>(r0) * row_pitch + 256u * w : kOutOfRange);
       }
+    // the unit's weights, last (FP4: at the first window of the unit)
+    if (FP8 || (lp.j & 1) == 0) {
+      const uint32_t ub = (FP8 ? 128u : 64u) * static_cast<uint32_t>(w);
+      unsigned char* dst = ring + lslot * kSkUnit;
+      buf_load_lds<16>(br, ok ? wl + ub : kOutOfRange, dst);
+      buf_load_lds<16>(br, ok ? wl8 + ub : kOutOfRange, dst + 1024);
+      lslot = lslot + 1 == NS ? 0 : lslot + 1;
+    }
     if (++lp.j == nws) {
       lp.j = 0;
       lp.tg += stride;
@@ -207,84 +250,85 @@ __global__ __launch_bounds__(64 * kSkWaves) void skinny_kernel(
   uint32_t tbias = 0;
   RawT raw[S];
   SkPos cp{static_cast<int>(blockIdx.x), 0};
+  int cslot = 0;  // ring slot of the unit being multiplied
 
 #pragma unroll
   for (int d = 0; d < D; ++d) load(raw[d]);
 
   auto consume = [&](const RawT& r) {
     const int j = cp.j;
+    const int w = ks * nws + j;
     if (j == 0) tbias = r.bias;
-    // activations: row-major chunks into the scratch, back in the MFMA
-    // layout (same wave, so LDS order needs no wait between the two)
+    V bw[4];
+    float scf = 1.0f;
+    if constexpr (FP8) {
+      sk_wait_vm<D*(4 * MT + 3)>();  // this window's weights have landed
+      const unsigned char* slot = ring + cslot * kSkUnit;
+      const u32x4 c0 = *reinterpret_cast<const u32x4*>(slot + wf0);
+      const u32x4 c1 = *reinterpret_cast<const u32x4*>(slot + wf1);
+      bw[0] = Tr::decode8_fp8(c0.x, c0.y);
+      bw[1] = Tr::decode8_fp8(c0.z, c0.w);
+      bw[2] = Tr::decode8_fp8(c1.x, c1.y);
+      bw[3] = Tr::decode8_fp8(c1.z, c1.w);
+      scf = __builtin_bit_cast(float, r.sc);
+      cslot = cslot + 1 == NS ? 0 : cslot + 1;
+    } else {
+      if (j % 16 == 0) {
+        *reinterpret_cast<u32x4*>(slice + kSkSlicePitch * lr + 16 * lc) = r.sc[0];
+        *reinterpret_cast<u32x4*>(slice + kSkSlicePitch * (8 + lr) + 16 * lc) = r.sc[1];
+      }
+      if ((j & 1) == 0) sk_wait_vm<D * 4 * MT>();  // this unit's weights have landed
+      const unsigned char* slot = ring + cslot * kSkUnit;
+      const u32x4 wv = *reinterpret_cast<const u32x4*>(slot + ((j & 1) ? wf1 : wf0));
+      // scales of blocks 2 g (steps 0, 1) and 2 g + 1 (steps 2, 3) of the
+      // window, folded into the operand (exact); windows past K get zero
+      const uint32_t sb =
+          w < NW ? *reinterpret_cast<const uint16_t*>(slice + kSkSlicePitch * li + 8 * (j % 16) + 2 * g) : 0u;
+      const float s0 = e4m3_to_f32<0>(sb), s1 = e4m3_to_f32<1>(sb);
+      bw[0] = Tr::decode8(wv.x, Tr::make_scale(s0));
+      bw[1] = Tr::decode8(wv.y, Tr::make_scale(s0));
+      bw[2] = Tr::decode8(wv.z, Tr::make_scale(s1));
+      bw[3] = Tr::decode8(wv.w, Tr::make_scale(s1));
+      if (j & 1) cslot = cslot + 1 == NS ? 0 : cslot + 1;
+    }
+    // activations, one row tile at a time: row-major chunks into the staging
+    // area, back in the MFMA layout (same wave, so LDS order needs no wait)
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
+    for (int t = 0; t < MT; ++t) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<u32x4*>(scr + 4096 * t + 1024 * q + (w_lds ^ (64u * q))) = r.a[4 * t + q];
-    V av[MT][4];
+        *reinterpret_cast<u32x4*>(scr + 1024 * q + (w_lds ^ (64u * q))) = r.a[4 * t + q];
+      V av[4];
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        av[t][i] = *reinterpret_cast<const V*>(scr + 4096 * t + (r_lds ^ (64u * i)));
-    V bw[4];
-    if constexpr (FP8) {
-      // units 2s / 2s+1 (and 8+2s / 9+2s) of lane group s: swap the high
-      // lane-group bit with the unit-slot bit
-      uint32_t q[8] = {r.w0.x, r.w0.y, r.w0.z, r.w0.w, r.w1.x, r.w1.y, r.w1.z, r.w1.w};
-      swap32(q[0], q[2]);
-      swap32(q[1], q[3]);
-      swap32(q[4], q[6]);
-      swap32(q[5], q[7]);
-      bw[0] = Tr::decode8_fp8(q[0], q[1]);
-      bw[1] = Tr::decode8_fp8(q[2], q[3]);
-      bw[2] = Tr::decode8_fp8(q[4], q[5]);
-      bw[3] = Tr::decode8_fp8(q[6], q[7]);
-      const float sc = __builtin_bit_cast(float, r.sc);
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
+      for (int i = 0; i < 4; ++i) av[i] = *reinterpret_cast<const V*>(scr + (r_lds ^ (16u * i)));
+      if constexpr (FP8) {
         f32x4 blk = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) blk = Tr::mfma(av[t][i], bw[i], blk);
+        for (int i = 0; i < 4; ++i) blk = Tr::mfma(av[i], bw[i], blk);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(blk[q], sc, acc[t][q]);
+        for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(blk[q], scf, acc[t][q]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[t] = Tr::mfma(av[i], bw[i], acc[t]);
       }
-    } else {
-      // 4 x 4 transpose of dwords across lane groups: register i of group g
-      // becomes k 32 i + 8 g of the window
-      uint32_t q[4] = {r.w.x, r.w.y, r.w.z, r.w.w};
-      swap32(q[0], q[2]);
-      swap32(q[1], q[3]);
-      swap16(q[0], q[1]);
-      swap16(q[2], q[3]);
-      // scale of block 2 i + g / 2 for step i, folded into the operand
-      const uint32_t lo = r.sc.x >> sc_shift, hi = r.sc.y >> sc_shift;
-      bw[0] = Tr::decode8(q[0], Tr::make_scale(e4m3_to_f32<0>(lo)));
-      bw[1] = Tr::decode8(q[1], Tr::make_scale(e4m3_to_f32<2>(lo)));
-      bw[2] = Tr::decode8(q[2], Tr::make_scale(e4m3_to_f32<0>(hi)));
-      bw[3] = Tr::decode8(q[3], Tr::make_scale(e4m3_to_f32<2>(hi)));
-#pragma unroll
-      for (int t = 0; t < MT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[t] = Tr::mfma(av[t][i], bw[i], acc[t]);
     }
     if (j == nws - 1) {
-      // end of a tile: reduce the K split through LDS, then the epilogue
+      // end of a tile: reduce the K split through the staging areas (this
+      // wave's reads of them were issued before these writes), then the
+      // epilogue
       if (KS > 1) {
-        // partial sums in the first MT KiB of each wave's scratch (its reads
-        // of this window were issued before these writes)
-        f32x4* red = reinterpret_cast<f32x4*>(smem);
-        constexpr int kWaveVec = MT * 4096 / 16;  // f32x4 per wave scratch
 #pragma unroll
-        for (int t = 0; t < MT; ++t) red[wave * kWaveVec + t * 64 + lane] = acc[t];
-        __syncthreads();
+        for (int t = 0; t < MT; ++t) *reinterpret_cast<f32x4*>(scr + 1024 * t + 16 * lane) = acc[t];
+        sk_lds_barrier();
         if (ks == 0) {
 #pragma unroll
           for (int v = 1; v < KS; ++v)
 #pragma unroll
-            for (int t = 0; t < MT; ++t) acc[t] += red[(wave + v) * kWaveVec + t * 64 + lane];
+            for (int t = 0; t < MT; ++t)
+              acc[t] += *reinterpret_cast<const f32x4*>(smem + (wave + v) * kWaveLds + NS * kSkUnit + 1024 * t +
+                                                        16 * lane);
         }
-        __syncthreads();
+        sk_lds_barrier();
       }
       if (ks == 0) {
         const int n = 16 * (cp.tg * TPW + tw) + li;
@@ -339,9 +383,9 @@ int sk_num_cus() {
   return cus;
 }
 
-template <int MT>
+template <bool FP8, int MT>
 constexpr size_t sk_lds() {
-  return static_cast<size_t>(kSkWaves) * MT * 4096;
+  return static_cast<size_t>(kSkWaves) * sk_lds_per_wave<FP8, sk_depth<MT>()>();
 }
 
 // Dynamic LDS above 64 KiB must be allowed per kernel, once.
@@ -350,7 +394,7 @@ void sk_allow_lds() {
   static bool done = false;
   if (!done) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&skinny_kernel<T, FP8, MT, KS, sk_depth<MT>()>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sk_lds<MT>()));
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sk_lds<FP8, MT>()));
     done = true;
   }
 }
@@ -360,7 +404,7 @@ int sk_slots() {
   sk_allow_lds<T, FP8, MT, KS>();
   int v = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, skinny_kernel<T, FP8, MT, KS, sk_depth<MT>()>,
-                                                   64 * kSkWaves, sk_lds<MT>()) != hipSuccess ||
+                                                   64 * kSkWaves, sk_lds<FP8, MT>()) != hipSuccess ||
       v < 1)
     v = 1;
   return v * sk_num_cus();
@@ -370,20 +414,44 @@ struct SkPlan {
   int KS, grid, nws;
 };
 
+// The K split KS (TPW = 8 / KS tiles side by side) with the least work on
+// the busiest wave: rounds of tile groups per workgroup (persistent grid,
+// capped at the resident workgroups) times windows per wave, counting the
+// windows a wave pads with (FP4 waves start at even windows, since a weight
+// unit holds two).  Ties go to less padding, then to the larger split; every
+// wave keeps at least two windows.
+template <typename T, bool FP8, int MT>
+int sk_slots_ks(int ks) {
+  switch (ks) {
+    case 1: return sk_slots<T, FP8, MT, 1>();
+    case 2: return sk_slots<T, FP8, MT, 2>();
+    case 4: return sk_slots<T, FP8, MT, 4>();
+    default: return sk_slots<T, FP8, MT, 8>();
+  }
+}
+
 template <typename T, bool FP8, int MT>
 SkPlan sk_plan(int64_t N, int NW) {
   const int64_t tiles = (N + 15) / 16;
-  int ks = kSkWaves;
-  while (ks > 1 && NW < 2 * ks) ks >>= 1;  // at least two windows per wave
-  int slots = 0;
-  switch (ks) {
-    case 1: slots = sk_slots<T, FP8, MT, 1>(); break;
-    case 2: slots = sk_slots<T, FP8, MT, 2>(); break;
-    case 4: slots = sk_slots<T, FP8, MT, 4>(); break;
-    default: slots = sk_slots<T, FP8, MT, 8>(); break;
+  SkPlan best{1, 1, NW + (FP8 ? 0 : (NW & 1))};
+  int64_t best_cost = -1;
+  int best_pad = 0;
+  for (int ks = kSkWaves; ks >= 1; ks >>= 1) {
+    if (ks > 1 && NW < 2 * ks) continue;
+    int nws = (NW + ks - 1) / ks;
+    if (!FP8) nws += nws & 1;
+    const int64_t ntg = (tiles + kSkWaves / ks - 1) / (kSkWaves / ks);
+    const int64_t slots = sk_slots_ks<T, FP8, MT>(ks);
+    const int64_t grid = ntg < slots ? ntg : slots;
+    const int64_t cost = (ntg + grid - 1) / grid * nws;
+    const int pad = nws * ks - NW;
+    if (best_cost < 0 || cost < best_cost || (cost == best_cost && pad < best_pad)) {
+      best_cost = cost;
+      best_pad = pad;
+      best = SkPlan{ks, static_cast<int>(grid), nws};
+    }
   }
-  const int64_t ntg = (tiles + kSkWaves / ks - 1) / (kSkWaves / ks);
-  return SkPlan{ks, static_cast<int>(ntg < slots ? ntg : slots), (NW + ks - 1) / ks};
+  return best;
 }
 
 // One plan per shape (occupancy queries cost more than the kernel).
@@ -426,7 +494,7 @@ void sk_launch_mt(const MatmulArgs& a, FastDiv wpb) {
 #define FP4W_SK_LAUNCH(KS_)                                                                              \
   sk_allow_lds<T, FP8, MT, KS_>();                                                                       \
   hipLaunchKernelGGL((skinny_kernel<T, FP8, MT, KS_, sk_depth<MT>()>), dim3(p.grid), dim3(64 * kSkWaves), \
-                     sk_lds<MT>(), s, static_cast<const T*>(a.A), a.B, a.scales, a.ws2, static_cast<const T*>(a.bias), \
+                     (sk_lds<FP8, MT>()), s, static_cast<const T*>(a.A), a.B, a.scales, a.ws2, static_cast<const T*>(a.bias), \
                      static_cast<T*>(a.Y), static_cast<int>(a.M), static_cast<int>(a.N),                 \
                      static_cast<int>(a.K), static_cast<int>(a.scale_cols), wpb, tiles, p.nws)
   switch (p.KS) {
