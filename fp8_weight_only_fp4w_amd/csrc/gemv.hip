@@ -1,16 +1,16 @@
 // Decode GEMV (1 <= M <= 8) for weight-only FP4 and FP8, on MFMA.
 //
-// Memory-bound: every packed weight byte and scale byte is read from HBM once
-// with 16-byte loads; activations (M x K, at most a few hundred KiB) come from
-// LDS or L2.
+// Memory-bound: every packed weight byte and scale byte is read from HBM once,
+// in whole 128-byte lines; activations (M x K, at most a few hundred KiB) come
+// from LDS or L2.
 //
 // Common structure (the pages' CUDA version is [FP4 doc] §4 "Tensor-core
 // sub-path" / [FP8 doc] §4.1, with mma.m16n8k16; this is re-derived for the
 // CDNA4 MFMA layouts).  A wave owns a tile of 16 output columns n (the MFMA B
 // operand: lane l supplies column l % 16).  K is a reduction axis, so it is
 // permuted freely as long as both operands agree: in window w (128 k) lane
-// group g = l / 16 loads the contiguous chunk c = 4w + g of 32 k of its
-// column, one 16-byte load per lane for FP4 (two for FP8).
+// group g = l / 16 takes the contiguous chunk c = 4w + g of 32 k of its
+// column, one 16-byte fragment per lane for FP4 (two for FP8).
 //
 // FP4 (16x16x32 MFMA, "block-diagonal" activations).  Folding the E4M3 scale
 // into BF16 weights would be exact ([FP4 doc] §4), but costs a convert, two
@@ -33,13 +33,13 @@
 // accumulated in a fresh MFMA accumulator.  Result lane (n, g) holds rows
 // 4g .. 4g + 3.
 //
-// Latency hiding (what decides the bandwidth): a wave keeps D windows of
-// weights in flight ahead of the one it multiplies; the pipeline runs as one
-// flat sequence over all tile groups the (persistent) workgroup owns, so it
-// never drains between tiles.  All loads are raw buffer loads and
-// branch-free (tails read zeros), so the loop only ever waits for its oldest
-// load.  A workgroup is KS x TPW waves: KS waves split the K windows of one
-// tile (the page's KSplit, reduced through LDS), TPW tiles side by side.
+// Pipeline: a wave keeps D units of weights (below) in flight ahead of the one
+// it multiplies; the pipeline runs as one flat sequence over all tile groups
+// the (persistent) workgroup owns, so it never drains between tiles.  All
+// loads are raw buffer loads and branch-free (tails read zeros), so the loop
+// only ever waits for its oldest loads.  A workgroup is KS x TPW waves: KS
+// waves split the K windows of one tile (the page's KSplit, reduced through
+// LDS), TPW tiles side by side.
 //
 // [FP4 doc] = "MatMulBlockQuantizedFp4Weight - CUDA Operator Documentation"
 // [FP8 doc] = "MatMulBlockQuantizedFp8Weight - CUDA Operator Documentation"
