@@ -60,6 +60,9 @@ FP4_CASES = [
     (4, 300, 17536, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMV]),
     (8, 100, 17408, 16, "fp16", True, "ceil", [fw.PATH_FP4_GEMV]),
     (6, 200, 5248, 16, "bf16", False, "ceil", [fw.PATH_FP4_GEMV]),
+    # many tile groups per persistent workgroup, with a K split that pads
+    # (10 windows = 5 two-window units)
+    (3, 70000, 1280, 16, "fp16", True, "ceil", [fw.PATH_FP4_GEMV]),
 ]
 
 
@@ -177,6 +180,9 @@ FP8_CASES = [
     # GEMV activation modes: streamed from L2 (K = 17408), shallow ring (8 rows)
     (4, 300, 17408, 128, "bf16", True, "ceil", [fw.PATH_FP8_GEMV]),
     (8, 200, 5120, 128, "fp16", False, "ceil", [fw.PATH_FP8_GEMV]),
+    # streamed activations, 137 windows (the K split pads), several tile
+    # groups per workgroup
+    (4, 5000, 17536, 128, "bf16", True, "ceil", [fw.PATH_FP8_GEMV]),
 ]
 
 
