@@ -393,6 +393,25 @@ def extra_w8a8(steps, warmup):
     return res
 
 
+def extra_mid_m(steps, warmup):
+    """FP4 matmul through the default dispatch at prompt-chunk sizes M = 64 ..
+    1024 (N = 17408, K = 5120): where the skinny kernel hands over to the
+    prefill GEMM, whose 256 x 256 tiles give these sizes few workgroups."""
+    N, K = 17408, 5120
+    B, ws = workloads.fp4_weights_on_device(N, K, 16, seed=11)
+    ws2 = torch.tensor([2.0 ** -8], dtype=torch.float32, device="cuda")
+    res = {}
+    for M in (64, 65, 128, 256, 512, 1024):
+        A = dev_bits(workloads.activations(np.random.default_rng(M), M, K, "bf16", "normal"), "bf16")
+        out = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        path = fw.fp4w_path_name(fw.fp4w_select_path(fw.OP_FP4_MATMUL, M, N, K, 16, K // 16))
+        n = max(4, min(steps, 20))
+        t = time_calls([lambda: fw.fp4w_matmul(A, B, ws, ws2, None, 16, out=out)], n, 2) / n
+        res[f"M{M}"] = {"path": path, "us": round(t * 1e6, 1), "TFLOPs": round(2 * M * N * K / t / 1e12, 1)}
+    del B, ws
+    return res
+
+
 def decode_step_setup():
     """Device inputs of the decode-step sequence: one weight set per launch,
     one activation per K, one output per shape (FP16, M = 4, no bias)."""
@@ -584,6 +603,7 @@ def main():
                          ("fp8_w8a8", lambda: extra_w8a8(args.steps, args.warmup)),
                          ("skinny", lambda: extra_skinny(args.steps, args.warmup)),
                          ("decode_step", lambda: extra_decode_step(args.steps, args.warmup)),
+                         ("mid_m", lambda: extra_mid_m(args.steps, args.warmup)),
                          ("fp4_prefill", extra_prefill_fp4)):
             if args.extra and name not in args.extra.split(","):
                 continue
