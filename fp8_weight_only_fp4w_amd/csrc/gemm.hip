@@ -273,6 +273,17 @@ struct LargeLds {
   uint8_t s[2][L_BN * 32];             // 2 x 8 KiB
 };
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// v_mfma_f32_32x32x16 (BF16 / FP16 in, FP32 accumulate)
+template <typename T>
+__device__ __forceinline__ f32x16 mfma32(typename ActTraits<T>::vec8 a, typename ActTraits<T>::vec8 b, f32x16 c) {
+  if constexpr (std::is_same<T, __bf16>::value)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
 // direct 16-byte global -> LDS load: lane l writes lds + 16 l
 __device__ __forceinline__ void load_lds16(const void* gptr, void* lds) {
   __builtin_amdgcn_global_load_lds(gptr, (lds_ptr_t)(lds), 16, 0, 0);
@@ -334,7 +345,7 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
   // bytes per column): same columns, LDS piece l % 4 holds global piece
   // (l % 4) ^ (col & 3).
   const uint32_t b_row = FP8 ? static_cast<uint32_t>(K) : static_cast<uint32_t>(K / 2);
-  auto b_swz = [](int col) { return FP8 ? (col & 3) : ((col >> 2) & 3); };
+  auto b_swz = [](int col) { return (col >> 2) & 3; };
   uint32_t b_off[2];  // FP4: byte offset in the tile's descriptor; FP8: global byte offset
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -390,54 +401,61 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
     }
   };
 
-  f32x4 acc[8][4];
+  // lane (c32, h): column c32 of each 32-wide N tile, k half h of every step
+  const int c32 = lane & 31, h = lane >> 5;
+  f32x16 acc[4][2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   auto compute = [&](int u) {
     const T* a_src = L.a[u % 3];
     const uint8_t* s_src = L.s[(u / kScaleSteps) & 1];
-    // lane (li, g): k 16g .. 16g + 15 of its 4 columns (FP4 8 bytes, FP8 16)
-    u32x4 bw[4];
-    float sc[4];
+    // lane (c32, h): k 32h .. 32h + 31 of its 2 columns (FP4 16 bytes, FP8 32)
+    u32x4 bw[2][FP8 ? 2 : 1];
+    float sc[2][FP8 ? 1 : 2];
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns) {
-      const int col = 64 * wn + 16 * ns + li;
+    for (int nt = 0; nt < 2; ++nt) {
+      const int col = 64 * wn + 32 * nt + c32;
       const int ss = (col >> 3) & 1;
       if constexpr (FP8) {
-        bw[ns] = *reinterpret_cast<const u32x4*>(&L.b[u % 3][col * 64 + 16 * (g ^ b_swz(col))]);
+        const uint8_t* bp = &L.b[u % 3][col * 64];
+        bw[nt][0] = *reinterpret_cast<const u32x4*>(bp + 16 * ((2 * h) ^ b_swz(col)));
+        bw[nt][1] = *reinterpret_cast<const u32x4*>(bp + 16 * ((2 * h + 1) ^ b_swz(col)));
         const int idx = min(u / spb, cols - 1) - slot_col(u / kScaleSteps);  // 0 .. 7
-        sc[ns] = *reinterpret_cast<const float*>(&s_src[col * 32 + 16 * ((idx >> 2) ^ ss) + 4 * (idx & 3)]);
+        sc[nt][0] = *reinterpret_cast<const float*>(&s_src[col * 32 + 16 * ((idx >> 2) ^ ss) + 4 * (idx & 3)]);
       } else {
-        const int gp = 2 * (u & 1) + (g >> 1);
-        const u32x2 v = *reinterpret_cast<const u32x2*>(
-            &L.b[(u >> 1) & 1][col * 64 + 16 * (gp ^ b_swz(col)) + 8 * (g & 1)]);
-        bw[ns].x = v.x;
-        bw[ns].y = v.y;
+        bw[nt][0] = *reinterpret_cast<const u32x4*>(
+            &L.b[(u >> 1) & 1][col * 64 + 16 * ((2 * (u & 1) + h) ^ b_swz(col))]);
         const int st8 = u % kScaleSteps;
-        sc[ns] = e4m3_to_f32<0>(s_src[col * 32 + 16 * ((st8 >> 2) ^ ss) + 4 * (st8 & 3) + g]);
+        const uint32_t s2 = *reinterpret_cast<const uint16_t*>(
+            &s_src[col * 32 + 16 * ((st8 >> 2) ^ ss) + 4 * (st8 & 3) + 2 * h]);
+        sc[nt][0] = e4m3_to_f32<0>(s2);
+        sc[nt][1] = e4m3_to_f32<1>(s2);
       }
     }
+    // MFMA i takes k 32h + 8i .. 32h + 8i + 7 of both operands
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      V aop[8];
+    for (int i = 0; i < 4; ++i) {
+      V aop[4];
 #pragma unroll
-      for (int ms = 0; ms < 8; ++ms)
-        aop[ms] = *reinterpret_cast<const V*>(&a_src[lds_index(128 * wm + 16 * ms + li, 2 * g + s)]);
-      V bop[4];
+      for (int ms = 0; ms < 4; ++ms)
+        aop[ms] = *reinterpret_cast<const V*>(&a_src[lds_index(128 * wm + 32 * ms + c32, 4 * h + i)]);
+      V bop[2];
 #pragma unroll
-      for (int ns = 0; ns < 4; ++ns) {
+      for (int nt = 0; nt < 2; ++nt) {
         if constexpr (FP8)
-          bop[ns] = decode8_fp8_scaled<T>(bw[ns][2 * s], bw[ns][2 * s + 1], sc[ns]);
+          bop[nt] = decode8_fp8_scaled<T>(bw[nt][i >> 1][2 * (i & 1)], bw[nt][i >> 1][2 * (i & 1) + 1], sc[nt][0]);
         else
-          bop[ns] = Tr::decode8(bw[ns][s], Tr::make_scale(sc[ns]));
+          bop[nt] = Tr::decode8(bw[nt][0][i], Tr::make_scale(sc[nt][i >> 1]));
       }
 #pragma unroll
-      for (int ms = 0; ms < 8; ++ms)
+      for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = Tr::mfma(aop[ms], bop[ns], acc[ms][ns]);
+        for (int nt = 0; nt < 2; ++nt) acc[ms][nt] = mfma32<T>(aop[ms], bop[nt], acc[ms][nt]);
     }
   };
 
@@ -478,23 +496,23 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
   constexpr int kOutPitch = L_BN + 8;  // elements per staged row (breaks bank aliasing)
   T* out = reinterpret_cast<T*>(&L.a[0][0]);
   const bool wide = (N % 8 == 0) && (reinterpret_cast<uintptr_t>(Y) % 16 == 0) && n0 + L_BN <= N;
-  float bsum[4];
+  float bsum[2];
 #pragma unroll
-  for (int ns = 0; ns < 4; ++ns) {
-    const int n = min(n0 + 64 * wn + 16 * ns + li, N - 1);
-    bsum[ns] = bias ? static_cast<float>(bias[n]) : 0.0f;
+  for (int nt = 0; nt < 2; ++nt) {
+    const int n = min(n0 + 64 * wn + 32 * nt + c32, N - 1);
+    bsum[nt] = bias ? static_cast<float>(bias[n]) : 0.0f;
   }
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     if (wm == half) {
 #pragma unroll
-      for (int ms = 0; ms < 8; ++ms)
+      for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns)
+        for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            out[(16 * ms + 4 * g + r) * kOutPitch + 64 * wn + 16 * ns + li] =
-                round_to<T>(fmaf(acc[ms][ns][r], ws2, bsum[ns]));
+          for (int r = 0; r < 16; ++r)
+            out[(32 * ms + 8 * (r >> 2) + 4 * h + (r & 3)) * kOutPitch + 64 * wn + 32 * nt + c32] =
+                round_to<T>(fmaf(acc[ms][nt][r], ws2, bsum[nt]));
     }
     __syncthreads();
     const int mrow0 = m0 + 128 * half;
