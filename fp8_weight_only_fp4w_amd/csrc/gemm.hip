@@ -266,10 +266,10 @@ __global__ __launch_bounds__(256 * WM) void gemm_kernel(
 constexpr int L_BM = 256, L_BN = 256;
 constexpr int kScaleSteps = 8;  // steps per scale slot
 
-template <typename T, bool FP8>
+template <typename T, bool FP8, bool SPLIT>
 struct LargeLds {
-  T a[3][L_BM * kLdsRow];              // 3 x 32 KiB
-  uint8_t b[FP8 ? 3 : 2][L_BN * 64];   // FP8: 3 steps; FP4: 2 slots of 2 steps (16 KiB each)
+  T a[3][L_BM * kLdsRow];                        // 3 x 32 KiB
+  uint8_t b[FP8 || SPLIT ? 3 : 2][L_BN * 64];    // FP8: 3 steps; FP4: 2 slots of 2 steps; split: 3 steps (16 KiB each)
   uint8_t s[2][L_BN * 32];             // 2 x 8 KiB
 };
 
@@ -301,49 +301,57 @@ __device__ __forceinline__ void wait_barrier() {
   __asm__ volatile("" ::: "memory");
 }
 
-template <typename T, bool FP8>
+template <typename T, bool FP8, bool SPLIT>
 __global__ __launch_bounds__(512) void gemm_large_kernel(
     const T* __restrict__ A, const uint8_t* __restrict__ B, const uint8_t* __restrict__ scales,
     const float* __restrict__ ws2p, const T* __restrict__ bias, T* __restrict__ Y, int M, int N,
-    int K, int cols, int bs, int tiles_m, int tiles_n) {
+    int K, int cols, int bs, int tiles_m, int tiles_n, int t_first) {
   typedef ActTraits<T> Tr;
   typedef typename Tr::vec8 V;
-  __shared__ __attribute__((aligned(16))) LargeLds<T, FP8> L;
+  __shared__ __attribute__((aligned(16))) LargeLds<T, FP8, SPLIT> L;
+  constexpr bool split = SPLIT;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, g = lane >> 4;
   const int wm = wave >> 2, wn = wave & 3;
 
-  // tile index: contiguous range per XCD, then groups of GM tile rows
-  const int ntiles = tiles_m * tiles_n;
+  // Whole tiles: workgroup b takes tile b (contiguous ranges per XCD, then
+  // groups of GM tile rows).  Split launch (tiles t_first ..): two workgroups
+  // take 128 rows each of one tile, and their two wave groups take the two
+  // halves of K, which are added through LDS at the end.
   int t = blockIdx.x;
-  if (ntiles % 8 == 0) t = (t % 8) * (ntiles / 8) + t / 8;
+  if (SPLIT)
+    t = t_first + t / 2;
+  else if (gridDim.x % 8 == 0)
+    t = (t % 8) * (gridDim.x / 8) + t / 8;
   constexpr int GM = 2;
   const int per_group = GM * tiles_n;
   const int first_m = (t / per_group) * GM;
   const int gsize = min(tiles_m - first_m, GM);
   const int tm = first_m + (t % per_group) % gsize;
   const int tn = (t % per_group) / gsize;
-  const int m0 = tm * L_BM, n0 = tn * L_BN;
+  const int m0 = tm * L_BM + (SPLIT ? 128 * (blockIdx.x & 1) : 0), n0 = tn * L_BN;
   const int rows_n = min(L_BN, N - n0);  // weight / scale rows of this tile
 
   // Activations: instruction j of wave w writes rows 8q .. 8q + 7 of the
   // stage, q = 8j + w; lane l lands in row 8q + l / 8, LDS chunk l % 8, which
-  // holds global chunk (l % 8) ^ lds_swz(row).
+  // holds global chunk (l % 8) ^ lds_swz(row).  Split: stage rows 128 + r hold
+  // tile row r in the second half of K.
   int a_off[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = 8 * (8 * j + wave) + (lane >> 3);
     const int chunk = (lane & 7) ^ lds_swz(row);
-    a_off[j] = min(m0 + row, M - 1) * K + 8 * chunk;
+    a_off[j] = split ? min(m0 + (row & 127), M - 1) * K + (row >> 7) * (K / 2) + 8 * chunk
+                     : min(m0 + row, M - 1) * K + 8 * chunk;
   }
   // Weights.  FP4 slot (two steps, 64 bytes per column, pieces 0-1 = the even
-  // step, 2-3 = the odd step): instruction j of wave w covers columns
+  // step, 2-3 = the odd step; split: one step, pieces 0-1 = its first half of
+  // K, 2-3 = its second half): instruction j of wave w covers columns
   // 16q .. 16q + 15, q = 8j + w; lane l lands in column 16q + l / 4, LDS piece
   // l % 4, holding global piece (l % 4) ^ ((col >> 2) & 3).  FP8 stage (64
-  // bytes per column): same columns, LDS piece l % 4 holds global piece
-  // (l % 4) ^ (col & 3).
+  // bytes per column): the same.
   const uint32_t b_row = FP8 ? static_cast<uint32_t>(K) : static_cast<uint32_t>(K / 2);
   auto b_swz = [](int col) { return (col >> 2) & 3; };
   uint32_t b_off[2];  // FP4: byte offset in the tile's descriptor; FP8: global byte offset
@@ -352,13 +360,15 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
     const int col = 16 * (8 * j + wave) + (lane >> 2);
     const int piece = (lane & 3) ^ b_swz(col);
     b_off[j] = FP8 ? static_cast<uint32_t>(min(n0 + col, N - 1)) * b_row + 16u * piece
-                   : static_cast<uint32_t>(col) * b_row + 16u * piece;
+                   : static_cast<uint32_t>(col) * b_row + 16u * piece +
+                         (split && piece >= 2 ? static_cast<uint32_t>(K / 4 - 32) : 0u);
   }
   const rsrc_t b_rsrc = make_rsrc(B + static_cast<size_t>(n0) * b_row, static_cast<uint32_t>(rows_n) * b_row);
-  // Scales: slot of 8 steps, 32 bytes per column.  Instruction j of wave w
-  // (4-byte pieces) covers columns 8q .. 8q + 7, q = 4w + j; lane l lands in
-  // column 8q + l / 8, LDS piece (l % 8) / 4 (16-byte), holding global piece
-  // ((l % 8) / 4) ^ ((col >> 3) & 1).
+  // Scales: slot of 8 steps, 32 bytes per column (split: of 4 steps, 16 bytes
+  // for each half of K).  Instruction j of wave w (4-byte pieces) covers
+  // columns 8q .. 8q + 7, q = 4w + j; lane l lands in column 8q + l / 8, LDS
+  // piece (l % 8) / 4 (16-byte), holding global piece ((l % 8) / 4) ^
+  // ((col >> 3) & 1).
   const uint32_t s_row = FP8 ? static_cast<uint32_t>(cols) * 4u : static_cast<uint32_t>(cols);
   uint32_t s_off[4];
 #pragma unroll
@@ -366,39 +376,41 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
     const int col = 8 * (4 * wave + j) + (lane >> 3);
     const int d = lane & 7;
     const int piece = (d >> 2) ^ ((col >> 3) & 1);
-    s_off[j] = static_cast<uint32_t>(col) * s_row + 16u * piece + 4u * (d & 3);
+    s_off[j] = static_cast<uint32_t>(col) * s_row + 4u * (d & 3) +
+               (split ? static_cast<uint32_t>(piece * (K / 32)) : 16u * piece);
   }
   const rsrc_t s_rsrc = make_rsrc(scales + static_cast<size_t>(n0) * s_row, static_cast<uint32_t>(rows_n) * s_row);
   const int spb = FP8 ? bs / BK : 1;  // steps per FP8 scale block (block_size % 64 == 0)
   // FP8: first scale column of the slot holding steps 8c .. 8c + 7
   auto slot_col = [&](int c) { return min(kScaleSteps * c / spb, cols - 1); };
 
-  const int nsteps = K / BK;
+  const int nsteps = split ? K / (2 * BK) : K / BK;
+  const int sl = split ? kScaleSteps / 2 : kScaleSteps;  // steps per scale slot
   // loads a wave issues for step u: activations, weights (FP4: at even steps,
-  // for the pair), scales (at the first step of each slot)
-  auto loads_for = [](int u) { return 4 + (FP8 ? 2 : ((u & 1) ? 0 : 2)) + (u % kScaleSteps == 0 ? 4 : 0); };
-  auto issue = [&](int u) {
-    T* a_dst = L.a[u % 3];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) load_lds16(A + a_off[j] + u * BK, &a_dst[(8 * j + wave) * 8 * kLdsRow]);
-    if constexpr (FP8) {
-      uint8_t* b_dst = L.b[u % 3];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) load_lds16(B + b_off[j] + static_cast<size_t>(u) * BK, &b_dst[(8 * j + wave) * 1024]);
-    } else {
-      if ((u & 1) == 0) {
-        uint8_t* b_dst = L.b[(u >> 1) & 1];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) buf_load_lds<16>(b_rsrc, b_off[j] + 32u * u, &b_dst[(8 * j + wave) * 1024]);
+  // for the pair; split: every step), scales (at the first step of each slot)
+  auto loads_for = [&](int u) { return 4 + (FP8 || split ? 2 : ((u & 1) ? 0 : 2)) + (u % sl == 0 ? 4 : 0); };
+  // part p (0 .. 3) of this wave's loads of step u
+  auto issue_part = [&](int u, int p) {
+    load_lds16(A + a_off[p] + u * BK, &L.a[u % 3][(8 * p + wave) * 8 * kLdsRow]);
+    if (p < 2) {
+      if constexpr (FP8) {
+        load_lds16(B + b_off[p] + static_cast<size_t>(u) * BK, &L.b[u % 3][(8 * p + wave) * 1024]);
+      } else {
+        if (split)
+          buf_load_lds<16>(b_rsrc, b_off[p] + 32u * u, &L.b[u % 3][(8 * p + wave) * 1024]);
+        else if ((u & 1) == 0)
+          buf_load_lds<16>(b_rsrc, b_off[p] + 32u * u, &L.b[(u >> 1) & 1][(8 * p + wave) * 1024]);
       }
     }
-    if (u % kScaleSteps == 0) {
-      const int c = u / kScaleSteps;
-      uint8_t* s_dst = L.s[c & 1];
-      const uint32_t base = FP8 ? 4u * static_cast<uint32_t>(slot_col(c)) : 32u * static_cast<uint32_t>(c);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) buf_load_lds<4>(s_rsrc, s_off[j] + base, &s_dst[(4 * wave + j) * 256]);
+    if (u % sl == 0) {
+      const int c = u / sl;
+      const uint32_t base = FP8 ? 4u * static_cast<uint32_t>(slot_col(c)) : static_cast<uint32_t>(4 * sl * c);
+      buf_load_lds<4>(s_rsrc, s_off[p] + base, &L.s[c & 1][(4 * wave + p) * 256]);
     }
+  };
+  auto issue = [&](int u) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) issue_part(u, p);
   };
 
   // lane (c32, h): column c32 of each 32-wide N tile, k half h of every step
@@ -411,9 +423,10 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto compute = [&](int u) {
+  // the MFMAs of step u; the loads of step ul, if any, are spread over them
+  auto compute = [&](int u, bool load, int ul) {
     const T* a_src = L.a[u % 3];
-    const uint8_t* s_src = L.s[(u / kScaleSteps) & 1];
+    const uint8_t* s_src = L.s[(u / sl) & 1];
     // lane (c32, h): k 32h .. 32h + 31 of its 2 columns (FP4 16 bytes, FP8 32)
     u32x4 bw[2][FP8 ? 2 : 1];
     float sc[2][FP8 ? 1 : 2];
@@ -428,11 +441,13 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
         const int idx = min(u / spb, cols - 1) - slot_col(u / kScaleSteps);  // 0 .. 7
         sc[nt][0] = *reinterpret_cast<const float*>(&s_src[col * 32 + 16 * ((idx >> 2) ^ ss) + 4 * (idx & 3)]);
       } else {
-        bw[nt][0] = *reinterpret_cast<const u32x4*>(
-            &L.b[(u >> 1) & 1][col * 64 + 16 * ((2 * (u & 1) + h) ^ b_swz(col))]);
-        const int st8 = u % kScaleSteps;
+        // split: wave group wm takes half wm of K
+        const uint8_t* bp = split ? &L.b[u % 3][col * 64 + 16 * ((2 * wm + h) ^ b_swz(col))]
+                                  : &L.b[(u >> 1) & 1][col * 64 + 16 * ((2 * (u & 1) + h) ^ b_swz(col))];
+        bw[nt][0] = *reinterpret_cast<const u32x4*>(bp);
+        const int q = split ? wm : (u % kScaleSteps) >> 2;
         const uint32_t s2 = *reinterpret_cast<const uint16_t*>(
-            &s_src[col * 32 + 16 * ((st8 >> 2) ^ ss) + 4 * (st8 & 3) + 2 * h]);
+            &s_src[col * 32 + 16 * (q ^ ss) + 4 * (u & 3) + 2 * h]);
         sc[nt][0] = e4m3_to_f32<0>(s2);
         sc[nt][1] = e4m3_to_f32<1>(s2);
       }
@@ -456,6 +471,8 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
       for (int ms = 0; ms < 4; ++ms)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) acc[ms][nt] = mfma32<T>(aop[ms], bop[nt], acc[ms][nt]);
+      if (load) issue_part(ul, i);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -479,8 +496,7 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
   }
   for (int step = 0; step < nsteps; ++step) {
     const bool ahead = step + 2 < nsteps;
-    if (ahead) issue(step + 2);
-    compute(step);
+    compute(step, ahead, step + 2);
     if (ahead)
       wait_all_but(loads_for(step + 2));  // the tiles of step + 1 have landed
     else
@@ -492,6 +508,30 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
   // to T, is staged in LDS (the operand stages are free now) one 128-row half
   // at a time and written back in whole 16-byte row pieces; tiles on the
   // ragged edge, or outputs that are not 16-byte aligned, store element-wise.
+  if (split) {
+    // add the second half of K (wave group 1) to the first (wave group 0)
+    float* red = reinterpret_cast<float*>(&L);
+    if (wm == 1) {
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            red[(32 * ms + 8 * (r >> 2) + 4 * h + (r & 3)) * L_BN + 64 * wn + 32 * nt + c32] = acc[ms][nt][r];
+    }
+    __syncthreads();
+    if (wm == 0) {
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            acc[ms][nt][r] += red[(32 * ms + 8 * (r >> 2) + 4 * h + (r & 3)) * L_BN + 64 * wn + 32 * nt + c32];
+    }
+    __syncthreads();
+  }
   const float ws2 = FP8 ? 1.0f : *ws2p;
   constexpr int kOutPitch = L_BN + 8;  // elements per staged row (breaks bank aliasing)
   T* out = reinterpret_cast<T*>(&L.a[0][0]);
@@ -504,6 +544,7 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
   }
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
+    if (split && half == 1) break;
     if (wm == half) {
 #pragma unroll
       for (int ms = 0; ms < 4; ++ms)
@@ -564,14 +605,44 @@ int launch_large(const MatmulArgs& a) {
       static_cast<int64_t>(L_BM) * a.K >= (int64_t(1) << 31) || a.M * a.K >= (int64_t(1) << 31))
     return launch<T, FP8>(a);
   const int64_t tiles_m = (a.M + L_BM - 1) / L_BM, tiles_n = (a.N + L_BN - 1) / L_BN;
-  if (tiles_m * tiles_n > 0x7fffffff) return -1;
-  hipLaunchKernelGGL((gemm_large_kernel<T, FP8>), dim3(static_cast<unsigned>(tiles_m * tiles_n)), dim3(512), 0,
-                     static_cast<hipStream_t>(a.stream), static_cast<const T*>(a.A), a.B,
-                     static_cast<const uint8_t*>(a.scales), a.ws2, static_cast<const T*>(a.bias),
-                     static_cast<T*>(a.Y), static_cast<int>(a.M), static_cast<int>(a.N), static_cast<int>(a.K),
-                     static_cast<int>(a.scale_cols), static_cast<int>(a.block_size), static_cast<int>(tiles_m),
-                     static_cast<int>(tiles_n));
+  const int64_t ntiles = tiles_m * tiles_n;
+  if (ntiles > 0x3fffffff) return -1;
+  // The tiles of a last, partial round (at most half the CUs' worth) go to a
+  // second launch that splits each of them over two workgroups, so that
+  // round takes half as long (FP4, K % 128 == 0).
+  const int64_t cus = device_cus(), rest = ntiles % cus;
+  const bool split = !FP8 && a.K % (2 * BK) == 0 && rest > 0 && 2 * rest <= cus;
+  const int64_t n_full = split ? ntiles - rest : ntiles;
+  const hipStream_t st = static_cast<hipStream_t>(a.stream);
+  const T* A = static_cast<const T*>(a.A);
+  const uint8_t* S = static_cast<const uint8_t*>(a.scales);
+  const T* bias = static_cast<const T*>(a.bias);
+  T* Y = static_cast<T*>(a.Y);
+  const int M = static_cast<int>(a.M), N = static_cast<int>(a.N), K = static_cast<int>(a.K);
+  const int cols = static_cast<int>(a.scale_cols), bs = static_cast<int>(a.block_size);
+  if (n_full > 0)
+    hipLaunchKernelGGL((gemm_large_kernel<T, FP8, false>), dim3(static_cast<unsigned>(n_full)), dim3(512), 0, st, A,
+                       a.B, S, a.ws2, bias, Y, M, N, K, cols, bs, static_cast<int>(tiles_m),
+                       static_cast<int>(tiles_n), 0);
+  if constexpr (!FP8) {
+    if (split)
+      hipLaunchKernelGGL((gemm_large_kernel<T, false, true>), dim3(static_cast<unsigned>(2 * rest)), dim3(512), 0,
+                         st, A, a.B, S, a.ws2, bias, Y, M, N, K, cols, bs, static_cast<int>(tiles_m),
+                         static_cast<int>(tiles_n), static_cast<int>(n_full));
+  }
   return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int device_cus() {
+  static int cus = -1;
+  if (cus < 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
+      v = 256;
+    cus = v;
+  }
+  return cus;
 }
 
 int launch_fp4_gemm(const MatmulArgs& a) {

@@ -55,6 +55,10 @@ struct QdqArgs {
 // an error at enqueue time.  Preconditions (checked by the dispatcher, never
 // by the launcher) are stated next to each.
 
+// compute units of the device current at the first call (cached for the
+// process; 256 if the query fails)
+int device_cus();
+
 // 1 <= M <= 8, block_size == 16, K % 128 == 0, scale_cols == K / 16,
 // A / B 16-byte aligned, scales 4-byte aligned, bias 2-byte aligned.
 int launch_fp4_gemv(const MatmulArgs& a);

@@ -371,18 +371,6 @@ constexpr int sk_depth() {
   return MT == 1 ? 4 : (MT == 2 ? 3 : 1);
 }
 
-int sk_num_cus() {
-  static int cus = -1;
-  if (cus < 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
-      v = 256;
-    cus = v;
-  }
-  return cus;
-}
-
 template <bool FP8, int MT>
 constexpr size_t sk_lds() {
   return static_cast<size_t>(kSkWaves) * sk_lds_per_wave<FP8, sk_depth<MT>()>();
@@ -407,7 +395,7 @@ int sk_slots() {
                                                    64 * kSkWaves, sk_lds<FP8, MT>()) != hipSuccess ||
       v < 1)
     v = 1;
-  return v * sk_num_cus();
+  return v * device_cus();
 }
 
 struct SkPlan {
