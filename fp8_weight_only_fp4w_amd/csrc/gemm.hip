@@ -8,7 +8,9 @@
 // scratch is written or re-read, and the tensor scale and bias are applied in
 // the epilogue.
 //
-// Tiling (gfx950, wave64):
+// Two kernels: gemm_large_kernel (below; every shape whose offsets fit in 32
+// bits) and gemm_kernel, the fallback for larger matrices.  gemm_kernel's
+// tiling (gfx950, wave64):
 //  * workgroup tile (128 WM) (M) x 256 (N) x 64 (K per step), WM x 4 waves,
 //    each wave 128 x 64 = 8 x 4 tiles of v_mfma_f32_16x16x32 (FP4: WM = 2,
 //    two waves per SIMD; FP8: WM = 1, one wave per SIMD, whose 512 registers
@@ -229,10 +231,10 @@ __global__ __launch_bounds__(256 * WM) void gemm_kernel(
 }
 
 // Prefill GEMM, large tiles (FP4 and FP8).  Workgroup 256 (M) x 256 (N) x
-// 64 (K per step), 8 waves in a 2 (M) x 4 (N) grid, each wave 128 x 64 = 8 x 4
-// tiles of v_mfma_f32_16x16x32 (128 FP32 accumulators per lane), two waves
-// per SIMD: a wave's weight decode (vector ALU) runs while the other wave's
-// MFMAs occupy the matrix core (one wave alone does not overlap the two).
+// 64 (K per step), 8 waves in a 2 (M) x 4 (N) grid, each wave 128 x 64 = 4 x 2
+// tiles of v_mfma_f32_32x32x16 (128 FP32 accumulators per lane).  Waves w and
+// w + 4 share a SIMD: a wave's weight decode (vector ALU) runs while the
+// other wave's MFMAs occupy the matrix core.
 //  * Every operand tile moves global -> LDS by direct loads (no registers).
 //    What limits these loads is the number of L2 requests rather than their
 //    bytes: a request carries one piece of at most 64 bytes of a line, so a
@@ -250,19 +252,27 @@ __global__ __launch_bounds__(256 * WM) void gemm_kernel(
 //       column (32 E4M3 bytes, or 8 FP32 block scales starting at the first
 //       block of the slot).  Weight and scale slots are read through a
 //       buffer descriptor per tile, so pieces past the matrix read zeros.
-//    The tiles of step t + 2 are requested during step t; the only wait is,
-//    at the end of each step, for the tiles of step t + 1 (loads complete in
-//    order), then one barrier.  A slot is refilled only after the barrier
-//    that ends its last reader's step.
+//    The tiles of step t + 2 are requested during step t (FP4: spread over
+//    its MFMA groups); the only wait is, at the end of each step, for the
+//    tiles of step t + 1 (loads complete in order), then one barrier.  A slot
+//    is refilled only after the barrier that ends its last reader's step.
 //  * LDS layouts are XOR-swizzled in 16-byte pieces (applied on the global
 //    side, since one direct load writes its 64 lanes' data contiguously), so
 //    the operand reads of a 16-lane group hit distinct banks.
-//  * Lane (li, g) takes k 16g .. 16g + 15 of each step for both operands
-//    (one 16-element scale block), split in two 8-k halves over two MFMAs;
-//    the E4M3 scale is folded into the decoded BF16/FP16 operand (exact).
+//  * Lane (c, h) takes column c of each 32-wide N tile and k 32h .. 32h + 31
+//    of each step for both operands (FP4: two 16-element scale blocks, one
+//    16-byte LDS read); MFMA i of the step takes k 32h + 8i .. 32h + 8i + 7.
+//    The E4M3 scale is folded into the decoded BF16/FP16 operand (exact).
 //  * Tile order: workgroups are dispatched round-robin over the 8 XCDs, each
 //    with its own L2, so the workgroup index is remapped to give every XCD a
 //    contiguous range of tiles, walked in groups of 2 tile rows.
+//  * SPLIT (FP4): the tiles of a last round that would fill at most half the
+//    CUs are launched separately, two workgroups per tile, 128 rows each; the
+//    row-half-0 waves take the first half of K and the row-half-1 waves the
+//    second (stage rows 128 + r hold row r at k + K / 2; a weight slot holds
+//    one step of both halves, a scale slot 4 steps of both), and the halves
+//    are added through LDS before the epilogue.  That round then takes about
+//    half as long.
 constexpr int L_BM = 256, L_BN = 256;
 constexpr int kScaleSteps = 8;  // steps per scale slot
 
