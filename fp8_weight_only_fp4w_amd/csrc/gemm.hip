@@ -323,7 +323,6 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int li = lane & 15, g = lane >> 4;
   const int wm = wave >> 2, wn = wave & 3;
 
   // Whole tiles: workgroup b takes tile b (contiguous ranges per XCD, then
