@@ -396,7 +396,9 @@ def extra_w8a8(steps, warmup):
 def extra_mid_m(steps, warmup):
     """FP4 matmul through the default dispatch at prompt-chunk sizes M = 64 ..
     1024 (N = 17408, K = 5120): where the skinny kernel hands over to the
-    prefill GEMM, whose 256 x 256 tiles give these sizes few workgroups."""
+    prefill GEMM, whose 256 x 256 tiles give these sizes few workgroups (a
+    last round of at most half the CUs' worth of tiles is split over two
+    workgroups per tile)."""
     N, K = 17408, 5120
     B, ws = workloads.fp4_weights_on_device(N, K, 16, seed=11)
     ws2 = torch.tensor([2.0 ** -8], dtype=torch.float32, device="cuda")

@@ -34,7 +34,9 @@ FP4_CASES = [
     (8, 777, 1024, 16, "bf16", False, "ceil", [fw.PATH_FP4_GEMV, fw.PATH_FP4_GEMM]),
     (5, 65590, 128, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMV]),  # 2 tiles per wave, ragged N
     (9, 300, 128, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMM, fw.PATH_FP4_GENERIC]),
-    (300, 700, 640, 16, "fp16", True, "ceil", [fw.PATH_FP4_GEMM]),  # ragged M and N
+    # ragged M and N; 2 x 3 tiles and K % 128 == 0, so every tile is split over
+    # two workgroups (row halves, K halves added in LDS), one half past M
+    (300, 700, 640, 16, "fp16", True, "ceil", [fw.PATH_FP4_GEMM]),
     (513, 256, 64, 16, "bf16", False, "ceil", [fw.PATH_FP4_GEMM]),
     # 3 x 8 = 24 tiles of 256 x 256 (a multiple of 8: the XCD tile remap is
     # active), ragged M and N, an odd number of K steps; the last column tile
