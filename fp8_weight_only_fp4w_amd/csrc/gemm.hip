@@ -273,14 +273,33 @@ __global__ __launch_bounds__(256 * WM) void gemm_kernel(
 //    one step of both halves, a scale slot 4 steps of both), and the halves
 //    are added through LDS before the epilogue.  That round then takes about
 //    half as long.
-constexpr int L_BM = 256, L_BN = 256;
+constexpr int L_BM = 256;       // most rows of an activation stage
 constexpr int kScaleSteps = 8;  // steps per scale slot
+
+// Tile shapes.  FP8: 256 x 256 output tiles, 2 (M) x 4 (N) waves.  FP4:
+// 128 x 512 output tiles, 1 x 8 waves (half the activation bytes per step of
+// the 256 x 256 shape, for twice the packed weight bytes, which are 4 times
+// smaller per element).  FP4 split: one workgroup takes 256 columns of a
+// 128 x 512 tile with its two wave groups on the two halves of K.
+template <bool FP8, bool SPLIT>
+struct LargeShape {
+  static constexpr bool kWide = !FP8 && !SPLIT;
+  static constexpr int kTM = FP8 ? 256 : 128;       // output rows of a tile
+  static constexpr int kTN = FP8 ? 256 : 512;       // output columns of a tile
+  static constexpr int kSR = kWide ? 128 : 256;     // rows of an activation stage
+  static constexpr int kSC = kWide ? 512 : 256;     // columns of a workgroup (weight and scale slots)
+  static constexpr int kAL = kSR / 64;              // activation loads per wave and step
+  static constexpr int kBL = kSC / 128;             // weight loads per wave and slot
+  static constexpr int kSL = kSC / 64;              // scale loads per wave and slot
+  static constexpr int kGM = FP8 ? 2 : 8;           // tile rows per group of the tile order
+};
 
 template <typename T, bool FP8, bool SPLIT>
 struct LargeLds {
-  T a[3][L_BM * kLdsRow];                        // 3 x 32 KiB
-  uint8_t b[FP8 || SPLIT ? 3 : 2][L_BN * 64];    // FP8: 3 steps; FP4: 2 slots of 2 steps; split: 3 steps (16 KiB each)
-  uint8_t s[2][L_BN * 32];             // 2 x 8 KiB
+  typedef LargeShape<FP8, SPLIT> Sh;
+  T a[3][Sh::kSR * kLdsRow];                      // 3 x 32 KiB (FP4 whole tiles: 3 x 16 KiB)
+  uint8_t b[FP8 || SPLIT ? 3 : 2][Sh::kSC * 64];  // FP8: 3 steps; FP4: 2 slots of 2 steps; split: 3 steps
+  uint8_t s[2][Sh::kSC * 32];                     // 2 slots
 };
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -319,37 +338,39 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
   typedef ActTraits<T> Tr;
   typedef typename Tr::vec8 V;
   __shared__ __attribute__((aligned(16))) LargeLds<T, FP8, SPLIT> L;
+  typedef LargeShape<FP8, SPLIT> Sh;
   constexpr bool split = SPLIT;
+  constexpr int SC = Sh::kSC;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = Sh::kWide ? 0 : wave >> 2, wn = Sh::kWide ? wave : wave & 3;
 
   // Whole tiles: workgroup b takes tile b (contiguous ranges per XCD, then
   // groups of GM tile rows).  Split launch (tiles t_first ..): two workgroups
-  // take 128 rows each of one tile, and their two wave groups take the two
+  // take 256 columns each of one tile, and their two wave groups take the two
   // halves of K, which are added through LDS at the end.
   int t = blockIdx.x;
   if (SPLIT)
     t = t_first + t / 2;
   else if (gridDim.x % 8 == 0)
     t = (t % 8) * (gridDim.x / 8) + t / 8;
-  constexpr int GM = 2;
+  constexpr int GM = Sh::kGM;
   const int per_group = GM * tiles_n;
   const int first_m = (t / per_group) * GM;
   const int gsize = min(tiles_m - first_m, GM);
   const int tm = first_m + (t % per_group) % gsize;
   const int tn = (t % per_group) / gsize;
-  const int m0 = tm * L_BM + (SPLIT ? 128 * (blockIdx.x & 1) : 0), n0 = tn * L_BN;
-  const int rows_n = min(L_BN, N - n0);  // weight / scale rows of this tile
+  const int m0 = tm * Sh::kTM, n0 = tn * Sh::kTN + (SPLIT ? 256 * (blockIdx.x & 1) : 0);
+  const int rows_n = max(min(SC, N - n0), 0);  // weight / scale rows of this workgroup
 
   // Activations: instruction j of wave w writes rows 8q .. 8q + 7 of the
   // stage, q = 8j + w; lane l lands in row 8q + l / 8, LDS chunk l % 8, which
   // holds global chunk (l % 8) ^ lds_swz(row).  Split: stage rows 128 + r hold
   // tile row r in the second half of K.
-  int a_off[4];
+  int a_off[Sh::kAL];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < Sh::kAL; ++j) {
     const int row = 8 * (8 * j + wave) + (lane >> 3);
     const int chunk = (lane & 7) ^ lds_swz(row);
     a_off[j] = split ? min(m0 + (row & 127), M - 1) * K + (row >> 7) * (K / 2) + 8 * chunk
@@ -363,9 +384,9 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
   // bytes per column): the same.
   const uint32_t b_row = FP8 ? static_cast<uint32_t>(K) : static_cast<uint32_t>(K / 2);
   auto b_swz = [](int col) { return (col >> 2) & 3; };
-  uint32_t b_off[2];  // FP4: byte offset in the tile's descriptor; FP8: global byte offset
+  uint32_t b_off[Sh::kBL];  // FP4: byte offset in the tile's descriptor; FP8: global byte offset
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < Sh::kBL; ++j) {
     const int col = 16 * (8 * j + wave) + (lane >> 2);
     const int piece = (lane & 3) ^ b_swz(col);
     b_off[j] = FP8 ? static_cast<uint32_t>(min(n0 + col, N - 1)) * b_row + 16u * piece
@@ -375,14 +396,14 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
   const rsrc_t b_rsrc = make_rsrc(B + static_cast<size_t>(n0) * b_row, static_cast<uint32_t>(rows_n) * b_row);
   // Scales: slot of 8 steps, 32 bytes per column (split: of 4 steps, 16 bytes
   // for each half of K).  Instruction j of wave w (4-byte pieces) covers
-  // columns 8q .. 8q + 7, q = 4w + j; lane l lands in column 8q + l / 8, LDS
+  // columns 8q .. 8q + 7, q = kSL w + j; lane l lands in column 8q + l / 8, LDS
   // piece (l % 8) / 4 (16-byte), holding global piece ((l % 8) / 4) ^
   // ((col >> 3) & 1).
   const uint32_t s_row = FP8 ? static_cast<uint32_t>(cols) * 4u : static_cast<uint32_t>(cols);
-  uint32_t s_off[4];
+  uint32_t s_off[Sh::kSL];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int col = 8 * (4 * wave + j) + (lane >> 3);
+  for (int j = 0; j < Sh::kSL; ++j) {
+    const int col = 8 * (Sh::kSL * wave + j) + (lane >> 3);
     const int d = lane & 7;
     const int piece = (d >> 2) ^ ((col >> 3) & 1);
     s_off[j] = static_cast<uint32_t>(col) * s_row + 4u * (d & 3) +
@@ -397,11 +418,13 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
   const int sl = split ? kScaleSteps / 2 : kScaleSteps;  // steps per scale slot
   // loads a wave issues for step u: activations, weights (FP4: at even steps,
   // for the pair; split: every step), scales (at the first step of each slot)
-  auto loads_for = [&](int u) { return 4 + (FP8 || split ? 2 : ((u & 1) ? 0 : 2)) + (u % sl == 0 ? 4 : 0); };
+  auto loads_for = [&](int u) {
+    return Sh::kAL + (FP8 || split ? Sh::kBL : ((u & 1) ? 0 : Sh::kBL)) + (u % sl == 0 ? Sh::kSL : 0);
+  };
   // part p (0 .. 3) of this wave's loads of step u
   auto issue_part = [&](int u, int p) {
-    load_lds16(A + a_off[p] + u * BK, &L.a[u % 3][(8 * p + wave) * 8 * kLdsRow]);
-    if (p < 2) {
+    if (p < Sh::kAL) load_lds16(A + a_off[p] + u * BK, &L.a[u % 3][(8 * p + wave) * 8 * kLdsRow]);
+    if (p < Sh::kBL) {
       if constexpr (FP8) {
         load_lds16(B + b_off[p] + static_cast<size_t>(u) * BK, &L.b[u % 3][(8 * p + wave) * 1024]);
       } else {
@@ -414,7 +437,10 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
     if (u % sl == 0) {
       const int c = u / sl;
       const uint32_t base = FP8 ? 4u * static_cast<uint32_t>(slot_col(c)) : static_cast<uint32_t>(4 * sl * c);
-      buf_load_lds<4>(s_rsrc, s_off[p] + base, &L.s[c & 1][(4 * wave + p) * 256]);
+      constexpr int kPer = Sh::kSL / 4;
+#pragma unroll
+      for (int j = kPer * p; j < kPer * (p + 1); ++j)
+        buf_load_lds<4>(s_rsrc, s_off[j] + base, &L.s[c & 1][(Sh::kSL * wave + j) * 256]);
     }
   };
   auto issue = [&](int u) {
@@ -488,10 +514,10 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
   // wait for everything but the n loads of the newest step, then barrier
   auto wait_all_but = [](int n) {
     switch (n) {
-      case 4: wait_barrier<4>(); break;
+      case 2: wait_barrier<2>(); break;
       case 6: wait_barrier<6>(); break;
-      case 8: wait_barrier<8>(); break;
       case 10: wait_barrier<10>(); break;
+      case 14: wait_barrier<14>(); break;
       default: wait_barrier<0>(); break;
     }
   };
@@ -515,11 +541,12 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
       wait_barrier<0>();
   }
 
-  // Epilogue: lane (li, g) holds columns 64 wn + 16 ns + li and rows
-  // 128 wm + 16 ms + 4 g + r of the tile.  Y = acc * ws2 + bias, rounded once
-  // to T, is staged in LDS (the operand stages are free now) one 128-row half
-  // at a time and written back in whole 16-byte row pieces; tiles on the
-  // ragged edge, or outputs that are not 16-byte aligned, store element-wise.
+  // Epilogue: lane (c, h) holds columns 64 wn + 32 nt + c and rows
+  // 128 wm + 32 ms + 8 (r / 4) + 4 h + r % 4 of the workgroup's block.
+  // Y = acc * ws2 + bias, rounded once to T, is staged in LDS (the operand
+  // stages are free now) one 128-row half at a time and written back in whole
+  // 16-byte row pieces; blocks on the ragged edge, or outputs that are not
+  // 16-byte aligned, store element-wise.
   if (split) {
     // add the second half of K (wave group 1) to the first (wave group 0)
     float* red = reinterpret_cast<float*>(&L);
@@ -530,7 +557,7 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            red[(32 * ms + 8 * (r >> 2) + 4 * h + (r & 3)) * L_BN + 64 * wn + 32 * nt + c32] = acc[ms][nt][r];
+            red[(32 * ms + 8 * (r >> 2) + 4 * h + (r & 3)) * SC + 64 * wn + 32 * nt + c32] = acc[ms][nt][r];
     }
     __syncthreads();
     if (wm == 0) {
@@ -540,14 +567,15 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            acc[ms][nt][r] += red[(32 * ms + 8 * (r >> 2) + 4 * h + (r & 3)) * L_BN + 64 * wn + 32 * nt + c32];
+            acc[ms][nt][r] += red[(32 * ms + 8 * (r >> 2) + 4 * h + (r & 3)) * SC + 64 * wn + 32 * nt + c32];
     }
     __syncthreads();
   }
   const float ws2 = FP8 ? 1.0f : *ws2p;
-  constexpr int kOutPitch = L_BN + 8;  // elements per staged row (breaks bank aliasing)
-  T* out = reinterpret_cast<T*>(&L.a[0][0]);
-  const bool wide = (N % 8 == 0) && (reinterpret_cast<uintptr_t>(Y) % 16 == 0) && n0 + L_BN <= N;
+  constexpr int kOutPitch = SC + 8;  // elements per staged row (breaks bank aliasing)
+  static_assert(sizeof(L) >= 128 * kOutPitch * sizeof(T), "output staging exceeds LDS");
+  T* out = reinterpret_cast<T*>(&L);
+  const bool wide = (N % 8 == 0) && (reinterpret_cast<uintptr_t>(Y) % 16 == 0) && n0 + SC <= N;
   float bsum[2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
@@ -555,8 +583,7 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
     bsum[nt] = bias ? static_cast<float>(bias[n]) : 0.0f;
   }
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    if (split && half == 1) break;
+  for (int half = 0; half < Sh::kTM / 128; ++half) {
     if (wm == half) {
 #pragma unroll
       for (int ms = 0; ms < 4; ++ms)
@@ -570,18 +597,18 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
     __syncthreads();
     const int mrow0 = m0 + 128 * half;
     if (wide) {
-      // 128 rows x 32 pieces of 16 bytes, 8 per thread
+      // 128 rows x SC / 8 pieces of 16 bytes
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < SC / 32; ++i) {
         const int q = tid + 512 * i;
-        const int row = q >> 5, piece = q & 31;
+        const int row = q / (SC / 8), piece = q % (SC / 8);
         if (mrow0 + row < M)
           *reinterpret_cast<u32x4*>(&Y[static_cast<size_t>(mrow0 + row) * N + n0 + 8 * piece]) =
               *reinterpret_cast<const u32x4*>(&out[row * kOutPitch + 8 * piece]);
       }
     } else {
-      for (int q = tid; q < 128 * L_BN; q += 512) {
-        const int row = q / L_BN, col = q % L_BN;
+      for (int q = tid; q < 128 * SC; q += 512) {
+        const int row = q / SC, col = q % SC;
         if (mrow0 + row < M && n0 + col < N)
           Y[static_cast<size_t>(mrow0 + row) * N + n0 + col] = out[row * kOutPitch + col];
       }
@@ -616,7 +643,8 @@ int launch_large(const MatmulArgs& a) {
   if (b_bytes >= (int64_t(1) << 31) || a.N * a.scale_cols >= (int64_t(1) << 31) ||
       static_cast<int64_t>(L_BM) * a.K >= (int64_t(1) << 31) || a.M * a.K >= (int64_t(1) << 31))
     return launch<T, FP8>(a);
-  const int64_t tiles_m = (a.M + L_BM - 1) / L_BM, tiles_n = (a.N + L_BN - 1) / L_BN;
+  typedef LargeShape<FP8, false> Sh;
+  const int64_t tiles_m = (a.M + Sh::kTM - 1) / Sh::kTM, tiles_n = (a.N + Sh::kTN - 1) / Sh::kTN;
   const int64_t ntiles = tiles_m * tiles_n;
   if (ntiles > 0x3fffffff) return -1;
   // The tiles of a last, partial round (at most half the CUs' worth) go to a
