@@ -230,11 +230,14 @@ __global__ __launch_bounds__(256 * WM) void gemm_kernel(
   }
 }
 
-// Prefill GEMM, large tiles (FP4 and FP8).  Workgroup 256 (M) x 256 (N) x
-// 64 (K per step), 8 waves in a 2 (M) x 4 (N) grid, each wave 128 x 64 = 4 x 2
-// tiles of v_mfma_f32_32x32x16 (128 FP32 accumulators per lane).  Waves w and
-// w + 4 share a SIMD: a wave's weight decode (vector ALU) runs while the
-// other wave's MFMAs occupy the matrix core.
+// Prefill GEMM, large tiles (FP4 and FP8).  Workgroup tile 128 (M) x 512 (N)
+// for FP4 with 8 waves side by side in N, 256 x 256 for FP8 with 8 waves in a
+// 2 (M) x 4 (N) grid; 64 K per step.  Each wave holds 128 x 64 = 4 x 2 tiles
+// of v_mfma_f32_32x32x16 (128 FP32 accumulators per lane).  Waves w and w + 4
+// share a SIMD: a wave's weight decode (vector ALU) runs while the other
+// wave's MFMAs occupy the matrix core.  The FP4 shape moves half the
+// activation bytes per step of the square one, for twice the packed weight
+// bytes, which are a quarter of the size per element.
 //  * Every operand tile moves global -> LDS by direct loads (no registers).
 //    What limits these loads is the number of L2 requests rather than their
 //    bytes: a request carries one piece of at most 64 bytes of a line, so a
@@ -243,8 +246,8 @@ __global__ __launch_bounds__(256 * WM) void gemm_kernel(
 //    kernel took more load time than the activation tiles, which are 80 % of
 //    the bytes).  So each operand is loaded in the largest contiguous pieces
 //    its layout allows:
-//     - activations: ring of 3 one-step stages [256 rows][64] of T (rows of
-//       128 contiguous bytes);
+//     - activations: ring of 3 one-step stages [rows][64] of T (rows of 128
+//       contiguous bytes);
 //     - FP4 weights: ring of 2 slots of two steps each, 64 contiguous bytes
 //       per column; FP8 weights: ring of 3 one-step stages, 64 bytes per
 //       column;
@@ -265,14 +268,13 @@ __global__ __launch_bounds__(256 * WM) void gemm_kernel(
 //    The E4M3 scale is folded into the decoded BF16/FP16 operand (exact).
 //  * Tile order: workgroups are dispatched round-robin over the 8 XCDs, each
 //    with its own L2, so the workgroup index is remapped to give every XCD a
-//    contiguous range of tiles, walked in groups of 2 tile rows.
+//    contiguous range of tiles, walked in groups of tile rows (FP8 2, FP4 8).
 //  * SPLIT (FP4): the tiles of a last round that would fill at most half the
-//    CUs are launched separately, two workgroups per tile, 128 rows each; the
-//    row-half-0 waves take the first half of K and the row-half-1 waves the
-//    second (stage rows 128 + r hold row r at k + K / 2; a weight slot holds
-//    one step of both halves, a scale slot 4 steps of both), and the halves
-//    are added through LDS before the epilogue.  That round then takes about
-//    half as long.
+//    CUs are launched separately, two workgroups per tile, 256 columns each;
+//    waves 0-3 take the first half of K and waves 4-7 the second (stage rows
+//    128 + r hold row r at k + K / 2; a weight slot holds one step of both
+//    halves, a scale slot 4 steps of both), and the halves are added through
+//    LDS before the epilogue.  That round then takes about half as long.
 constexpr int L_BM = 256;       // most rows of an activation stage
 constexpr int kScaleSteps = 8;  // steps per scale slot
 
