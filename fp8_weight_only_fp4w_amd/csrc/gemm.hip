@@ -253,8 +253,10 @@ __global__ __launch_bounds__(256 * WM) void gemm_kernel(
 //       column;
 //     - scales: ring of 2 slots of eight steps each, 32 contiguous bytes per
 //       column (32 E4M3 bytes, or 8 FP32 block scales starting at the first
-//       block of the slot).  Weight and scale slots are read through a
-//       buffer descriptor per tile, so pieces past the matrix read zeros.
+//       block of the slot).
+//    Every load goes through a buffer descriptor (32-bit offsets, cheaper to
+//    issue than 64-bit addresses); the weight and scale descriptors cover the
+//    workgroup's columns, so pieces past the matrix read zeros.
 //    The tiles of step t + 2 are requested during step t (FP4: spread over
 //    its MFMA groups); the only wait is, at the end of each step, for the
 //    tiles of step t + 1 (loads complete in order), then one barrier.  A slot
@@ -313,11 +315,6 @@ __device__ __forceinline__ f32x16 mfma32(typename ActTraits<T>::vec8 a, typename
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   else
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-
-// direct 16-byte global -> LDS load: lane l writes lds + 16 l
-__device__ __forceinline__ void load_lds16(const void* gptr, void* lds) {
-  __builtin_amdgcn_global_load_lds(gptr, (lds_ptr_t)(lds), 16, 0, 0);
 }
 
 // wait until at most N vector-memory loads are in flight and every LDS access
@@ -384,16 +381,18 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
   // 16q .. 16q + 15, q = 8j + w; lane l lands in column 16q + l / 4, LDS piece
   // l % 4, holding global piece (l % 4) ^ ((col >> 2) & 3).  FP8 stage (64
   // bytes per column): the same.
+  // all loads go through buffer descriptors (32-bit offsets; cheaper to
+  // issue than 64-bit addresses: 2-4 % on this kernel)
+  const rsrc_t a_rsrc = make_rsrc(A, static_cast<uint32_t>(M) * static_cast<uint32_t>(K) * 2u);
   const uint32_t b_row = FP8 ? static_cast<uint32_t>(K) : static_cast<uint32_t>(K / 2);
   auto b_swz = [](int col) { return (col >> 2) & 3; };
-  uint32_t b_off[Sh::kBL];  // FP4: byte offset in the tile's descriptor; FP8: global byte offset
+  uint32_t b_off[Sh::kBL];  // byte offset in the workgroup's descriptor
 #pragma unroll
   for (int j = 0; j < Sh::kBL; ++j) {
     const int col = 16 * (8 * j + wave) + (lane >> 2);
     const int piece = (lane & 3) ^ b_swz(col);
-    b_off[j] = FP8 ? static_cast<uint32_t>(min(n0 + col, N - 1)) * b_row + 16u * piece
-                   : static_cast<uint32_t>(col) * b_row + 16u * piece +
-                         (split && piece >= 2 ? static_cast<uint32_t>(K / 4 - 32) : 0u);
+    b_off[j] = static_cast<uint32_t>(col) * b_row + 16u * piece +
+               (split && piece >= 2 ? static_cast<uint32_t>(K / 4 - 32) : 0u);
   }
   const rsrc_t b_rsrc = make_rsrc(B + static_cast<size_t>(n0) * b_row, static_cast<uint32_t>(rows_n) * b_row);
   // Scales: slot of 8 steps, 32 bytes per column (split: of 4 steps, 16 bytes
@@ -425,10 +424,11 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
   };
   // part p (0 .. 3) of this wave's loads of step u
   auto issue_part = [&](int u, int p) {
-    if (p < Sh::kAL) load_lds16(A + a_off[p] + u * BK, &L.a[u % 3][(8 * p + wave) * 8 * kLdsRow]);
+    if (p < Sh::kAL)
+      buf_load_lds<16>(a_rsrc, 2u * static_cast<uint32_t>(a_off[p] + u * BK), &L.a[u % 3][(8 * p + wave) * 8 * kLdsRow]);
     if (p < Sh::kBL) {
       if constexpr (FP8) {
-        load_lds16(B + b_off[p] + static_cast<size_t>(u) * BK, &L.b[u % 3][(8 * p + wave) * 1024]);
+        buf_load_lds<16>(b_rsrc, b_off[p] + static_cast<uint32_t>(u * BK), &L.b[u % 3][(8 * p + wave) * 1024]);
       } else {
         if (split)
           buf_load_lds<16>(b_rsrc, b_off[p] + 32u * u, &L.b[u % 3][(8 * p + wave) * 1024]);
