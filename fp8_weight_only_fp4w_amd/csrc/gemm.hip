@@ -605,8 +605,9 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
         const int q = tid + 512 * i;
         const int row = q / (SC / 8), piece = q % (SC / 8);
         if (mrow0 + row < M)
-          *reinterpret_cast<u32x4*>(&Y[static_cast<size_t>(mrow0 + row) * N + n0 + 8 * piece]) =
-              *reinterpret_cast<const u32x4*>(&out[row * kOutPitch + 8 * piece]);
+          // non-temporal: Y is not read again here, keep A and B in the caches
+          __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&out[row * kOutPitch + 8 * piece]),
+                                      reinterpret_cast<u32x4*>(&Y[static_cast<size_t>(mrow0 + row) * N + n0 + 8 * piece]));
       }
     } else {
       for (int q = tid; q < 128 * SC; q += 512) {
