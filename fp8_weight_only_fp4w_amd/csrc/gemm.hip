@@ -677,14 +677,14 @@ int launch_large(const MatmulArgs& a) {
 }
 
 int device_cus() {
-  static int cus = -1;
-  if (cus < 0) {
+  // initialised once, thread-safely, on the first call
+  static const int cus = [] {
     int dev = 0, v = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
       v = 256;
-    cus = v;
-  }
+    return v;
+  }();
   return cus;
 }
 
