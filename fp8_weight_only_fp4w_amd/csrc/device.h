@@ -262,6 +262,9 @@ __device__ __forceinline__ uint32_t buf_load_u16(rsrc_t r, uint32_t off) {
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// LDS pointers for reads whose addresses are computed in 32 bits
+typedef __attribute__((address_space(3))) const unsigned char* lds_cbytes;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
 
 // Direct buffer -> LDS load of SIZE bytes per lane: lane l writes lds +
 // SIZE l (lds must be wave-uniform); offsets past the descriptor's range

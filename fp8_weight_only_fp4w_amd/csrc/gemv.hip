@@ -223,6 +223,17 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
       a_off[h] = static_cast<uint32_t>(valid ? m : 0) * (ACT_LDS ? lds_pitch : kStagePitch4) + 64u * g;
     }
   }
+  // ACT_LDS: the lane's LDS address of window 0 and its step per window; a
+  // lane that carries no row keeps reading the zero block (step 0), so the
+  // window loop computes each address with one multiply-add
+  // (32-bit LDS addresses)
+  lds_cbytes a_win0[FP8 ? 1 : R];
+  uint32_t a_wstep[FP8 ? 1 : R];
+#pragma unroll
+  for (int h = 0; h < (FP8 ? 1 : R); ++h) {
+    a_win0[h] = (lds_cbytes)(a_lds + (a_valid[h] ? a_off[h] : zero_off));
+    a_wstep[h] = a_valid[h] ? 256u : 0u;
+  }
   // ACT_REG: this wave's staging area, the lane's global offset (unit 0) in
   // the row-major loads and its place in the staging area.  FP4 load b:
   // rows 2b + (lane >> 5), 16 bytes at 16 (lane & 31) of the row's 512;
@@ -421,11 +432,15 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
         u32x4 av[R][4];
 #pragma unroll
         for (int h = 0; h < R; ++h) {
-          const unsigned char* q =
-              ACT_LDS ? a_lds + (a_valid[h] ? a_off[h] + 256u * wa : zero_off)
-                      : stage + (a_valid[h] ? a_off[h] + 256u * s2 : 4u * R * kStagePitch4);
+          if constexpr (ACT_LDS) {
+            const lds_cbytes q = a_win0[h] + __umul24(a_wstep[h], static_cast<uint32_t>(wa));
 #pragma unroll
-          for (int i = 0; i < 4; ++i) av[h][i] = *reinterpret_cast<const u32x4*>(q + 16u * i);
+            for (int i = 0; i < 4; ++i) av[h][i] = *reinterpret_cast<const lds_u32x4*>(q + 16u * i);
+          } else {
+            const unsigned char* q = stage + (a_valid[h] ? a_off[h] + 256u * s2 : 4u * R * kStagePitch4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) av[h][i] = *reinterpret_cast<const u32x4*>(q + 16u * i);
+          }
         }
         // weights of the lane: chunk 4 s2 + g of row li (32 codes); dword
         // 2s + p holds piece p of set s (block 2g + s)
