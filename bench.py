@@ -271,7 +271,8 @@ def extra_prefill_fp4(reps=10, warmup=3):
     t = time_calls([lambda: fw.fp4w_matmul(d["A"], d["B"][0], d["ws"][0], d["ws2"], None, 16, out=out)],
                    reps, warmup) / reps
     res = {"fused_ms": round(t * 1e3, 3), "fused_TFLOPs": round(flops / t / 1e12, 1),
-           "fused_frac_of_bf16_peak": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
+           "fused_frac_of_bf16_peak": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4),
+           "clocks_after_fused": read_clocks()}
     # baseline: dequant to a [N, K] scratch, then hipBLASLt (torch.matmul)
     scratch = torch.empty(p.N, p.K, dtype=torch.bfloat16, device="cuda")
 
@@ -465,6 +466,26 @@ def extra_decode_step(steps, warmup):
 
 # ------------------------------------------------------------------ profiling mode
 
+def read_clocks():
+    """Shader (per XCD) and memory clocks from amd-smi, run as a child
+    process right after a timed region; None where amd-smi is unavailable."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True, text=True,
+                           timeout=30)
+        data = json.loads(r.stdout)
+        gpu = data["gpu_data"][0] if isinstance(data, dict) else data[0]
+        clk = gpu["clock"]
+        val = lambda e, k: e.get(k, {}).get("value") if isinstance(e.get(k), dict) else None
+        gfx = [val(e, "clk") for k, e in sorted(clk.items()) if k.startswith("gfx")]
+        out = {"gfx_MHz": gfx, "gfx_max_MHz": next((val(e, "max_clk") for k, e in clk.items() if k.startswith("gfx")), None),
+               "mem_MHz": next((val(e, "clk") for k, e in clk.items() if k.startswith("mem")), None),
+               "source": "amd-smi metric -c, sampled right after a timed region"}
+        return out
+    except Exception as e:  # noqa: BLE001 - a missing tool only loses this record
+        return {"error": f"{type(e).__name__}: {e}"[:200]}
+
+
 def profile_kernel(which, launches=50):
     """Launch one kernel `launches` times without graphs, for rocprofv3 runs
     (kernel trace or PMC counters).  Weight copies rotate as in the timed runs."""
@@ -596,7 +617,7 @@ def main():
                 "kernel": "fp4_gemv_kernel (MFMA decode GEMV)",
                 "alg_bytes_per_launch": round(alg_per_launch), "mean_launch_us": round(mean_launch * 1e6, 3)}
 
-    extra = {"per_M": h["per_m"], "weight_copies": h["R"]}
+    extra = {"per_M": h["per_m"], "weight_copies": h["R"], "clocks": read_clocks()}
     if not args.no_extra:
         for name, fn in (("hbm_copy_GBps", hbm_copy_gbps),
                          ("fp4_gemv_small", lambda: extra_small_gemv(args.steps, args.warmup)),
