@@ -252,6 +252,59 @@ def hbm_copy_gbps():
     return round(2 * n * 20 / t / 1e9, 1)
 
 
+def hbm_read(weight_bytes):
+    """Measured HBM read rate from this repository's read-stream kernel
+    (libhbmprobe.so): the peak over a 4 GiB buffer, and the rate at the
+    headline's weight bytes per launch over 72 rotated slices (1.06 GB, past
+    the last-level cache) launched back to back from a HIP graph.  Each is the
+    best over grid sizes and loads in flight per thread."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "fp8_weight_only_fp4w_amd", "libhbmprobe.so"))
+    lib.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_uint32,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    lib.hbm_read_probe.restype = ctypes.c_int
+    grids, unrolls = (256, 512, 1024, 2048), (4, 8)
+    big_bytes = 4 << 30
+    buf = torch.full((big_bytes,), 1, dtype=torch.uint8, device="cuda")  # every thread's XOR is 0
+    sink = torch.empty(max(grids) * 512, dtype=torch.int32, device="cuda")
+    key = 0xFFFFFFFF  # never equal to a reduction of these bytes: nothing is stored
+
+    def launch(ptr, nbytes, grid, unroll):
+        rc = lib.hbm_read_probe(ctypes.c_void_p(ptr), nbytes, grid, unroll, key, ctypes.c_void_p(sink.data_ptr()),
+                                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hbm_read_probe failed ({rc})")
+
+    peak = {}
+    for g in grids:
+        for u in unrolls:
+            t = time_calls([lambda g=g, u=u: launch(buf.data_ptr(), big_bytes, g, u)], 10, 2)
+            peak[f"grid{g}_u{u}"] = round(big_bytes * 10 / t / 1e9, 1)
+    nb = weight_bytes - weight_bytes % 16
+    slices = 72
+    at_size = {}
+    for g in grids:
+        for u in unrolls:
+            def body(g=g, u=u):
+                for i in range(slices):
+                    launch(buf.data_ptr() + i * nb, nb, g, u)
+            body()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                body()
+            graph.replay()
+            torch.cuda.synchronize()
+            t = time_calls([graph.replay], 5, 1)
+            at_size[f"grid{g}_u{u}"] = round(nb * slices * 5 / t / 1e9, 1)
+    del buf, sink
+    best = max(peak.values())
+    best_sz = max(at_size.values())
+    return {"peak_GBps": best, "peak_config": max(peak, key=peak.get), "buffer_bytes": big_bytes,
+            "at_headline_size_GBps": best_sz, "at_headline_size_config": max(at_size, key=at_size.get),
+            "at_headline_size_bytes": nb, "sweep_4GiB": peak, "sweep_headline_size": at_size}
+
+
 def extra_small_gemv(steps, warmup):
     w = workloads.WORKLOADS["fp4_gemv_small"]
     p = w.make()
@@ -618,6 +671,12 @@ def main():
                 "alg_bytes_per_launch": round(alg_per_launch), "mean_launch_us": round(mean_launch * 1e6, 3)}
 
     extra = {"per_M": h["per_m"], "weight_copies": h["R"], "clocks": read_clocks()}
+    rd = hbm_read(h["weight_bytes"])
+    rd["headline_frac_of_peak"] = round(value / rd["peak_GBps"], 4)
+    rd["headline_frac_at_size"] = round(value / rd["at_headline_size_GBps"], 4)
+    extra["hbm_read"] = rd
+    torch.cuda.empty_cache()
+    log(f"hbm_read: {rd}")
     if not args.no_extra:
         for name, fn in (("hbm_copy_GBps", hbm_copy_gbps),
                          ("fp4_gemv_small", lambda: extra_small_gemv(args.steps, args.warmup)),

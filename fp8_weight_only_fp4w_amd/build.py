@@ -1,5 +1,6 @@
 """Build libfp4w.so in-tree: hipcc for the gfx950 kernels, g++ for the host
-dispatch, hipcc -shared for the link.
+dispatch, hipcc -shared for the link; and libhbmprobe.so, the bench's HBM
+read-stream probe.
 
     python -m fp8_weight_only_fp4w_amd.build [-v]
 """
@@ -14,6 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfp4w.so")
+PROBE_LIB = os.path.join(HERE, "libhbmprobe.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
@@ -75,6 +77,10 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    # the bench's HBM read-stream probe, a library of its own
+    tmp = PROBE_LIB + ".tmp"
+    _run([HIPCC, *HIP_FLAGS, "-shared", os.path.join(HERE, "probe", "hbm_read.hip"), "-o", tmp], verbose)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

@@ -35,6 +35,21 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_hbm_probe_library_exports_its_entry_point():
+    # the bench's read-stream probe is built beside the matmul library and
+    # exports nothing but its one entry point
+    import ctypes
+    import os
+    import subprocess
+    path = os.path.join(os.path.dirname(fw.LIB_PATH), "libhbmprobe.so")
+    assert os.path.exists(path), "build() also builds libhbmprobe.so"
+    lib = ctypes.CDLL(path)
+    assert hasattr(lib, "hbm_read_probe")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+    exported = sorted(line.split()[-1] for line in out.splitlines() if " T " in line)
+    assert exported == ["hbm_read_probe"], exported
+
+
 def test_status_and_path_strings():
     assert fw.fp4w_status_string(fw.OK) == "ok"
     for st in (fw.ERR_NULL, fw.ERR_SHAPE, fw.ERR_DTYPE, fw.ERR_BLOCK, fw.ERR_PATH, fw.ERR_LAUNCH, fw.ERR_ALIAS):
