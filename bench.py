@@ -694,6 +694,13 @@ def main():
             torch.cuda.empty_cache()
             log(f"{name}: {extra[name]} ({time.perf_counter() - t0:.1f} s)")
 
+    # the bandwidth-bound GEMV extras against the measured read peak
+    peak_rd = extra["hbm_read"]["peak_GBps"]
+    if "fp4_gemv_wide" in extra:
+        extra["fp4_gemv_wide"]["frac_of_measured_read_peak"] = round(extra["fp4_gemv_wide"]["weight_GBps"] / peak_rd, 4)
+    if "fp8" in extra:
+        extra["fp8"]["gemv_M4_frac_of_measured_read_peak"] = round(extra["fp8"]["gemv_M4_weight_GBps"] / peak_rd, 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline()
