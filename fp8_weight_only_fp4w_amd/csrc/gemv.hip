@@ -425,8 +425,11 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
       for (int s2 = 0; s2 < 2; ++s2) {
         const int w = 2 * u + s2;
         const int wa = min(w, NW - 1);  // windows past NW meet zero scales
-        const u32x2 sb = w < NW ? *reinterpret_cast<const u32x2*>(slice + kSlicePitch * li + 8 * (2 * (j % SU) + s2))
-                                : u32x2{0u, 0u};
+        // the slice bytes are always readable; a window past NW takes zero
+        // scales (a uniform mask instead of a branch)
+        const uint32_t keep = w < NW ? ~0u : 0u;
+        const u32x2 sr = *reinterpret_cast<const u32x2*>(slice + kSlicePitch * li + 8 * (2 * (j % SU) + s2));
+        const u32x2 sb = u32x2{sr.x & keep, sr.y & keep};
         // activations of the lane: 4 x 16 bytes per row half; chunk i = 2s + p
         // holds k 32g + 16s + 8p .. + 7 of the window (piece p of set s)
         u32x4 av[R][4];
