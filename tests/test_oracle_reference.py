@@ -135,15 +135,18 @@ def test_dequant_fp8_output_bits_vs_torch():
 # ------------------------------------------------------------ matmul pins
 
 def _brute_fp4(p):
-    """Exact rational Y for an Fp4Problem, with explicit loops."""
+    """Exact rational Y and S = sum_k |A * B_dq| for an Fp4Problem, with
+    explicit loops."""
     A = codecs.bits_to_f64(p.A, p.dtype)
     bias = None if p.bias is None else codecs.bits_to_f64(p.bias, p.dtype)
     cols = p.weight_scale.shape[1]
     ws2 = Fraction(float(np.float32(p.weight_scale_2)))
     Y = [[Fraction(0)] * p.N for _ in range(p.M)]
+    S = [[Fraction(0)] * p.N for _ in range(p.M)]
     for m in range(p.M):
         for n in range(p.N):
             acc = Fraction(0)
+            mag = Fraction(0)
             for k in range(p.K):
                 byte = int(p.B[n, k // 2])
                 code = byte & 0xF if k % 2 == 0 else byte >> 4
@@ -152,11 +155,14 @@ def _brute_fp4(p):
                     col = cols - 1
                 q = Fraction(codecs.e2m1_value(code))
                 s = Fraction(codecs.e4m3fn_value(int(p.weight_scale[n, col])))
-                acc += Fraction(float(A[m, k])) * q * s * ws2
+                term = Fraction(float(A[m, k])) * q * s * ws2
+                acc += term
+                mag += abs(term)
             if bias is not None:
                 acc += Fraction(float(bias[n]))
             Y[m][n] = acc
-    return Y
+            S[m][n] = mag
+    return Y, S
 
 
 def _brute_fp8(p):
@@ -164,24 +170,35 @@ def _brute_fp8(p):
     bias = None if p.bias is None else codecs.bits_to_f64(p.bias, p.dtype)
     cols = p.b_scale.shape[1]
     Y = [[Fraction(0)] * p.N for _ in range(p.M)]
+    S = [[Fraction(0)] * p.N for _ in range(p.M)]
     for m in range(p.M):
         for n in range(p.N):
             acc = Fraction(0)
+            mag = Fraction(0)
             for k in range(p.K):
                 col = min(k // p.block_size, cols - 1)
                 q = Fraction(codecs.e4m3fn_value(int(p.B[n, k])))
-                acc += Fraction(float(A[m, k])) * q * Fraction(float(p.b_scale[n, col]))
+                term = Fraction(float(A[m, k])) * q * Fraction(float(p.b_scale[n, col]))
+                acc += term
+                mag += abs(term)
             if bias is not None:
                 acc += Fraction(float(bias[n]))
             Y[m][n] = acc
-    return Y
+            S[m][n] = mag
+    return Y, S
 
 
 def _close(Y, S, exact, K):
+    """The oracle's Y and S against the exact rationals: Y within float64
+    accumulation error; S (the scale of every tolerance) likewise, so a slip
+    that inflates or shrinks it fails here."""
+    exact_Y, exact_S = exact
     for m in range(Y.shape[0]):
         for n in range(Y.shape[1]):
-            err = abs(Fraction(float(Y[m, n])) - exact[m][n])
-            assert err <= Fraction(K + 2) * Fraction(2.0 ** -52) * (Fraction(float(S[m, n])) + abs(exact[m][n])), (m, n)
+            err = abs(Fraction(float(Y[m, n])) - exact_Y[m][n])
+            assert err <= Fraction(K + 2) * Fraction(2.0 ** -52) * (exact_S[m][n] + abs(exact_Y[m][n])), (m, n)
+            s_err = abs(Fraction(float(S[m, n])) - exact_S[m][n])
+            assert s_err <= Fraction(K) * Fraction(2.0 ** -52) * exact_S[m][n], ("S", m, n)
 
 
 FP4_TINY = [
@@ -246,6 +263,34 @@ def test_fp4_partial_final_block_uses_last_column():
     Y3, _ = ref.matmul_fp4_reference(A, "bf16", B, three, bs, 1.0)
     Y2, _ = ref.matmul_fp4_reference(A, "bf16", B, two, bs, 1.0)
     assert Y3[0, 0] == 4.0 and Y2[0, 0] == 2.0
+
+
+def test_tolerance_scale_hand_computed_fp4():
+    """A worked example computed by hand, for Y and S = sum_k |A * B_dq|.
+
+    Codes 0x2, 0xB, 0x7, 0x9 are E2M1 1.0, -1.5, 6.0, -0.5 ([FP4 doc] §2);
+    packed low nibble first: bytes 0xB2, 0x97.  One block of 4 with scale byte
+    0x40 (E4M3 2.0) and ws2 = 0.5, so B_dq = (1, -1.5, 6, -0.5).  A (bf16) =
+    (1, -2, 0.5, 3): the products are 1, 3, 3, -1.5, so Y = 5.5 and S = 8.5."""
+    A = np.array([[0x3F80, 0xC000, 0x3F00, 0x4040]], dtype=np.uint16)
+    B = np.array([[0xB2, 0x97]], dtype=np.uint8)
+    ws = np.array([[0x40]], dtype=np.uint8)
+    Y, S = ref.matmul_fp4_reference(A, "bf16", B, ws, 4, 0.5)
+    assert Y[0, 0] == 5.5 and S[0, 0] == 8.5
+    tol = ref.matmul_tolerance(Y, S)
+    assert tol[0, 0] == 2e-3 * 8.5 + 1e-3 * 5.5
+
+
+def test_tolerance_scale_hand_computed_fp8():
+    """FP8 worked example: E4M3 bytes 0x38 (1.0), 0xC0 (-2.0), 0x30 (0.5) with
+    FP32 block scales 4.0 (k 0-1, block 2) and 0.25 (k 2); A (fp16) = (0.5,
+    1.5, -8): B_dq = (4, -8, 0.125), products 2, -12, -1, so Y = -11 and S =
+    15 ([FP8 doc] §2, partial final block with its own column)."""
+    A = np.array([[0x3800, 0x3E00, 0xC800]], dtype=np.uint16)
+    B = np.array([[0x38, 0xC0, 0x30]], dtype=np.uint8)
+    bs = np.array([[4.0, 0.25]], dtype=np.float32)
+    Y, S = ref.matmul_fp8_reference(A, "fp16", B, bs, 2)
+    assert Y[0, 0] == -11.0 and S[0, 0] == 15.0
 
 
 def test_unit_scales_reduce_to_library_matmul():
