@@ -53,20 +53,37 @@ int check_shape(int op, int64_t M, int64_t N, int64_t K, int64_t bs, int64_t col
   return FP4W_OK;
 }
 
-bool fp4_gemv_ok(int64_t M, int64_t K, int64_t bs) {
-  return M >= 1 && M <= 8 && bs == 16 && K % 128 == 0 && K > 0;
+// Sizes the fast kernels address with 32-bit offsets (anything larger takes
+// the generic kernel).  GEMV / skinny: one 16-column tile of B and all of A
+// inside a buffer descriptor.  GEMM: offsets relative to a workgroup's first
+// row of A, B and the scales (128 rows of A, 512 rows of B: K < 2^22), and a
+// tile count that fits the grid.
+bool streams_fit(int64_t M, int64_t N, int64_t K) {
+  return N <= INT_MAX - 16 && K <= (int64_t(1) << 26) && M * K * 2 < (int64_t(1) << 31);
 }
-bool fp4_skinny_ok(int64_t M, int64_t K, int64_t bs) {
-  return M >= 1 && M <= 64 && bs == 16 && K % 128 == 0 && K > 0;
+bool gemm_fits(int64_t M, int64_t N, int64_t K) {
+  return M <= INT_MAX && N <= INT_MAX && K < (int64_t(1) << 22) &&
+         ceil_div(M, 128) * ceil_div(N, 256) <= (int64_t(1) << 30);
 }
-bool fp8_skinny_ok(int64_t M, int64_t K, int64_t bs) {
-  return M >= 1 && M <= 64 && bs % 128 == 0 && K % 128 == 0 && K > 0;
+
+bool fp4_gemv_ok(int64_t M, int64_t N, int64_t K, int64_t bs) {
+  return M >= 1 && M <= 8 && bs == 16 && K % 128 == 0 && K > 0 && streams_fit(M, N, K);
 }
-bool fp4_gemm_ok(int64_t M, int64_t K, int64_t bs) { return M >= 1 && bs == 16 && K % 64 == 0 && K > 0; }
-bool fp8_gemv_ok(int64_t M, int64_t K, int64_t bs) {
-  return M >= 1 && M <= 8 && bs % 128 == 0 && K % 128 == 0 && K > 0;
+bool fp4_skinny_ok(int64_t M, int64_t N, int64_t K, int64_t bs) {
+  return M >= 1 && M <= 64 && bs == 16 && K % 128 == 0 && K > 0 && streams_fit(M, N, K);
 }
-bool fp8_gemm_ok(int64_t M, int64_t K, int64_t bs) { return M >= 1 && bs % 64 == 0 && K % 64 == 0 && K > 0; }
+bool fp8_skinny_ok(int64_t M, int64_t N, int64_t K, int64_t bs) {
+  return M >= 1 && M <= 64 && bs % 128 == 0 && K % 128 == 0 && K > 0 && streams_fit(M, N, K);
+}
+bool fp4_gemm_ok(int64_t M, int64_t N, int64_t K, int64_t bs) {
+  return M >= 1 && bs == 16 && K % 64 == 0 && K > 0 && gemm_fits(M, N, K);
+}
+bool fp8_gemv_ok(int64_t M, int64_t N, int64_t K, int64_t bs) {
+  return M >= 1 && M <= 8 && bs % 128 == 0 && K % 128 == 0 && K > 0 && streams_fit(M, N, K);
+}
+bool fp8_gemm_ok(int64_t M, int64_t N, int64_t K, int64_t bs) {
+  return M >= 1 && bs % 64 == 0 && K % 64 == 0 && K > 0 && gemm_fits(M, N, K);
+}
 bool dequant_vec_ok(int64_t N, int64_t K, int64_t bs) {
   return K % 8 == 0 && bs % 8 == 0 && K > 0 && N > 0 && (N * (K / 8)) < (int64_t(1) << 32);
 }
@@ -86,14 +103,14 @@ int shape_path(int op, int64_t M, int64_t N, int64_t K, int64_t bs) {
   }
   if (M == 0 || N == 0) return FP4W_PATH_NONE;
   if (op == FP4W_OP_FP4_MATMUL) {
-    if (fp4_gemv_ok(M, K, bs)) return FP4W_PATH_FP4_GEMV;
-    if (M > 8 && fp4_skinny_ok(M, K, bs)) return FP4W_PATH_FP4_SKINNY;
-    if (M > 8 && fp4_gemm_ok(M, K, bs)) return FP4W_PATH_FP4_GEMM;
+    if (fp4_gemv_ok(M, N, K, bs)) return FP4W_PATH_FP4_GEMV;
+    if (M > 8 && fp4_skinny_ok(M, N, K, bs)) return FP4W_PATH_FP4_SKINNY;
+    if (M > 8 && fp4_gemm_ok(M, N, K, bs)) return FP4W_PATH_FP4_GEMM;
     return FP4W_PATH_FP4_GENERIC;
   }
-  if (fp8_gemv_ok(M, K, bs)) return FP4W_PATH_FP8_GEMV;
-  if (M > 8 && fp8_skinny_ok(M, K, bs)) return FP4W_PATH_FP8_SKINNY;
-  if (M > 8 && fp8_gemm_ok(M, K, bs)) return FP4W_PATH_FP8_GEMM;
+  if (fp8_gemv_ok(M, N, K, bs)) return FP4W_PATH_FP8_GEMV;
+  if (M > 8 && fp8_skinny_ok(M, N, K, bs)) return FP4W_PATH_FP8_SKINNY;
+  if (M > 8 && fp8_gemm_ok(M, N, K, bs)) return FP4W_PATH_FP8_GEMM;
   return FP4W_PATH_FP8_GENERIC;
 }
 
@@ -101,25 +118,25 @@ int shape_path(int op, int64_t M, int64_t N, int64_t K, int64_t bs) {
 bool path_applies(int path, const MatmulArgs& a) {
   switch (path) {
     case FP4W_PATH_FP4_GEMV:
-      return fp4_gemv_ok(a.M, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 16) &&
+      return fp4_gemv_ok(a.M, a.N, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 16) &&
              aligned(a.scales, 4) && aligned(a.bias, 2) && aligned(a.Y, 2);
     case FP4W_PATH_FP4_SKINNY:
-      return fp4_skinny_ok(a.M, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 16) &&
+      return fp4_skinny_ok(a.M, a.N, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 16) &&
              aligned(a.scales, 4) && aligned(a.bias, 2) && aligned(a.Y, 2);
     case FP4W_PATH_FP4_GEMM:
-      return fp4_gemm_ok(a.M, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 16) &&
+      return fp4_gemm_ok(a.M, a.N, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 16) &&
              aligned(a.scales, 4) && aligned(a.bias, 2) && aligned(a.Y, 2);
     case FP4W_PATH_FP4_GENERIC:
     case FP4W_PATH_FP8_GENERIC:
       return true;
     case FP4W_PATH_FP8_GEMV:
-      return fp8_gemv_ok(a.M, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 16) &&
+      return fp8_gemv_ok(a.M, a.N, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 16) &&
              aligned(a.scales, 4) && aligned(a.bias, 2) && aligned(a.Y, 2);
     case FP4W_PATH_FP8_SKINNY:
-      return fp8_skinny_ok(a.M, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 16) &&
+      return fp8_skinny_ok(a.M, a.N, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 16) &&
              aligned(a.scales, 4) && aligned(a.bias, 2) && aligned(a.Y, 2);
     case FP4W_PATH_FP8_GEMM:
-      return fp8_gemm_ok(a.M, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 16) &&
+      return fp8_gemm_ok(a.M, a.N, a.K, a.block_size) && aligned(a.A, 16) && aligned(a.B, 16) &&
              aligned(a.scales, 4) && aligned(a.bias, 2) && aligned(a.Y, 2);
     default:
       return false;

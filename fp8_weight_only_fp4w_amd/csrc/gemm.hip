@@ -8,29 +8,26 @@
 // scratch is written or re-read, and the tensor scale and bias are applied in
 // the epilogue.
 //
-// Two kernels: gemm_large_kernel (below; every shape whose offsets fit in 32
-// bits) and gemm_kernel, the fallback for larger matrices.  gemm_kernel's
-// tiling (gfx950, wave64):
-//  * workgroup tile (128 WM) (M) x 256 (N) x 64 (K per step), WM x 4 waves,
-//    each wave 128 x 64 = 8 x 4 tiles of v_mfma_f32_16x16x32 (FP4: WM = 2,
-//    two waves per SIMD; FP8: WM = 1, one wave per SIMD, whose 512 registers
-//    hold both the running sum and the current scale block's sum);
-//  * the activation tile (128 WM x 64 of T) is staged in LDS, double
-//    buffered, 16-byte chunks XOR-swizzled by row so the ds_read_b128 of an
-//    MFMA operand is bank-conflict free;
-//  * weights go global -> registers directly: each wave owns 64 columns, so
-//    its packed bytes are private to it; lane (column li, k-group g) loads the
-//    16 consecutive k of its column in this step (8 bytes FP4 / 16 bytes FP8),
-//    which is one whole 16-element FP4 scale block (K permuted per lane as in
-//    the GEMV: the same permutation is applied to both operands);
-//  * FP4: the E4M3 scale is folded into the decoded BF16/FP16 operand (exact,
-//    [FP4 doc] §4); the FP32 weight_scale_2 multiplies the FP32 accumulator
-//    once in the epilogue, together with the bias;
-//  * FP8: E4M3 -> T is exact but the FP32 block scale is not, so the steps of
-//    one scale block (block_size % 64 == 0) are accumulated in a separate
-//    MFMA accumulator, which is then added to the running sum scaled in FP32.
+// One kernel, gemm_large_kernel, in three shapes (gfx950, wave64, 8 waves per
+// workgroup, 64 K per step, v_mfma_f32_32x32x16 with FP32 accumulators):
+//  * FP4 whole tiles: 128 (M) x 512 (N), the 8 waves side by side in N, each
+//    128 x 64 = 4 x 2 MFMA tiles.  The E4M3 block scale is folded into the
+//    decoded BF16/FP16 operand, which is exact (E2M1 x E4M3 needs 6
+//    significand bits; [FP4 doc] §4); weight_scale_2 and the bias are applied
+//    once in the epilogue.
+//  * FP4 split tiles (the last, partial round of tiles): one workgroup takes
+//    256 columns of a 128 x 512 tile, and its two wave groups take the two
+//    halves of K (see SPLIT below).
+//  * FP8: 128 x 256, waves in a 2 (M) x 4 (N) grid, each 64 x 64 = 2 x 2 MFMA
+//    tiles.  E4M3 -> T is exact; the FP32 block scale is not representable in
+//    the operand, so every scale block (block_size % 64 == 0) accumulates in
+//    a fresh set of FP32 accumulators, which is then added to the running sum
+//    multiplied by its b_scale in FP32 ([FP8 doc] §2: B_dq = e4m3 * b_scale).
+//    The two sets take 128 registers per lane, which is why an FP8 wave holds
+//    half the outputs of an FP4 wave.
 //
 // [FP4 doc] = "MatMulBlockQuantizedFp4Weight - CUDA Operator Documentation"
+// [FP8 doc] = "MatMulBlockQuantizedFp8Weight - CUDA Operator Documentation"
 // [Blog]    = "ONNX Runtime #32128 - Why Dequantizing 4-Bit Weights Became the
 //             Most Expensive Kernel in H200 Prefill"
 
@@ -44,7 +41,7 @@
 namespace fp4w {
 namespace {
 
-constexpr int BN = 256, BK = 64;
+constexpr int BK = 64;
 constexpr int kLdsRow = BK;  // elements per LDS row (no padding: XOR swizzle)
 
 // 16-byte chunk c of row r sits in slot c ^ ((r >> 1) & 7): the 16 rows read
@@ -55,189 +52,9 @@ __device__ __forceinline__ int lds_index(int row, int chunk) {
   return row * kLdsRow + ((chunk ^ lds_swz(row)) << 3);
 }
 
-template <typename T, bool FP8, int WM>
-__global__ __launch_bounds__(256 * WM) void gemm_kernel(
-    const T* __restrict__ A, const uint8_t* __restrict__ B, const void* __restrict__ scales,
-    const float* __restrict__ ws2p, const T* __restrict__ bias, T* __restrict__ Y, int M, int N,
-    int K, int cols, int bs, int tiles_m) {
-  typedef ActTraits<T> Tr;
-  typedef typename Tr::vec8 V;
-  constexpr int BM = 128 * WM;
-  __shared__ __attribute__((aligned(16))) T As[2][BM * kLdsRow];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int li = lane & 15, g = lane >> 4;
-  const int wm = wave >> 2, wn = wave & 3;
-  const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
-  const int m0 = tm * BM, n0 = tn * BN;
-
-  // activation staging: 4 chunks of 16 bytes per thread per step
-  const T* a_src[4];
-  int a_dst[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = (tid >> 3) + 32 * WM * j;
-    const int gm = min(m0 + row, M - 1);
-    a_src[j] = A + static_cast<size_t>(gm) * K + (tid & 7) * 8;
-    a_dst[j] = lds_index(row, tid & 7);
-  }
-  // this lane's 4 weight columns (one per 16-wide N sub-tile)
-  const uint8_t* b_src[4];
-  const void* s_src[4];
-#pragma unroll
-  for (int ns = 0; ns < 4; ++ns) {
-    const int n = min(n0 + 64 * wn + 16 * ns + li, N - 1);
-    if (FP8) {
-      b_src[ns] = B + static_cast<size_t>(n) * K + 16 * g;
-      s_src[ns] = static_cast<const float*>(scales) + static_cast<size_t>(n) * cols;
-    } else {
-      b_src[ns] = B + static_cast<size_t>(n) * (K / 2) + 8 * g;
-      s_src[ns] = static_cast<const uint8_t*>(scales) + static_cast<size_t>(n) * cols + g;
-    }
-  }
-
-  f32x4 acc[8][4];
-  f32x4 blk[FP8 ? 8 : 1][4];  // FP8: sum over the current scale block
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < (FP8 ? 8 : 1); ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) blk[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nsteps = K / BK;
-  u32x4 a_reg[4];
-  // raw weights of one step: FP4 2 dwords per column, FP8 4 dwords
-  u32x4 b_cur[4], b_nxt[4];
-  float s_cur[4], s_nxt[4];
-
-  auto load_a = [&](int step) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) a_reg[j] = *reinterpret_cast<const u32x4*>(a_src[j] + step * BK);
-  };
-  auto store_a = [&](int stage) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(&As[stage][a_dst[j]]) = a_reg[j];
-  };
-  auto load_b = [&](int step, u32x4 (&bw)[4], float (&sc)[4]) {
-    const int k0 = step * BK;
-#pragma unroll
-    for (int ns = 0; ns < 4; ++ns) {
-      if (FP8) {
-        bw[ns] = *reinterpret_cast<const u32x4*>(b_src[ns] + k0);
-        const int col = min(k0 / bs, cols - 1);
-        sc[ns] = static_cast<const float*>(s_src[ns])[col];
-      } else {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(b_src[ns] + k0 / 2);
-        bw[ns] = u32x4{v.x, v.y, 0u, 0u};
-        sc[ns] = e4m3_to_f32<0>(static_cast<const uint8_t*>(s_src[ns])[k0 / 16]);
-      }
-    }
-  };
-
-  load_a(0);
-  store_a(0);
-  load_b(0, b_cur, s_cur);
-  __syncthreads();
-
-  for (int step = 0; step < nsteps; ++step) {
-    const int cur = step & 1;
-    const bool more = step + 1 < nsteps;
-    if (more) {
-      load_a(step + 1);
-      load_b(step + 1, b_nxt, s_nxt);
-    }
-    const T* as = As[cur];
-    if (!FP8) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        V bop[4];
-#pragma unroll
-        for (int ns = 0; ns < 4; ++ns)
-          bop[ns] = Tr::decode8(s == 0 ? b_cur[ns].x : b_cur[ns].y, Tr::make_scale(s_cur[ns]));
-#pragma unroll
-        for (int ms = 0; ms < 8; ++ms) {
-          const int row = 128 * wm + 16 * ms + li;
-          const V aop = *reinterpret_cast<const V*>(&as[lds_index(row, 2 * g + s)]);
-#pragma unroll
-          for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = Tr::mfma(aop, bop[ns], acc[ms][ns]);
-        }
-      }
-    } else {
-      V bop[2][4];
-#pragma unroll
-      for (int ns = 0; ns < 4; ++ns) {
-        bop[0][ns] = Tr::decode8_fp8(b_cur[ns].x, b_cur[ns].y);
-        bop[1][ns] = Tr::decode8_fp8(b_cur[ns].z, b_cur[ns].w);
-      }
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-#pragma unroll
-        for (int ms = 0; ms < 8; ++ms) {
-          const int row = 128 * wm + 16 * ms + li;
-          const V aop = *reinterpret_cast<const V*>(&as[lds_index(row, 2 * g + s)]);
-#pragma unroll
-          for (int ns = 0; ns < 4; ++ns) blk[ms][ns] = Tr::mfma(aop, bop[s][ns], blk[ms][ns]);
-        }
-      }
-      // close the scale block after its last step: running sum += block sum * scale
-      const int k0 = step * BK;
-      const bool flush = !more || min((k0 + BK) / bs, cols - 1) != min(k0 / bs, cols - 1);
-      if (flush) {
-#pragma unroll
-        for (int ms = 0; ms < 8; ++ms)
-#pragma unroll
-          for (int ns = 0; ns < 4; ++ns) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[ms][ns][r] = fmaf(blk[ms][ns][r], s_cur[ns], acc[ms][ns][r]);
-            blk[ms][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
-          }
-      }
-    }
-    if (more) {
-      store_a(cur ^ 1);
-#pragma unroll
-      for (int ns = 0; ns < 4; ++ns) {
-        b_cur[ns] = b_nxt[ns];
-        s_cur[ns] = s_nxt[ns];
-      }
-    }
-    __syncthreads();
-  }
-
-  // epilogue: lane (li, g) holds columns n0 + 64 wn + 16 ns + li and rows
-  // m0 + 128 wm + 16 ms + 4 g + r
-  const float ws2 = FP8 ? 1.0f : *ws2p;
-#pragma unroll
-  for (int ns = 0; ns < 4; ++ns) {
-    const int n = n0 + 64 * wn + 16 * ns + li;
-    if (n >= N) continue;
-    const float b = bias ? static_cast<float>(bias[n]) : 0.0f;
-#pragma unroll
-    for (int ms = 0; ms < 8; ++ms) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + 128 * wm + 16 * ms + 4 * g + r;
-        if (m < M) {
-          const float y = FP8 ? acc[ms][ns][r] + b : fmaf(acc[ms][ns][r], ws2, b);
-          Y[static_cast<size_t>(m) * N + n] = round_to<T>(y);
-        }
-      }
-    }
-  }
-}
-
-// Prefill GEMM, large tiles (FP4 and FP8).  Workgroup tile 128 (M) x 512 (N)
-// for FP4 with 8 waves side by side in N, 256 x 256 for FP8 with 8 waves in a
-// 2 (M) x 4 (N) grid; 64 K per step.  Each wave holds 128 x 64 = 4 x 2 tiles
-// of v_mfma_f32_32x32x16 (128 FP32 accumulators per lane).  Waves w and w + 4
-// share a SIMD: a wave's weight decode (vector ALU) runs while the other
-// wave's MFMAs occupy the matrix core.  The FP4 shape moves half the
-// activation bytes per step of the square one, for twice the packed weight
-// bytes, which are a quarter of the size per element.
+// Common structure of the three shapes.  Waves w and w + 4 share a SIMD: a
+// wave's weight decode (vector ALU) runs while the other wave's MFMAs occupy
+// the matrix core.
 //  * Every operand tile moves global -> LDS by direct loads (no registers).
 //    What limits these loads is the number of L2 requests rather than their
 //    bytes: a request carries one piece of at most 64 bytes of a line, so a
@@ -255,8 +72,9 @@ __global__ __launch_bounds__(256 * WM) void gemm_kernel(
 //       column (32 E4M3 bytes, or 8 FP32 block scales starting at the first
 //       block of the slot).
 //    Every load goes through a buffer descriptor (32-bit offsets, cheaper to
-//    issue than 64-bit addresses); the weight and scale descriptors cover the
-//    workgroup's columns, so pieces past the matrix read zeros.
+//    issue than 64-bit addresses) whose base is the workgroup's first row of
+//    A and first column of B and of the scales, so any matrix size works;
+//    pieces past the matrix read zeros.
 //    The tiles of step t + 2 are requested during step t (FP4: spread over
 //    its MFMA groups); the only wait is, at the end of each step, for the
 //    tiles of step t + 1 (loads complete in order), then one barrier.  A slot
@@ -267,41 +85,36 @@ __global__ __launch_bounds__(256 * WM) void gemm_kernel(
 //  * Lane (c, h) takes column c of each 32-wide N tile and k 32h .. 32h + 31
 //    of each step for both operands (FP4: two 16-element scale blocks, one
 //    16-byte LDS read); MFMA i of the step takes k 32h + 8i .. 32h + 8i + 7.
-//    The E4M3 scale is folded into the decoded BF16/FP16 operand (exact).
 //  * Tile order: workgroups are dispatched round-robin over the 8 XCDs, each
 //    with its own L2, so the workgroup index is remapped to give every XCD a
-//    contiguous range of tiles, walked in groups of tile rows (FP8 2, FP4 8).
+//    contiguous range of tiles, walked in groups of tile rows.
 //  * SPLIT (FP4): the tiles of a last round that would fill at most half the
 //    CUs are launched separately, two workgroups per tile, 256 columns each;
 //    waves 0-3 take the first half of K and waves 4-7 the second (stage rows
 //    128 + r hold row r at k + K / 2; a weight slot holds one step of both
 //    halves, a scale slot 4 steps of both), and the halves are added through
 //    LDS before the epilogue.  That round then takes about half as long.
-constexpr int L_BM = 256;       // most rows of an activation stage
 constexpr int kScaleSteps = 8;  // steps per scale slot
 
-// Tile shapes.  FP8: 256 x 256 output tiles, 2 (M) x 4 (N) waves.  FP4:
-// 128 x 512 output tiles, 1 x 8 waves (half the activation bytes per step of
-// the 256 x 256 shape, for twice the packed weight bytes, which are 4 times
-// smaller per element).  FP4 split: one workgroup takes 256 columns of a
-// 128 x 512 tile with its two wave groups on the two halves of K.
 template <bool FP8, bool SPLIT>
 struct LargeShape {
   static constexpr bool kWide = !FP8 && !SPLIT;
-  static constexpr int kTM = FP8 ? 256 : 128;       // output rows of a tile
+  static constexpr int kTM = 128;                   // output rows of a tile
   static constexpr int kTN = FP8 ? 256 : 512;       // output columns of a tile
-  static constexpr int kSR = kWide ? 128 : 256;     // rows of an activation stage
+  static constexpr int kSR = SPLIT ? 256 : 128;     // rows of an activation stage
   static constexpr int kSC = kWide ? 512 : 256;     // columns of a workgroup (weight and scale slots)
+  static constexpr int kWaveM = FP8 ? 64 : 128;     // output rows of a wave
+  static constexpr int kMS = kWaveM / 32;           // MFMA row tiles of a wave
   static constexpr int kAL = kSR / 64;              // activation loads per wave and step
   static constexpr int kBL = kSC / 128;             // weight loads per wave and slot
   static constexpr int kSL = kSC / 64;              // scale loads per wave and slot
-  static constexpr int kGM = FP8 ? 2 : 8;           // tile rows per group of the tile order
+  static constexpr int kGM = FP8 ? 4 : 8;           // tile rows per group of the tile order
 };
 
 template <typename T, bool FP8, bool SPLIT>
 struct LargeLds {
   typedef LargeShape<FP8, SPLIT> Sh;
-  T a[3][Sh::kSR * kLdsRow];                      // 3 x 32 KiB (FP4 whole tiles: 3 x 16 KiB)
+  T a[3][Sh::kSR * kLdsRow];                      // 3 x 16 KiB (split: 3 x 32 KiB)
   uint8_t b[FP8 || SPLIT ? 3 : 2][Sh::kSC * 64];  // FP8: 3 steps; FP4: 2 slots of 2 steps; split: 3 steps
   uint8_t s[2][Sh::kSC * 32];                     // 2 slots
 };
@@ -340,9 +153,12 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
   typedef LargeShape<FP8, SPLIT> Sh;
   constexpr bool split = SPLIT;
   constexpr int SC = Sh::kSC;
+  constexpr int MS = Sh::kMS;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  // FP4 whole tiles: 8 waves in N.  Split: wave group wm takes half wm of K.
+  // FP8: wave group wm takes rows 64 wm .. 64 wm + 63.
   const int wm = Sh::kWide ? 0 : wave >> 2, wn = Sh::kWide ? wave : wave & 3;
 
   // Whole tiles: workgroup b takes tile b (contiguous ranges per XCD, then
@@ -361,19 +177,21 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
   const int tm = first_m + (t % per_group) % gsize;
   const int tn = (t % per_group) / gsize;
   const int m0 = tm * Sh::kTM, n0 = tn * Sh::kTN + (SPLIT ? 256 * (blockIdx.x & 1) : 0);
+  const int rows_m = min(Sh::kTM, M - m0);      // activation rows of this tile
   const int rows_n = max(min(SC, N - n0), 0);  // weight / scale rows of this workgroup
 
   // Activations: instruction j of wave w writes rows 8q .. 8q + 7 of the
   // stage, q = 8j + w; lane l lands in row 8q + l / 8, LDS chunk l % 8, which
   // holds global chunk (l % 8) ^ lds_swz(row).  Split: stage rows 128 + r hold
-  // tile row r in the second half of K.
+  // tile row r in the second half of K.  Rows past M repeat the last row
+  // (their outputs are not stored).  Offsets are relative to row m0.
   int a_off[Sh::kAL];
 #pragma unroll
   for (int j = 0; j < Sh::kAL; ++j) {
     const int row = 8 * (8 * j + wave) + (lane >> 3);
     const int chunk = (lane & 7) ^ lds_swz(row);
-    a_off[j] = split ? min(m0 + (row & 127), M - 1) * K + (row >> 7) * (K / 2) + 8 * chunk
-                     : min(m0 + row, M - 1) * K + 8 * chunk;
+    a_off[j] = split ? min(row & 127, rows_m - 1) * K + (row >> 7) * (K / 2) + 8 * chunk
+                     : min(row, rows_m - 1) * K + 8 * chunk;
   }
   // Weights.  FP4 slot (two steps, 64 bytes per column, pieces 0-1 = the even
   // step, 2-3 = the odd step; split: one step, pieces 0-1 = its first half of
@@ -381,9 +199,8 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
   // 16q .. 16q + 15, q = 8j + w; lane l lands in column 16q + l / 4, LDS piece
   // l % 4, holding global piece (l % 4) ^ ((col >> 2) & 3).  FP8 stage (64
   // bytes per column): the same.
-  // all loads go through buffer descriptors (32-bit offsets; cheaper to
-  // issue than 64-bit addresses: 2-4 % on this kernel)
-  const rsrc_t a_rsrc = make_rsrc(A, static_cast<uint32_t>(M) * static_cast<uint32_t>(K) * 2u);
+  const rsrc_t a_rsrc = make_rsrc(A + static_cast<size_t>(m0) * K,
+                                  static_cast<uint32_t>(rows_m) * static_cast<uint32_t>(K) * 2u);
   const uint32_t b_row = FP8 ? static_cast<uint32_t>(K) : static_cast<uint32_t>(K / 2);
   auto b_swz = [](int col) { return (col >> 2) & 3; };
   uint32_t b_off[Sh::kBL];  // byte offset in the workgroup's descriptor
@@ -412,7 +229,9 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
   }
   const rsrc_t s_rsrc = make_rsrc(scales + static_cast<size_t>(n0) * s_row, static_cast<uint32_t>(rows_n) * s_row);
   const int spb = FP8 ? bs / BK : 1;  // steps per FP8 scale block (block_size % 64 == 0)
-  // FP8: first scale column of the slot holding steps 8c .. 8c + 7
+  // FP8: scale column of step u, and the first scale column of the slot
+  // holding steps 8c .. 8c + 7
+  auto step_col = [&](int u) { return min(u / spb, cols - 1); };
   auto slot_col = [&](int c) { return min(kScaleSteps * c / spb, cols - 1); };
 
   const int nsteps = split ? K / (2 * BK) : K / BK;
@@ -452,21 +271,30 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
 
   // lane (c32, h): column c32 of each 32-wide N tile, k half h of every step
   const int c32 = lane & 31, h = lane >> 5;
-  f32x16 acc[4][2];
+  const int a_row0 = Sh::kWaveM * wm;  // this wave's first row in an activation stage
+  f32x16 acc[MS][2];
+  // FP8: the current scale block's sum (fresh at the first step of a block)
+  f32x16 blk[FP8 ? MS : 1][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MS; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+#pragma unroll
+  for (int i = 0; i < (FP8 ? MS : 1); ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) blk[i][j] = f32x16{};
 
-  // the MFMAs of step u; the loads of step ul, if any, are spread over them
-  auto compute = [&](int u, bool load, int ul) {
+  // The MFMAs of step u; the loads of step ul, if any, are spread over them.
+  // FP8: FRESH = u starts a scale block (its first MFMAs start from zero).
+  auto compute = [&](int u, bool load, int ul, auto fresh_c) {
+    constexpr bool FRESH = decltype(fresh_c)::value;
     const T* a_src = L.a[u % 3];
     const uint8_t* s_src = L.s[(u / sl) & 1];
     // lane (c32, h): k 32h .. 32h + 31 of its 2 columns (FP4 16 bytes, FP8 32)
     u32x4 bw[2][FP8 ? 2 : 1];
-    float sc[2][FP8 ? 1 : 2];
+    float sc[2][2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int col = 64 * wn + 32 * nt + c32;
@@ -475,8 +303,6 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
         const uint8_t* bp = &L.b[u % 3][col * 64];
         bw[nt][0] = *reinterpret_cast<const u32x4*>(bp + 16 * ((2 * h) ^ b_swz(col)));
         bw[nt][1] = *reinterpret_cast<const u32x4*>(bp + 16 * ((2 * h + 1) ^ b_swz(col)));
-        const int idx = min(u / spb, cols - 1) - slot_col(u / kScaleSteps);  // 0 .. 7
-        sc[nt][0] = *reinterpret_cast<const float*>(&s_src[col * 32 + 16 * ((idx >> 2) ^ ss) + 4 * (idx & 3)]);
       } else {
         // split: wave group wm takes half wm of K
         const uint8_t* bp = split ? &L.b[u % 3][col * 64 + 16 * ((2 * wm + h) ^ b_swz(col))]
@@ -492,37 +318,76 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
     // MFMA i takes k 32h + 8i .. 32h + 8i + 7 of both operands
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      V aop[4];
+      V aop[MS];
 #pragma unroll
-      for (int ms = 0; ms < 4; ++ms)
-        aop[ms] = *reinterpret_cast<const V*>(&a_src[lds_index(128 * wm + 32 * ms + c32, 4 * h + i)]);
+      for (int ms = 0; ms < MS; ++ms)
+        aop[ms] = *reinterpret_cast<const V*>(&a_src[lds_index(a_row0 + 32 * ms + c32, 4 * h + i)]);
       V bop[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         if constexpr (FP8)
-          bop[nt] = decode8_fp8_scaled<T>(bw[nt][i >> 1][2 * (i & 1)], bw[nt][i >> 1][2 * (i & 1) + 1], sc[nt][0]);
+          bop[nt] = Tr::decode8_fp8(bw[nt][i >> 1][2 * (i & 1)], bw[nt][i >> 1][2 * (i & 1) + 1]);
         else
           bop[nt] = Tr::decode8(bw[nt][0][i], Tr::make_scale(sc[nt][i >> 1]));
       }
 #pragma unroll
-      for (int ms = 0; ms < 4; ++ms)
+      for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[ms][nt] = mfma32<T>(aop[ms], bop[nt], acc[ms][nt]);
+        for (int nt = 0; nt < 2; ++nt) {
+          if constexpr (FP8) {
+            blk[ms][nt] = mfma32<T>(aop[ms], bop[nt], FRESH && i == 0 ? f32x16{} : blk[ms][nt]);
+          } else {
+            acc[ms][nt] = mfma32<T>(aop[ms], bop[nt], acc[ms][nt]);
+          }
+        }
       if (load) issue_part(ul, i);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-
+  // FP8, after the last step of a scale block: running sum += block sum *
+  // b_scale (FP32), column by column
+  auto flush = [&](int u) {
+    const uint8_t* s_src = L.s[(u / sl) & 1];
+    const int idx = step_col(u) - slot_col(u / kScaleSteps);  // 0 .. 7
+    float sc[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int col = 64 * wn + 32 * nt + c32;
+      sc[nt] = *reinterpret_cast<const float*>(&s_src[col * 32 + 16 * ((idx >> 2) ^ ((col >> 3) & 1)) + 4 * (idx & 3)]);
+    }
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[ms][nt][r] = fmaf(blk[ms][nt][r], sc[nt], acc[ms][nt][r]);
+  };
   // wait for everything but the n loads of the newest step, then barrier
   auto wait_all_but = [](int n) {
     switch (n) {
       case 2: wait_barrier<2>(); break;
+      case 4: wait_barrier<4>(); break;
       case 6: wait_barrier<6>(); break;
+      case 8: wait_barrier<8>(); break;
       case 10: wait_barrier<10>(); break;
       case 14: wait_barrier<14>(); break;
       default: wait_barrier<0>(); break;
     }
   };
+  // one step: its next loads (FP8 issues them first; FP4 spreads them over
+  // its MFMAs), its MFMAs, then the wait for the tiles of step u + 1
+  auto step_body = [&](int u, auto fresh_c) {
+    const bool ahead = u + 2 < nsteps;
+    if (FP8 && ahead) issue(u + 2);
+    compute(u, !FP8 && ahead, u + 2, fresh_c);
+    if constexpr (FP8)
+      if (u == nsteps - 1 || step_col(u + 1) != step_col(u)) flush(u);
+    if (ahead)
+      wait_all_but(loads_for(u + 2));  // the tiles of step u + 1 have landed
+    else
+      wait_barrier<0>();
+  };
+
 
   issue(0);
   if (nsteps > 1) {
@@ -531,30 +396,34 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
   } else {
     wait_barrier<0>();
   }
-  for (int step = 0; step < nsteps; ++step) {
-    const bool ahead = step + 2 < nsteps;
-    // FP4 spreads the next loads over the MFMAs; FP8 (measured a little
-    // faster that way) issues them before
-    if (FP8 && ahead) issue(step + 2);
-    compute(step, !FP8 && ahead, step + 2);
-    if (ahead)
-      wait_all_but(loads_for(step + 2));  // the tiles of step + 1 have landed
-    else
-      wait_barrier<0>();
+  if constexpr (FP8) {
+    // scale block by scale block: the first step of a block starts its sum
+    // from zero, the last one flushes it (the last column also takes the
+    // partial final block)
+    for (int u0 = 0; u0 < nsteps;) {
+      const int c = step_col(u0);
+      const int end = c == cols - 1 ? nsteps : min(nsteps, (c + 1) * spb);
+      step_body(u0, std::true_type{});
+      for (int u = u0 + 1; u < end; ++u) step_body(u, std::false_type{});
+      u0 = end;
+    }
+  } else {
+    for (int u = 0; u < nsteps; ++u) step_body(u, std::false_type{});
   }
 
   // Epilogue: lane (c, h) holds columns 64 wn + 32 nt + c and rows
-  // 128 wm + 32 ms + 8 (r / 4) + 4 h + r % 4 of the workgroup's block.
+  // o_row0 + 32 ms + 8 (r / 4) + 4 h + r % 4 of the 128-row tile.
   // Y = acc * ws2 + bias, rounded once to T, is staged in LDS (the operand
-  // stages are free now) one 128-row half at a time and written back in whole
-  // 16-byte row pieces; blocks on the ragged edge, or outputs that are not
-  // 16-byte aligned, store element-wise.
+  // stages are free now) and written back in whole 16-byte row pieces; tiles
+  // on the ragged edge, or outputs that are not 16-byte aligned, store
+  // element-wise.
+  const int o_row0 = FP8 ? 64 * wm : 0;
   if (split) {
     // add the second half of K (wave group 1) to the first (wave group 0)
     float* red = reinterpret_cast<float*>(&L);
     if (wm == 1) {
 #pragma unroll
-      for (int ms = 0; ms < 4; ++ms)
+      for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -564,7 +433,7 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
     __syncthreads();
     if (wm == 0) {
 #pragma unroll
-      for (int ms = 0; ms < 4; ++ms)
+      for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -575,7 +444,7 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
   }
   const float ws2 = FP8 ? 1.0f : *ws2p;
   constexpr int kOutPitch = SC + 8;  // elements per staged row (breaks bank aliasing)
-  static_assert(sizeof(L) >= 128 * kOutPitch * sizeof(T), "output staging exceeds LDS");
+  static_assert(sizeof(L) >= Sh::kTM * kOutPitch * sizeof(T), "output staging exceeds LDS");
   T* out = reinterpret_cast<T*>(&L);
   const bool wide = (N % 8 == 0) && (reinterpret_cast<uintptr_t>(Y) % 16 == 0) && n0 + SC <= N;
   float bsum[2];
@@ -584,68 +453,44 @@ __global__ __launch_bounds__(512) void gemm_large_kernel(
     const int n = min(n0 + 64 * wn + 32 * nt + c32, N - 1);
     bsum[nt] = bias ? static_cast<float>(bias[n]) : 0.0f;
   }
+  if (!split || wm == 0) {
 #pragma unroll
-  for (int half = 0; half < Sh::kTM / 128; ++half) {
-    if (wm == half) {
+    for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
-      for (int ms = 0; ms < 4; ++ms)
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            out[(32 * ms + 8 * (r >> 2) + 4 * h + (r & 3)) * kOutPitch + 64 * wn + 32 * nt + c32] =
-                round_to<T>(fmaf(acc[ms][nt][r], ws2, bsum[nt]));
-    }
-    __syncthreads();
-    const int mrow0 = m0 + 128 * half;
-    if (wide) {
-      // 128 rows x SC / 8 pieces of 16 bytes
-#pragma unroll
-      for (int i = 0; i < SC / 32; ++i) {
-        const int q = tid + 512 * i;
-        const int row = q / (SC / 8), piece = q % (SC / 8);
-        if (mrow0 + row < M)
-          // non-temporal: Y is not read again here, keep A and B in the caches
-          __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&out[row * kOutPitch + 8 * piece]),
-                                      reinterpret_cast<u32x4*>(&Y[static_cast<size_t>(mrow0 + row) * N + n0 + 8 * piece]));
-      }
-    } else {
-      for (int q = tid; q < 128 * SC; q += 512) {
-        const int row = q / SC, col = q % SC;
-        if (mrow0 + row < M && n0 + col < N)
-          Y[static_cast<size_t>(mrow0 + row) * N + n0 + col] = out[row * kOutPitch + col];
-      }
-    }
-    __syncthreads();
+        for (int r = 0; r < 16; ++r)
+          out[(o_row0 + 32 * ms + 8 * (r >> 2) + 4 * h + (r & 3)) * kOutPitch + 64 * wn + 32 * nt + c32] =
+              round_to<T>(fmaf(acc[ms][nt][r], ws2, bsum[nt]));
   }
-}
-
-template <typename T, bool FP8>
-int launch(const MatmulArgs& a) {
-  constexpr int WM = FP8 ? 1 : 2;
-  constexpr int BM = 128 * WM;
-  if (a.M > 0x7fffffff || a.N > 0x7fffffff || a.K > 0x7fffffff) return -1;
-  const int64_t tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
-  if (tiles_m * tiles_n > 0x7fffffff) return -1;
-  hipLaunchKernelGGL((gemm_kernel<T, FP8, WM>), dim3(static_cast<unsigned>(tiles_m * tiles_n)),
-                     dim3(256 * WM), 0, static_cast<hipStream_t>(a.stream),
-                     static_cast<const T*>(a.A), a.B, a.scales, a.ws2,
-                     static_cast<const T*>(a.bias), static_cast<T*>(a.Y), static_cast<int>(a.M),
-                     static_cast<int>(a.N), static_cast<int>(a.K), static_cast<int>(a.scale_cols),
-                     static_cast<int>(a.block_size), static_cast<int>(tiles_m));
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  __syncthreads();
+  if (wide) {
+    // 128 rows x SC / 8 pieces of 16 bytes
+#pragma unroll
+    for (int i = 0; i < SC / 32; ++i) {
+      const int q = tid + 512 * i;
+      const int row = q / (SC / 8), piece = q % (SC / 8);
+      if (row < rows_m)
+        // non-temporal: Y is not read again here, keep A and B in the caches
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&out[row * kOutPitch + 8 * piece]),
+                                    reinterpret_cast<u32x4*>(&Y[static_cast<size_t>(m0 + row) * N + n0 + 8 * piece]));
+    }
+  } else {
+    for (int q = tid; q < 128 * SC; q += 512) {
+      const int row = q / SC, col = q % SC;
+      if (row < rows_m && n0 + col < N) Y[static_cast<size_t>(m0 + row) * N + n0 + col] = out[row * kOutPitch + col];
+    }
+  }
 }
 
 }  // namespace
 
 template <typename T, bool FP8>
 int launch_large(const MatmulArgs& a) {
-  if (a.M > 0x7fffffff || a.N > 0x7fffffff || a.K > 0x7fffffff) return -1;
-  // 32-bit element offsets inside the kernel
-  const int64_t b_bytes = a.N * (FP8 ? a.K : a.K / 2);
-  if (b_bytes >= (int64_t(1) << 31) || a.N * a.scale_cols >= (int64_t(1) << 31) ||
-      static_cast<int64_t>(L_BM) * a.K >= (int64_t(1) << 31) || a.M * a.K >= (int64_t(1) << 31))
-    return launch<T, FP8>(a);
+  // Offsets inside the kernel are 32-bit and relative to the workgroup's
+  // first row of A, B and the scales: 128 rows of A, 512 rows of B and of the
+  // scales must each span less than 2^31 bytes (K < 2^22 covers all three).
+  if (a.M > 0x7fffffff || a.N > 0x7fffffff || a.K >= (int64_t(1) << 22)) return -1;
   typedef LargeShape<FP8, false> Sh;
   const int64_t tiles_m = (a.M + Sh::kTM - 1) / Sh::kTM, tiles_n = (a.N + Sh::kTN - 1) / Sh::kTN;
   const int64_t ntiles = tiles_m * tiles_n;

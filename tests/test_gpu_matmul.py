@@ -16,6 +16,7 @@ import numpy as np
 import pytest
 import torch
 
+import fp8_fold_cases
 import fp8_weight_only_fp4w_amd as fw
 import workloads
 from oracle import codecs, reference as ref
@@ -214,6 +215,55 @@ def test_fp8_one_hot_probe_bit_exact(M, N, K, bs, path):
     assert_bits_equal(got, want, f"one-hot fp8 path {path}", zero_sign=False)
 
 
+@pytest.mark.parametrize("M,K,row_powers,paths", [
+    (4, 768, False, [fw.PATH_FP8_GEMV, fw.PATH_FP8_SKINNY, fw.PATH_FP8_GENERIC]),
+    (40, 5120, False, [fw.PATH_FP8_SKINNY, fw.PATH_FP8_GEMM]),
+    (300, 768, True, [fw.PATH_FP8_GEMM, fw.PATH_FP8_GENERIC]),
+    (256, 5120, True, [fw.PATH_FP8_GEMM]),
+])
+def test_fp8_block_scale_exact_on_fold_breaking_inputs(M, K, row_powers, paths):
+    """Inputs on which multiplying RNE_bf16(e4m3 * b_scale) instead of the
+    exact B_dq fails every element (pinned on the CPU by
+    test_fp8_fold_witness.py): each FP8 kernel must apply the FP32 block scale
+    to an FP32 block sum ([FP8 doc] §2)."""
+    require_gpu()
+    A, B, s = fp8_fold_cases.fold_breaking_problem(M, K, n_cols=16, row_powers=row_powers)
+    p = workloads.Fp8Problem(M, B.shape[0], K, 128, "bf16", A, B, s, None)
+    Y_ref, S = ref_fp8(p)
+    d = fp8_device(p)
+    for path in [fw.PATH_AUTO] + paths:
+        assert_parity(run_fp8(p, d, path), "bf16", Y_ref, S, f"fp8 fold-breaking M{M} K{K} path {path}")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_gemm_activations_past_2gib(fp8):
+    """M x K x 2 bytes of activations beyond 2^31 (offsets are relative to
+    each tile's first row): sampled rows, including those on both sides of
+    the 2 GiB boundary, against the oracle."""
+    require_gpu()
+    K, N = 1024, 300
+    M = (1 << 31) // (2 * K) + 333
+    g = torch.Generator(device="cuda").manual_seed(21)
+    A = torch.randn(M, K, generator=g, device="cuda").to(torch.bfloat16)
+    rows = np.unique(np.concatenate([np.arange(16), np.arange(M - 16, M), (1 << 20) + np.arange(-8, 8),
+                                     np.random.default_rng(21).integers(0, M, 32)]))
+    A_rows = dev_to_bits(A[torch.from_numpy(rows).cuda()])
+    if fp8:
+        p = workloads.make_fp8(1, N, K, 128, "bf16", seed=22, with_bias=True)
+        d = fp8_device(p)
+        Y = fw.fp8w_matmul(A, d["B"], d["bs"], d["bias"], 128, path=fw.PATH_FP8_GEMM)
+        Y_ref, S = ref.matmul_fp8_reference(A_rows, "bf16", p.B, p.b_scale, 128, p.bias)
+    else:
+        p = workloads.make_fp4(1, N, K, 16, "bf16", seed=22, with_bias=True)
+        d = fp4_device(p)
+        Y = fw.fp4w_matmul(A, d["B"], d["ws"], d["ws2"], d["bias"], 16, path=fw.PATH_FP4_GEMM)
+        Y_ref, S = ref.matmul_fp4_reference(A_rows, "bf16", p.B, p.weight_scale, 16, p.weight_scale_2, p.bias)
+    got = dev_to_bits(Y[torch.from_numpy(rows).cuda()])
+    del A, Y
+    torch.cuda.empty_cache()
+    assert_parity(got, "bf16", Y_ref, S, f"gemm past 2 GiB fp8={fp8}")
+
+
 # ----------------------------------------------------------------- the five workloads
 
 def _sample_rows(M, seed, n_rand=32):
@@ -265,14 +315,10 @@ def test_workload_fp8_gemv_and_prefill():
     assert_parity(Y[rows], "bf16", Y_ref, S, "fp8 prefill sampled rows")
 
 
-def test_workload_fp4_gemv_wide_sampled_columns():
+def test_workload_fp4_gemv_wide_full_output():
+    """The wide-output GEMV (M=4, N=152064, K=5120) on every output column."""
     require_gpu()
-    w = workloads.WORKLOADS["fp4_gemv_wide"]
-    p = w.make()
+    p = workloads.WORKLOADS["fp4_gemv_wide"].make()
     Y = run_fp4(p)
-    rng = np.random.default_rng(13)
-    cols = np.unique(np.concatenate([np.arange(1024), np.arange(w.N - 1024, w.N), rng.integers(0, w.N, 6144)]))
-    sub = workloads.Fp4Problem(p.M, cols.size, p.K, p.block_size, p.dtype, p.A, p.B[cols],
-                               p.weight_scale[cols], p.weight_scale_2, None)
-    Y_ref, S = ref_fp4(sub)
-    assert_parity(Y[:, cols], "bf16", Y_ref, S, "fp4_gemv_wide sampled columns")
+    Y_ref, S = ref_fp4(p)
+    assert_parity(Y, "bf16", Y_ref, S, "fp4_gemv_wide full output")
