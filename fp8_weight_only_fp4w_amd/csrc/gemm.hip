@@ -521,18 +521,6 @@ int launch_large(const MatmulArgs& a) {
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int device_cus() {
-  // initialised once, thread-safely, on the first call
-  static const int cus = [] {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
-      v = 256;
-    return v;
-  }();
-  return cus;
-}
-
 int launch_fp4_gemm(const MatmulArgs& a) {
   return a.act == Act::BF16 ? launch_large<__bf16, false>(a) : launch_large<_Float16, false>(a);
 }

@@ -323,46 +323,29 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
   Pos cp{static_cast<int>(blockIdx.x), 0};  // unit being multiplied
 
   if constexpr (ACT_LDS) {
-    // Rows 0 .. M-1 of A, zero beyond K, then (FP4) the zero block.  The
-    // first eight 16-byte chunks per thread are requested before the weights,
-    // so their stores wait for them alone (loads complete in order); any
-    // further chunks (large M x K) follow the weight requests.  Chunk indices
-    // past the end are clamped to the last chunk (same data, same address),
-    // so every load is consumed by a store and none stays in flight into the
-    // main loop.
+    // Rows 0 .. M-1 of A, zero beyond K, then (FP4) the zero block, by direct
+    // loads: LDS chunk q (16 bytes) holds row q / cpr, column q % cpr; the
+    // row padding, the zero block and the tail of the last instruction are
+    // out-of-range reads, which write zeros and touch no memory.  The fill is
+    // requested before the weights, so waiting until only the first D units'
+    // weight loads are outstanding means the fill (and the first scale and
+    // bias loads) have landed.
     const uint32_t cpr = chunks_per_row.d;  // lds_pitch / 16
     const uint32_t nload = static_cast<uint32_t>(M) * cpr;
     const uint32_t nall = FP8 ? nload : nload + 16u;  // FP4: the 256-byte zero block
-    constexpr uint32_t kStep = 64u * kWaves;
-    auto fill_load = [&](uint32_t q0, u32x4 (&v)[8]) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t q = min(q0 + i * kStep, nload - 1u);
-        const uint32_t row = fdiv(q, chunks_per_row), col = q - row * cpr;
-        const uint32_t off = col * 8u < static_cast<uint32_t>(K) ? row * static_cast<uint32_t>(K) * 2u + col * 16u
-                                                                : kOutOfRange;
-        v[i] = buf_load_b128(a_rsrc, off);
-      }
-    };
-    auto fill_store = [&](uint32_t q0, const u32x4 (&v)[8]) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<u32x4*>(a_lds + 16u * min(q0 + i * kStep, nload - 1u)) = v[i];
-    };
-    u32x4 v[8];
-    fill_load(threadIdx.x, v);
+    for (uint32_t q0 = 64u * static_cast<uint32_t>(wave); q0 < nall; q0 += 64u * kWaves) {
+      const uint32_t q = q0 + static_cast<uint32_t>(lane);
+      const uint32_t row = fdiv(q, chunks_per_row), col = q - row * cpr;
+      const bool in = q < nload && col * 8u < static_cast<uint32_t>(K);
+      buf_load_lds<16>(a_rsrc, in ? row * static_cast<uint32_t>(K) * 2u + col * 16u : kOutOfRange, a_lds + 16u * q0);
+    }
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       load(raw[d], ring + d * kUnitBytes);
     }
-    fill_store(threadIdx.x, v);
-    for (uint32_t q0 = threadIdx.x + 8u * kStep; q0 < nload; q0 += 8u * kStep) {
-      fill_load(q0, v);
-      fill_store(q0, v);
-    }
-    for (uint32_t q = nload + threadIdx.x; q < nall; q += kStep)
-      *reinterpret_cast<u32x4*>(a_lds + 16u * q) = u32x4{0u, 0u, 0u, 0u};
-    lds_barrier();
+    wait_vm<2 * D>();
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
   } else {
     // FP4: the staging area's zero block (wave-private: no barrier)
     if constexpr (!FP8)
@@ -544,21 +527,10 @@ size_t lds_bytes(int mode, bool fp8, int M, int NW) {
   // ACT_LDS: the M rows (FP4: plus the 256-byte zero block); ACT_REG: the
   // staging areas
   const size_t stage = fp8 ? stage_bytes<true, 1>() : M > 4 ? stage_bytes<false, 2>() : stage_bytes<false, 1>();
-  const size_t act = mode > 0 ? static_cast<size_t>(M) * (static_cast<size_t>(NW) * 256 + 16) + (fp8 ? 0 : 256)
-                              : kWaves * stage;
+  // ACT_LDS: whole direct-load instructions of 64 chunks of 16 bytes
+  const size_t act_chunks = static_cast<size_t>(M) * (static_cast<size_t>(NW) * 16 + 1) + (fp8 ? 0 : 16);
+  const size_t act = mode > 0 ? (act_chunks + 63) / 64 * 1024 : kWaves * stage;
   return ring + slices + act;
-}
-
-int num_cus() {
-  static int cus = -1;
-  if (cus < 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
-      v = 256;
-    cus = v;
-  }
-  return cus;
 }
 
 template <typename T, int KS, bool FP8, int MODE, int R>
@@ -566,15 +538,14 @@ constexpr auto kernel_ptr() {
   return &gemv_kernel<T, KS, FP8, (MODE > 0), R, depth<FP8, MODE, R>()>;
 }
 
-// Dynamic LDS above 64 KiB must be allowed per kernel, once.
+// Dynamic LDS above 64 KiB must be allowed per kernel, once per device.
 template <typename T, int KS, bool FP8, int MODE, int R>
 void allow_lds() {
-  static bool done = false;
-  if (!done) {
+  static std::once_flag once[kMaxDevices];
+  once_per_device(once, [] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel_ptr<T, KS, FP8, MODE, R>()),
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kMaxLds));
-    done = true;
-  }
+  });
 }
 
 // Resident workgroups per CU for a kernel variant and LDS size.
@@ -606,7 +577,7 @@ int slots_for(int KS, int R, int M, int NW) {
     case 4: per = wg_per_cu_r<T, 4, FP8, MODE>(R, lds); break;
     default: per = wg_per_cu_r<T, 8, FP8, MODE>(R, lds); break;
   }
-  return num_cus() * per;
+  return device_cus() * per;
 }
 
 struct Plan {

@@ -4,6 +4,8 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 namespace fp4w {
 
 enum class Act : int { F16 = 0, BF16 = 1 };
@@ -55,9 +57,27 @@ struct QdqArgs {
 // an error at enqueue time.  Preconditions (checked by the dispatcher, never
 // by the launcher) are stated next to each.
 
-// compute units of the device current at the first call (cached for the
-// process; 256 if the query fails)
+// Host-side state is per device and initialised once, thread-safely: the
+// library keeps no other state between calls.
+constexpr int kMaxDevices = 64;
+
+// the calling thread's current HIP device (0 if the query fails)
+int current_device();
+
+// compute units of the current device, queried once per device (256 if the
+// query fails)
 int device_cus();
+
+// Runs f() once per device for the given flag array (device ids beyond
+// kMaxDevices run it on every call; f must be idempotent).
+template <typename F>
+void once_per_device(std::once_flag (&flags)[kMaxDevices], F&& f) {
+  const int dev = current_device();
+  if (dev < 0 || dev >= kMaxDevices)
+    f();
+  else
+    std::call_once(flags[dev], f);
+}
 
 // 1 <= M <= 8, block_size == 16, K % 128 == 0, scale_cols == K / 16,
 // A / B 16-byte aligned, scales 4-byte aligned, bias 2-byte aligned.

@@ -376,15 +376,14 @@ constexpr size_t sk_lds() {
   return static_cast<size_t>(kSkWaves) * sk_lds_per_wave<FP8, sk_depth<MT>()>();
 }
 
-// Dynamic LDS above 64 KiB must be allowed per kernel, once.
+// Dynamic LDS above 64 KiB must be allowed per kernel, once per device.
 template <typename T, bool FP8, int MT, int KS>
 void sk_allow_lds() {
-  static bool done = false;
-  if (!done) {
+  static std::once_flag once[kMaxDevices];
+  once_per_device(once, [] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&skinny_kernel<T, FP8, MT, KS, sk_depth<MT>()>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sk_lds<FP8, MT>()));
-    done = true;
-  }
+  });
 }
 
 template <typename T, bool FP8, int MT, int KS>
