@@ -21,7 +21,10 @@ using fp4w::Fp8DequantArgs;
 using fp4w::MatmulArgs;
 using fp4w::QdqArgs;
 
-constexpr int64_t kMaxElems = int64_t(1) << 62;
+// Element counts (M * K, N * K, M * N, N * scale_cols) are capped at 2^60, so
+// every byte count derived from them (at most 4 bytes per element) stays
+// below 2^63.
+constexpr int64_t kMaxElems = int64_t(1) << 60;
 
 bool mul_ok(int64_t a, int64_t b) { return a == 0 || b <= kMaxElems / a; }
 

@@ -1,0 +1,33 @@
+// Host-only stand-ins for the HIP launchers, for a sanitizer build of the
+// C ABI's validation and dispatch (dispatch.cpp) on a machine without a GPU.
+// Each launcher records which kernel the dispatcher chose and launches
+// nothing.
+#include "../../fp8_weight_only_fp4w_amd/csrc/launch.h"
+
+#include <cstring>
+
+namespace fp4w {
+const char* g_last = "";
+int current_device() { return 0; }
+int device_cus() { return 256; }
+#define STUB(name, T)          \
+  int name(const T&) {         \
+    g_last = #name;            \
+    return 0;                  \
+  }
+STUB(launch_fp4_gemv, MatmulArgs)
+STUB(launch_fp4_gemm, MatmulArgs)
+STUB(launch_fp4_skinny, MatmulArgs)
+STUB(launch_fp4_generic, MatmulArgs)
+STUB(launch_fp8_gemv, MatmulArgs)
+STUB(launch_fp8_gemm, MatmulArgs)
+STUB(launch_fp8_skinny, MatmulArgs)
+STUB(launch_fp8_generic, MatmulArgs)
+STUB(launch_dequant_vec, DequantArgs)
+STUB(launch_dequant_generic, DequantArgs)
+STUB(launch_fp8_dequant_vec, Fp8DequantArgs)
+STUB(launch_fp8_dequant_generic, Fp8DequantArgs)
+STUB(launch_qdq_vec, QdqArgs)
+STUB(launch_qdq_generic, QdqArgs)
+#undef STUB
+}  // namespace fp4w

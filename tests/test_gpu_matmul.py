@@ -106,6 +106,33 @@ def test_fp4_one_hot_probe_bit_exact(M, N, K, path, dtype):
     assert_bits_equal(got, want, f"one-hot fp4 path {path}", zero_sign=False)
 
 
+@pytest.mark.parametrize("M,N,K,path", [
+    (4, 64, 256, fw.PATH_FP4_GEMV), (24, 64, 256, fw.PATH_FP4_SKINNY), (130, 520, 256, fw.PATH_FP4_GEMM),
+    (4, 64, 256, fw.PATH_FP4_GENERIC),
+])
+def test_fp4_fp16_overflow_rounds_to_inf(M, N, K, path):
+    """FP16 outputs beyond 65504 round to +-inf (round to nearest even, no
+    saturation): activations of 1000, E2M1 weights of +-6 with scale 448 and
+    ws2 = 1 give column sums far beyond the FP16 range, while the columns
+    with mixed weights stay finite."""
+    require_gpu()
+    p = workloads.make_fp4(M, N, K, 16, "fp16", seed=M + N, with_bias=False)
+    p.A[:] = 0x63D0                                          # fp16 1000.0
+    rng = np.random.default_rng(M)
+    big = rng.random(N) < 0.5
+    sign = np.where(rng.random(N) < 0.5, 0x8, 0x0)
+    code = (0x7 | sign).astype(np.uint8)                      # +-6
+    p.B[big] = (code[big, None] | (code[big, None] << 4))
+    p.weight_scale[big] = 0x7E                                # E4M3 448
+    p.weight_scale[~big] = 0x08                               # E4M3 2^-6: those sums stay finite
+    p.weight_scale_2 = np.float32(1.0)
+    Y_ref, S = ref_fp4(p)
+    got = run_fp4(p, path=path)
+    inf = (got & 0x7FFF) == 0x7C00
+    assert inf[:, big].all() and not inf[:, ~big].any()
+    assert_parity(got, "fp16", Y_ref, S, f"fp16 overflow path {path}")
+
+
 def test_fp4_k_zero_gives_bias():
     require_gpu()
     for dtype in ("bf16", "fp16"):

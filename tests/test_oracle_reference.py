@@ -414,6 +414,29 @@ def test_tolerance_constants():
     assert not ref.check_matmul(np.array([[0x3FA0]], dtype=np.uint16), "bf16", Y, S)["ok"]
 
 
+def test_check_matmul_fp16_overflow_reading():
+    """FP32 -> FP16 rounds to nearest even and overflows to +-inf (no
+    saturation).  Values from 65520 up round to +inf.  Y_ref = 70000 with S =
+    70000 (tol = 210): the whole band rounds to +inf, so +inf passes and the
+    largest finite value 65504 fails; Y_ref = 65400 (tol = 196.2): the band
+    [65203.8, 65596.2] rounds to [65216, +inf], so 65216, 65504 and +inf
+    pass, and 65184, -inf and NaN fail."""
+    INF, MAXF = 0x7C00, 0x7BFF
+    Y, S = np.array([[70000.0]]), np.array([[70000.0]])
+    assert ref.check_matmul(np.array([[INF]], np.uint16), "fp16", Y, S)["ok"]
+    assert not ref.check_matmul(np.array([[MAXF]], np.uint16), "fp16", Y, S)["ok"]
+    Y, S = np.array([[65400.0]]), np.array([[65400.0]])
+    assert ref.check_matmul(np.array([[MAXF]], np.uint16), "fp16", Y, S)["ok"]
+    assert ref.check_matmul(np.array([[INF]], np.uint16), "fp16", Y, S)["ok"]
+    assert ref.check_matmul(np.array([[0x7BF6]], np.uint16), "fp16", Y, S)["ok"]      # 65216
+    assert not ref.check_matmul(np.array([[0x7BF5]], np.uint16), "fp16", Y, S)["ok"]  # 65184
+    assert not ref.check_matmul(np.array([[0xFC00]], np.uint16), "fp16", Y, S)["ok"]  # -inf
+    assert not ref.check_matmul(np.array([[0x7E00]], np.uint16), "fp16", Y, S)["ok"]  # NaN
+    # a finite band still rejects +-inf
+    Y, S = np.array([[1.0]]), np.array([[1.0]])
+    assert not ref.check_matmul(np.array([[INF]], np.uint16), "fp16", Y, S)["ok"]
+
+
 def test_check_matmul_nan_reference():
     Y = np.array([[np.nan, 1.0]])
     S = np.array([[1.0, 1.0]])
