@@ -69,8 +69,10 @@ bool gemm_fits(int64_t M, int64_t N, int64_t K) {
          ceil_div(M, 128) * ceil_div(N, 256) <= (int64_t(1) << 30);
 }
 
+// FP4 GEMV: K % 32 == 0, as the pages' decode path ([FP4 doc] §3, Dispatch
+// Chain); a last window of 32, 64 or 96 k has its missing scale bytes masked.
 bool fp4_gemv_ok(int64_t M, int64_t N, int64_t K, int64_t bs) {
-  return M >= 1 && M <= 8 && bs == 16 && K % 128 == 0 && K > 0 && streams_fit(M, N, K);
+  return M >= 1 && M <= 8 && bs == 16 && K % 32 == 0 && K > 0 && streams_fit(M, N, K);
 }
 bool fp4_skinny_ok(int64_t M, int64_t N, int64_t K, int64_t bs) {
   return M >= 1 && M <= 64 && bs == 16 && K % 128 == 0 && K > 0 && streams_fit(M, N, K);

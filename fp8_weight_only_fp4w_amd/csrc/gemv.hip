@@ -106,7 +106,8 @@ template <bool FP8, bool ACT_REG, int R>
 struct Raw;
 template <bool ACT_REG, int R>
 struct Raw<false, ACT_REG, R> {
-  u32x4 sc[2];  // rows lr and 8 + lr, 16 bytes each
+  u32x4 sc[2];      // rows lr and 8 + lr, 16 bytes each from a dword-aligned offset
+  uint32_t sct[2];  // the dword after each (for the realignment of rows that start off a dword)
   uint32_t bias;
   u32x4 a[ACT_REG ? kActLoads<false, R> : 1];
 };
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
   const int li = lane & 15, g = lane >> 4;    // fragment side: row li, chunk group g
   const int lr = lane >> 3, lc = lane & 7;    // load side: row lr of an 8-row half, position lc
   const int ks = wave % KS, tw = wave / KS;
-  const int NW = K >> 7;                      // 128-k windows (K % 128 == 0)
+  const int NW = (K + 127) >> 7;              // 128-k windows (FP4: the last may hold 32, 64 or 96 k)
   const int NU = (NW + UW - 1) / UW;          // units per row
   const int ntg = (num_tiles + TPW - 1) / TPW;
   const int iters = (ntg - static_cast<int>(blockIdx.x) + static_cast<int>(gridDim.x) - 1) /
@@ -262,7 +263,11 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
     const int rows = max(0, min(16, N - 16 * t));
     const size_t n0 = static_cast<size_t>(16) * t;
     br = make_rsrc(B + n0 * row_bytes, rows * row_bytes);
-    sr = make_rsrc(static_cast<const uint8_t*>(scales) + n0 * srow_bytes, rows * srow_bytes);
+    // rounded up to whole dwords: a buffer load checks its range dword by
+    // dword, so a row whose last scale bytes share a dword with the end of
+    // the array would read them as zero (the bytes past the array in that
+    // dword are past the row's last column, and masked)
+    sr = make_rsrc(static_cast<const uint8_t*>(scales) + n0 * srow_bytes, (rows * srow_bytes + 3u) & ~3u);
     biasr = make_rsrc(bias + n0, bias ? rows * 2u : 0u);
   };
   set_load_tile();
@@ -271,9 +276,14 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
   // the descriptor.
   const uint32_t wl = lr * row_bytes + 16u * (lc ^ lr);
   const uint32_t wl8 = wl + 8u * row_bytes;
-  // FP4 scale pieces: row lr (+ 8), bytes 16 lc of the 128-byte piece
+  // FP4 scale pieces: row lr (+ 8), bytes 16 lc of the 128-byte piece.
+  // With K % 64 != 0 a row of K / 16 scale bytes may start off a dword
+  // boundary, and buffer loads address whole dwords: the piece is loaded
+  // from the dword boundary below, with one dword more, and realigned by
+  // sc_shift bytes (the same for rows lr and 8 + lr: 8 * srow_bytes % 4 == 0).
   const uint32_t sl = lr * srow_bytes + 16u * lc;
   const uint32_t sl8 = sl + 8u * srow_bytes;
+  const uint32_t sc_shift = sl & 3u;
 
   auto load = [&](RawT& r, unsigned char* slot) {
     // bias and scale pieces are only requested for the units that carry
@@ -290,8 +300,10 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
     } else {
       // E4M3 scales of windows 2u .. 2u + 15 (bytes past the row are never used)
       if (piece) {
-        r.sc[0] = buf_load_b128(sr, sl + 16u * u);
-        r.sc[1] = buf_load_b128(sr, sl8 + 16u * u);
+        r.sc[0] = buf_load_b128(sr, (sl & ~3u) + 16u * u);
+        r.sct[0] = buf_load_b32(sr, (sl & ~3u) + 16u * u + 16u);
+        r.sc[1] = buf_load_b128(sr, (sl8 & ~3u) + 16u * u);
+        r.sct[1] = buf_load_b32(sr, (sl8 & ~3u) + 16u * u + 16u);
       }
     }
     if constexpr (ACT_REG) {
@@ -395,8 +407,12 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
       for (int i = 0; i < R; ++i) acc[i] = fmaf(blk[i], sc, acc[i]);
     } else {
       if (j % SU == 0) {
-        *reinterpret_cast<u32x4*>(slice + kSlicePitch * lr + 16 * lc) = r.sc[0];
-        *reinterpret_cast<u32x4*>(slice + kSlicePitch * (8 + lr) + 16 * lc) = r.sc[1];
+        auto realign = [&](const u32x4& v, uint32_t t) {
+          return u32x4{__builtin_amdgcn_alignbyte(v.y, v.x, sc_shift), __builtin_amdgcn_alignbyte(v.z, v.y, sc_shift),
+                       __builtin_amdgcn_alignbyte(v.w, v.z, sc_shift), __builtin_amdgcn_alignbyte(t, v.w, sc_shift)};
+        };
+        *reinterpret_cast<u32x4*>(slice + kSlicePitch * lr + 16 * lc) = realign(r.sc[0], r.sct[0]);
+        *reinterpret_cast<u32x4*>(slice + kSlicePitch * (8 + lr) + 16 * lc) = realign(r.sc[1], r.sct[1]);
       }
       if constexpr (ACT_REG) {
 #pragma unroll
@@ -408,11 +424,15 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
       for (int s2 = 0; s2 < 2; ++s2) {
         const int w = 2 * u + s2;
         const int wa = min(w, NW - 1);  // windows past NW meet zero scales
-        // the slice bytes are always readable; a window past NW takes zero
-        // scales (a uniform mask instead of a branch)
-        const uint32_t keep = w < NW ? ~0u : 0u;
+        // the slice bytes are always readable; scale bytes past the row's
+        // last column (a last window of 32, 64 or 96 k, or a window past NW)
+        // are masked to E4M3 zero: they belong to the next row and may hold
+        // a NaN code (a uniform mask instead of a branch)
+        const int nb = cols - 8 * w;  // scale bytes of this window inside the row
+        const uint32_t keep_lo = nb >= 4 ? ~0u : nb <= 0 ? 0u : (1u << (8 * nb)) - 1u;
+        const uint32_t keep_hi = nb >= 8 ? ~0u : nb <= 4 ? 0u : (1u << (8 * (nb - 4))) - 1u;
         const u32x2 sr = *reinterpret_cast<const u32x2*>(slice + kSlicePitch * li + 8 * (2 * (j % SU) + s2));
-        const u32x2 sb = u32x2{sr.x & keep, sr.y & keep};
+        const u32x2 sb = u32x2{sr.x & keep_lo, sr.y & keep_hi};
         // activations of the lane: 4 x 16 bytes per row half; chunk i = 2s + p
         // holds k 32g + 16s + 8p .. + 7 of the window (piece p of set s)
         u32x4 av[R][4];
@@ -692,7 +712,7 @@ int launch_t(const MatmulArgs& a) {
   if (a.N > 0x7fffffff - 16 || a.K > (int64_t(1) << 26) || a.M * a.K * 2 >= (int64_t(1) << 31))
     return -1;
   const int M = static_cast<int>(a.M);
-  const int NW = static_cast<int>(a.K / 128);
+  const int NW = static_cast<int>((a.K + 127) / 128);
   // FP8: result rows a lane scales; FP4: row halves
   const int R = FP8 ? (M >= 3 ? 4 : M) : (M > 4 ? 2 : 1);
   const Plan p = cached_plan<T, FP8>(a.N, M, R, NW);

@@ -79,7 +79,7 @@ void once_per_device(std::once_flag (&flags)[kMaxDevices], F&& f) {
     std::call_once(flags[dev], f);
 }
 
-// 1 <= M <= 8, block_size == 16, K % 128 == 0, scale_cols == K / 16,
+// 1 <= M <= 8, block_size == 16, K % 32 == 0, scale_cols == K / 16,
 // A / B 16-byte aligned, scales 4-byte aligned, bias 2-byte aligned.
 int launch_fp4_gemv(const MatmulArgs& a);
 // M >= 1, block_size == 16, K % 64 == 0, scale_cols == K / 16,

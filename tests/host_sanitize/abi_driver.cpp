@@ -37,6 +37,7 @@ int main() {
       {4, 5120, 5120, 16, "launch_fp4_gemv"},   {8, 16, 128, 16, "launch_fp4_gemv"},
       {40, 300, 256, 16, "launch_fp4_skinny"},  {100, 300, 256, 16, "launch_fp4_gemm"},
       {100, 300, 96, 16, "launch_fp4_generic"}, {4, 300, 30, 15, "launch_fp4_generic"},
+      {3, 1000, 480, 16, "launch_fp4_gemv"},    {3, 1000, 464, 16, "launch_fp4_generic"},
       {100, 300, int64_t(1) << 22, 16, "launch_fp4_generic"},
   };
   for (const Case& c : fp4_cases) {

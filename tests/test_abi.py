@@ -81,8 +81,12 @@ def test_dispatch_fp4():
     assert sel(F, 8192, 17408, 5120, 16) == fw.PATH_FP4_GEMM
     # outside the fast predicates -> generic ([Blog] "Existing FP4 tests did not
     # reach the prefill kernel": every leaf must be reachable and tested)
-    assert sel(F, 4, 64, 48, 16) == fw.PATH_FP4_GENERIC        # K % 128 != 0
-    assert sel(F, 4, 64, 192, 16) == fw.PATH_FP4_GENERIC       # K % 128 != 0
+    assert sel(F, 4, 64, 48, 16) == fw.PATH_FP4_GENERIC        # K % 32 != 0
+    assert sel(F, 4, 64, 464, 16) == fw.PATH_FP4_GENERIC       # K % 32 != 0
+    # the GEMV takes K % 32 == 0 ([FP4 doc] §3): a last window of 32, 64 or 96 k
+    assert sel(F, 4, 64, 192, 16) == fw.PATH_FP4_GEMV
+    assert sel(F, 3, 1000, 480, 16) == fw.PATH_FP4_GEMV
+    assert sel(F, 8, 64, 32, 16) == fw.PATH_FP4_GEMV
     assert sel(F, 4, 64, 64, 32) == fw.PATH_FP4_GENERIC        # block_size != 16
     assert sel(F, 4, 64, 30, 15) == fw.PATH_FP4_GENERIC        # odd block size
     assert sel(F, 100, 64, 96, 16) == fw.PATH_FP4_GENERIC      # K % 64 != 0 for GEMM

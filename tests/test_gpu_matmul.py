@@ -31,7 +31,13 @@ pytestmark = pytest.mark.gpu
 FP4_CASES = [
     # M, N, K, bs, dtype, bias, partial, paths to force (besides AUTO)
     (1, 16, 128, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMV, fw.PATH_FP4_GENERIC]),
-    (3, 1000, 480, 16, "fp16", True, "ceil", [fw.PATH_FP4_GENERIC]),  # K % 128 != 0: generic
+    # K % 128 != 0: the GEMV's last window holds 96, 64 or 32 k (scale bytes
+    # past the row masked), against the generic kernel
+    (3, 1000, 480, 16, "fp16", True, "ceil", [fw.PATH_FP4_GEMV, fw.PATH_FP4_GENERIC]),
+    (8, 300, 320, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMV]),
+    (1, 77, 32, 16, "bf16", False, "ceil", [fw.PATH_FP4_GEMV]),
+    (5, 4100, 5152, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMV]),
+    (4, 300, 17440, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMV]),  # streamed activations, 137 windows
     (8, 777, 1024, 16, "bf16", False, "ceil", [fw.PATH_FP4_GEMV, fw.PATH_FP4_GEMM]),
     (5, 65590, 128, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMV]),  # 2 tiles per wave, ragged N
     (9, 300, 128, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMM, fw.PATH_FP4_GENERIC]),
@@ -96,6 +102,7 @@ def _one_hot_fp4(M, N, K, dtype, seed):
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("M,N,K,path", [
     (8, 64, 256, fw.PATH_FP4_GEMV), (5, 48, 128, fw.PATH_FP4_GEMV), (1, 32, 4096, fw.PATH_FP4_GEMV),
+    (8, 64, 480, fw.PATH_FP4_GEMV), (3, 40, 160, fw.PATH_FP4_GEMV),
     (8, 300, 512, fw.PATH_FP4_GEMM), (64, 512, 1024, fw.PATH_FP4_GEMM), (16, 40, 96, fw.PATH_FP4_GENERIC),
     (13, 80, 512, fw.PATH_FP4_SKINNY), (64, 48, 1024, fw.PATH_FP4_SKINNY),
 ])
@@ -131,6 +138,21 @@ def test_fp4_fp16_overflow_rounds_to_inf(M, N, K, path):
     inf = (got & 0x7FFF) == 0x7C00
     assert inf[:, big].all() and not inf[:, ~big].any()
     assert_parity(got, "fp16", Y_ref, S, f"fp16 overflow path {path}")
+
+
+@pytest.mark.parametrize("K", [480, 352, 160])
+def test_fp4_gemv_partial_window_masks_next_row_scales(K):
+    """K % 128 != 0: the last 128-k window of a row reads scale bytes past the
+    row's last column, which belong to the next row.  Every odd row's first
+    8 scale bytes hold the E4M3 NaN code 0x7F: the odd rows' outputs are NaN
+    (their own scales), and the even rows' must not be touched by them."""
+    require_gpu()
+    p = workloads.make_fp4(4, 96, K, 16, "bf16", seed=K, with_bias=True)
+    p.weight_scale[1::2, :8] = 0x7F
+    Y_ref, S = ref_fp4(p)
+    assert np.isnan(Y_ref[:, 1::2]).all() and np.isfinite(Y_ref[:, 0::2]).all()
+    for path in (fw.PATH_FP4_GEMV, fw.PATH_FP4_GENERIC):
+        assert_parity(run_fp4(p, path=path), "bf16", Y_ref, S, f"fp4 K={K} NaN scales path {path}")
 
 
 def test_fp4_k_zero_gives_bias():
