@@ -83,8 +83,10 @@ bool fp8_skinny_ok(int64_t M, int64_t N, int64_t K, int64_t bs) {
 bool fp4_gemm_ok(int64_t M, int64_t N, int64_t K, int64_t bs) {
   return M >= 1 && bs == 16 && K % 64 == 0 && K > 0 && gemm_fits(M, N, K);
 }
+// FP8 GEMV: K % 16 == 0 ([FP8 doc] §3-4) and block_size % 64 == 0 (each 64-k
+// half of a 128-k window lies in one scale block).
 bool fp8_gemv_ok(int64_t M, int64_t N, int64_t K, int64_t bs) {
-  return M >= 1 && M <= 8 && bs % 128 == 0 && K % 128 == 0 && K > 0 && streams_fit(M, N, K);
+  return M >= 1 && M <= 8 && bs % 64 == 0 && K % 16 == 0 && K > 0 && streams_fit(M, N, K);
 }
 bool fp8_gemm_ok(int64_t M, int64_t N, int64_t K, int64_t bs) {
   return M >= 1 && bs % 64 == 0 && K % 64 == 0 && K > 0 && gemm_fits(M, N, K);

@@ -71,13 +71,14 @@ constexpr int kSlicePitch = 144;       // FP4 scale slice: bytes per row (128 + 
 
 template <bool FP8>
 constexpr uint32_t slice_bytes() {
-  return FP8 ? 1024u : 16u * kSlicePitch;
+  return 16u * kSlicePitch;  // FP4: 128 E4M3 bytes per row, FP8: 32 FP32 scales per row
 }
 
 // Units per scale piece.  FP4: 8 E4M3 bytes per window, 128 bytes per row =
 // 16 windows = 8 units, loaded like the weights (8 rows x 128 bytes per
-// instruction).  FP8: one FP32 scale per 128-k window (or per several:
-// block_size % 128 == 0), 16 scales of a row = 64 bytes per piece.
+// instruction).  FP8: one FP32 scale per 64-k half window at most
+// (block_size % 64 == 0), 32 scales of a row = 128 bytes per piece of 16
+// windows.
 template <bool FP8>
 constexpr int kScaleUnits = FP8 ? 16 : 8;
 
@@ -113,7 +114,7 @@ struct Raw<false, ACT_REG, R> {
 };
 template <bool ACT_REG, int R>
 struct Raw<true, ACT_REG, R> {
-  u32x4 sc;
+  u32x4 sc[2];  // columns 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3 of the piece
   uint32_t bias;
   u32x4 a[ACT_REG ? kActLoads<true, R> : 1];
 };
@@ -168,7 +169,7 @@ template <typename T, int KS, bool FP8, bool ACT_LDS, int R, int D>
 __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
     const T* __restrict__ A, const uint8_t* __restrict__ B, const void* __restrict__ scales,
     const float* __restrict__ ws2p, const T* __restrict__ bias, T* __restrict__ Y, int M, int N,
-    int K, int cols, FastDiv win_per_block, FastDiv chunks_per_row, int num_tiles, int nus) {
+    int K, int cols, FastDiv halves_per_block, FastDiv chunks_per_row, int num_tiles, int nus) {
   constexpr bool ACT_REG = !ACT_LDS;
   constexpr int TPW = kWaves / KS;
   constexpr int S = D + 1;          // unit slots (LDS ring and registers)
@@ -245,9 +246,10 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
   const uint32_t st_pos = 16u * static_cast<uint32_t>(FP8 ? (lane & 15) : (lane & 31));
   const uint32_t st_pitch = FP8 ? kStagePitch8 : kStagePitch4;
   const uint32_t unit_act = FP8 ? 256u : 512u;  // activation bytes of a row per unit
-  // scale column of window w (FP8; windows past NW are clamped)
-  auto scol = [&](int w) {
-    return min(fdiv(static_cast<uint32_t>(min(w, NW - 1)), win_per_block), static_cast<uint32_t>(cols - 1));
+  // FP8: scale column of 64-k half window hw (block_size % 64 == 0, so a
+  // half lies in one block; halves past the row are clamped to the last)
+  auto hcol = [&](int hw) {
+    return min(fdiv(static_cast<uint32_t>(min(hw, 2 * NW - 1)), halves_per_block), static_cast<uint32_t>(cols - 1));
   };
 
   // Window mapping.  Unit u covers bytes 128u .. 128u + 127 of every row.
@@ -295,15 +297,23 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
     const bool piece = ok && lp.j % SU == 0;
     if constexpr (FP8) {
       const int w = u;
-      // FP32 scales of columns scol(w) .. + 15 (bytes past the row are never used)
-      if (piece) r.sc = buf_load_b128(sr, li * srow_bytes + 4u * scol(w) + 16u * g);
+      // FP32 scales of columns hcol(2w) .. + 31 (bytes past the row are never used)
+      // (the second 16 columns only for 64-k blocks: with larger blocks 16
+      // windows span at most 16 columns)
+      if (piece) {
+        const uint32_t o = li * srow_bytes + 4u * hcol(2 * w) + 16u * g;
+        r.sc[0] = buf_load_b128(sr, o);
+        if (halves_per_block.d == 1) r.sc[1] = buf_load_b128(sr, o + 64u);
+      }
     } else {
       // E4M3 scales of windows 2u .. 2u + 15 (bytes past the row are never used)
       if (piece) {
         r.sc[0] = buf_load_b128(sr, (sl & ~3u) + 16u * u);
-        r.sct[0] = buf_load_b32(sr, (sl & ~3u) + 16u * u + 16u);
         r.sc[1] = buf_load_b128(sr, (sl8 & ~3u) + 16u * u);
-        r.sct[1] = buf_load_b32(sr, (sl8 & ~3u) + 16u * u + 16u);
+        if (srow_bytes & 3u) {  // uniform
+          r.sct[0] = buf_load_b32(sr, (sl & ~3u) + 16u * u + 16u);
+          r.sct[1] = buf_load_b32(sr, (sl8 & ~3u) + 16u * u + 16u);
+        }
       }
     }
     if constexpr (ACT_REG) {
@@ -377,12 +387,18 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
     typedef typename Tr::vec8 V;
     const int sw = li & 7;  // swizzle of the lane's row in the slot
     if constexpr (FP8) {
-      if (j % SU == 0) *reinterpret_cast<u32x4*>(slice + 64 * li + 16 * g) = r.sc;
+      // slice rows of kSlicePitch bytes: the 16 rows' scale reads of a
+      // window fall in distinct banks
+      if (j % SU == 0) {
+        *reinterpret_cast<u32x4*>(slice + kSlicePitch * li + 16 * g) = r.sc[0];
+        if (halves_per_block.d == 1) *reinterpret_cast<u32x4*>(slice + kSlicePitch * li + 64 + 16 * g) = r.sc[1];
+      }
       const int w = min(u, NW - 1);  // windows past NW meet zero weights
-      // the scale of this window's column, from the piece of the first
-      // window of its group (the column offset is at most 15)
-      const uint32_t c0 = scol(ks * nus + (j - j % SU));
-      const float sc = *reinterpret_cast<const float*>(slice + 64 * li + 4 * (scol(w) - c0));
+      // the scales of this window's two halves, from the piece of the first
+      // window of its group (column offsets at most 31)
+      const uint32_t c0 = hcol(2 * (ks * nus + (j - j % SU)));
+      const uint32_t c_lo = hcol(2 * w), c_hi = hcol(2 * w + 1);
+      const float s_lo = *reinterpret_cast<const float*>(slice + kSlicePitch * li + 4 * (c_lo - c0));
       if constexpr (ACT_REG) {
 #pragma unroll
         for (int b = 0; b < kActLoads<FP8, R>; ++b)
@@ -395,24 +411,67 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
       a[2] = *reinterpret_cast<const V*>(q + 128u);
       a[3] = *reinterpret_cast<const V*>(q + 144u);
       wait_vm<D * LPU>();  // this unit's weights have landed
-      const u32x4 w0 = *reinterpret_cast<const u32x4*>(slot + 128 * li + 16 * (g ^ sw));
-      const u32x4 w1 = *reinterpret_cast<const u32x4*>(slot + 128 * li + 16 * ((4 + g) ^ sw));
-      f32x4 blk = f32x4{0.f, 0.f, 0.f, 0.f};
-      blk = Tr::mfma(a[0], Tr::decode8_fp8(w0.x, w0.y), blk);
-      blk = Tr::mfma(a[1], Tr::decode8_fp8(w0.z, w0.w), blk);
-      blk = Tr::mfma(a[2], Tr::decode8_fp8(w1.x, w1.y), blk);
-      blk = Tr::mfma(a[3], Tr::decode8_fp8(w1.z, w1.w), blk);
-      // lane holds column n (one scale) and rows 4g .. 4g + 3
+      u32x4 w0 = *reinterpret_cast<const u32x4*>(slot + 128 * li + 16 * (g ^ sw));
+      u32x4 w1 = *reinterpret_cast<const u32x4*>(slot + 128 * li + 16 * ((4 + g) ^ sw));
+      if ((K & 127) && 128 * (w + 1) > K) {
+        // a last window of K % 128 k: the bytes past the row are the next
+        // row's E4M3 codes, which may be NaN; zero the lane's chunks past K
+        // (K % 16 == 0: whole chunks)
+        const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+        if (128 * w + 16 * g >= K) w0 = z;
+        if (128 * w + 64 + 16 * g >= K) w1 = z;
+      }
+      // MFMAs 0-1 take k 0 .. 63 of the window, 2-3 k 64 .. 127.  Where
+      // both halves lie in one scale block (always, for block_size % 128 ==
+      // 0) the four MFMAs make one sum; otherwise each half has its own sum
+      // and scale (uniform branch).  The lane holds column n and rows
+      // 4g .. 4g + 3.
+      f32x4 lo = f32x4{0.f, 0.f, 0.f, 0.f};
+      lo = Tr::mfma(a[0], Tr::decode8_fp8(w0.x, w0.y), lo);
+      lo = Tr::mfma(a[1], Tr::decode8_fp8(w0.z, w0.w), lo);
+      if (c_lo == c_hi) {
+        lo = Tr::mfma(a[2], Tr::decode8_fp8(w1.x, w1.y), lo);
+        lo = Tr::mfma(a[3], Tr::decode8_fp8(w1.z, w1.w), lo);
 #pragma unroll
-      for (int i = 0; i < R; ++i) acc[i] = fmaf(blk[i], sc, acc[i]);
+        for (int i = 0; i < R; ++i) acc[i] = fmaf(lo[i], s_lo, acc[i]);
+      } else {
+        const float s_hi = *reinterpret_cast<const float*>(slice + kSlicePitch * li + 4 * (c_hi - c0));
+        f32x4 hi = f32x4{0.f, 0.f, 0.f, 0.f};
+        hi = Tr::mfma(a[2], Tr::decode8_fp8(w1.x, w1.y), hi);
+        hi = Tr::mfma(a[3], Tr::decode8_fp8(w1.z, w1.w), hi);
+#pragma unroll
+        for (int i = 0; i < R; ++i) acc[i] = fmaf(hi[i], s_hi, fmaf(lo[i], s_lo, acc[i]));
+      }
     } else {
       if (j % SU == 0) {
-        auto realign = [&](const u32x4& v, uint32_t t) {
-          return u32x4{__builtin_amdgcn_alignbyte(v.y, v.x, sc_shift), __builtin_amdgcn_alignbyte(v.z, v.y, sc_shift),
-                       __builtin_amdgcn_alignbyte(v.w, v.z, sc_shift), __builtin_amdgcn_alignbyte(t, v.w, sc_shift)};
-        };
-        *reinterpret_cast<u32x4*>(slice + kSlicePitch * lr + 16 * lc) = realign(r.sc[0], r.sct[0]);
-        *reinterpret_cast<u32x4*>(slice + kSlicePitch * (8 + lr) + 16 * lc) = realign(r.sc[1], r.sct[1]);
+        // The piece (scale columns 16u .. 16u + 127 of rows lr and 8 + lr)
+        // goes to the slice realigned where rows start off a dword, and with
+        // the bytes past the row's last column set to E4M3 zero: they belong
+        // to the next row and may hold a NaN code (windows past the row, or a
+        // last window of 32, 64 or 96 k).  Both steps are skipped where they
+        // change nothing (uniform branches).
+        u32x4 v0 = r.sc[0], v1 = r.sc[1];
+        if (srow_bytes & 3u) {
+          auto realign = [&](const u32x4& v, uint32_t t) {
+            return u32x4{__builtin_amdgcn_alignbyte(v.y, v.x, sc_shift), __builtin_amdgcn_alignbyte(v.z, v.y, sc_shift),
+                         __builtin_amdgcn_alignbyte(v.w, v.z, sc_shift), __builtin_amdgcn_alignbyte(t, v.w, sc_shift)};
+          };
+          v0 = realign(v0, r.sct[0]);
+          v1 = realign(v1, r.sct[1]);
+        }
+        if (16 * u + 128 > cols) {
+          const int vb = cols - 16 * u - 16 * lc;  // valid bytes of the lane's 16
+          u32x4 m;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const int nv = vb - 4 * d;
+            m[d] = nv >= 4 ? ~0u : nv <= 0 ? 0u : (1u << (8 * nv)) - 1u;
+          }
+          v0 &= m;
+          v1 &= m;
+        }
+        *reinterpret_cast<u32x4*>(slice + kSlicePitch * lr + 16 * lc) = v0;
+        *reinterpret_cast<u32x4*>(slice + kSlicePitch * (8 + lr) + 16 * lc) = v1;
       }
       if constexpr (ACT_REG) {
 #pragma unroll
@@ -423,16 +482,8 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const int w = 2 * u + s2;
-        const int wa = min(w, NW - 1);  // windows past NW meet zero scales
-        // the slice bytes are always readable; scale bytes past the row's
-        // last column (a last window of 32, 64 or 96 k, or a window past NW)
-        // are masked to E4M3 zero: they belong to the next row and may hold
-        // a NaN code (a uniform mask instead of a branch)
-        const int nb = cols - 8 * w;  // scale bytes of this window inside the row
-        const uint32_t keep_lo = nb >= 4 ? ~0u : nb <= 0 ? 0u : (1u << (8 * nb)) - 1u;
-        const uint32_t keep_hi = nb >= 8 ? ~0u : nb <= 4 ? 0u : (1u << (8 * (nb - 4))) - 1u;
-        const u32x2 sr = *reinterpret_cast<const u32x2*>(slice + kSlicePitch * li + 8 * (2 * (j % SU) + s2));
-        const u32x2 sb = u32x2{sr.x & keep_lo, sr.y & keep_hi};
+        const int wa = min(w, NW - 1);  // windows past NW meet zero scales (zeroed in the slice)
+        const u32x2 sb = *reinterpret_cast<const u32x2*>(slice + kSlicePitch * li + 8 * (2 * (j % SU) + s2));
         // activations of the lane: 4 x 16 bytes per row half; chunk i = 2s + p
         // holds k 32g + 16s + 8p .. + 7 of the window (piece p of set s)
         u32x4 av[R][4];
@@ -718,7 +769,7 @@ int launch_t(const MatmulArgs& a) {
   const Plan p = cached_plan<T, FP8>(a.N, M, R, NW);
   const int tiles = static_cast<int>((a.N + 15) / 16);
   const size_t lds = lds_bytes(p.mode, FP8, M, NW);
-  const FastDiv wpb = make_fastdiv(FP8 ? static_cast<uint32_t>(a.block_size / 128) : 1u);
+  const FastDiv wpb = make_fastdiv(FP8 ? static_cast<uint32_t>(a.block_size / 64) : 1u);  // FP8: halves per block
   const FastDiv cpr = make_fastdiv(static_cast<uint32_t>(NW) * 16u + 1u);  // 16-byte chunks per LDS row
   if (p.mode == 2)
     launch_mode<T, FP8, 2>(a, p, R, lds, wpb, cpr, tiles);

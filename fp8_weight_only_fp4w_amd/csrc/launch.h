@@ -91,7 +91,7 @@ int launch_fp4_skinny(const MatmulArgs& a);
 // any validated FP4 arguments (K may be 0)
 int launch_fp4_generic(const MatmulArgs& a);
 
-// 1 <= M <= 8, block_size % 128 == 0, K % 128 == 0, A / B 16-byte aligned,
+// 1 <= M <= 8, block_size % 64 == 0, K % 16 == 0, A / B 16-byte aligned,
 // scales 4-byte aligned.
 int launch_fp8_gemv(const MatmulArgs& a);
 // M >= 1, block_size % 64 == 0, K % 64 == 0, A / B 16-byte aligned.

@@ -62,7 +62,7 @@ typedef enum {
   FP4W_PATH_FP4_GEMV = 2,        /* MFMA decode GEMV: 1 <= M <= 8, block_size 16, K % 32 == 0 */
   FP4W_PATH_FP4_GEMM = 3,        /* fused MFMA prefill GEMM: block_size 16, K % 64 == 0 */
   FP4W_PATH_FP4_GENERIC = 4,     /* any legal FP4 arguments */
-  FP4W_PATH_FP8_GEMV = 5,        /* MFMA decode GEMV: 1 <= M <= 8, block_size % 128 == 0, K % 128 == 0 */
+  FP4W_PATH_FP8_GEMV = 5,        /* MFMA decode GEMV: 1 <= M <= 8, block_size % 64 == 0, K % 16 == 0 */
   FP4W_PATH_FP8_GEMM = 6,        /* MFMA prefill GEMM: block_size % 64 == 0, K % 64 == 0 */
   FP4W_PATH_FP8_GENERIC = 7,     /* any legal FP8 arguments */
   FP4W_PATH_DEQUANT_VEC = 8,     /* vectorised dequant: K % 8 == 0, block_size % 8 == 0 */

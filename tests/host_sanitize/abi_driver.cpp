@@ -51,6 +51,7 @@ int main() {
   const Case fp8_cases[] = {
       {4, 17408, 5120, 128, "launch_fp8_gemv"}, {40, 300, 512, 128, "launch_fp8_skinny"},
       {300, 520, 640, 128, "launch_fp8_gemm"},  {3, 21, 37, 16, "launch_fp8_generic"},
+      {4, 300, 208, 64, "launch_fp8_gemv"},     {4, 300, 256, 32, "launch_fp8_generic"},
   };
   for (const Case& c : fp8_cases) {
     fp4w::g_last = "";

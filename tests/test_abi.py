@@ -105,8 +105,11 @@ def test_dispatch_fp8():
     assert sel(F, 65, 4096, 4096, 128) == fw.PATH_FP8_GEMM
     assert sel(F, 16, 4096, 4096, 64) == fw.PATH_FP8_GEMM         # skinny needs bs % 128
     assert sel(F, 64, 256, 256, 64) == fw.PATH_FP8_GEMM
-    assert sel(F, 4, 256, 256, 64) == fw.PATH_FP8_GENERIC      # GEMV needs bs % 128
-    assert sel(F, 4, 256, 208, 128) == fw.PATH_FP8_GENERIC     # K % 128 != 0
+    # the GEMV takes block_size % 64 == 0 and K % 16 == 0 ([FP8 doc] §3-4)
+    assert sel(F, 4, 256, 256, 64) == fw.PATH_FP8_GEMV
+    assert sel(F, 4, 256, 208, 128) == fw.PATH_FP8_GEMV
+    assert sel(F, 4, 256, 256, 32) == fw.PATH_FP8_GENERIC      # block_size % 64 != 0
+    assert sel(F, 4, 256, 200, 64) == fw.PATH_FP8_GENERIC      # K % 16 != 0
     assert sel(F, 64, 256, 208, 128) == fw.PATH_FP8_GENERIC
     assert sel(F, 3, 256, 37, 16) == fw.PATH_FP8_GENERIC       # odd K is legal for FP8
     assert sel(F, 0, 256, 256, 128) == fw.PATH_NONE

@@ -226,8 +226,14 @@ FP8_CASES = [
     (20, 20000, 1024, 128, "bf16", False, "ceil", [fw.PATH_FP8_SKINNY]),
     (64, 256, 448, 64, "fp16", False, "ceil", [fw.PATH_FP8_GEMM]),
     (33, 100, 320, 128, "bf16", True, "floor", [fw.PATH_FP8_GEMM, fw.PATH_FP8_GENERIC]),  # partial block
-    (5, 40, 208, 128, "bf16", True, "ceil", [fw.PATH_FP8_GENERIC]),
-    (5, 40, 208, 128, "fp16", True, "floor", [fw.PATH_FP8_GENERIC]),
+    # GEMV: K % 128 != 0 (a last window of 80 k), block size 64 (two scale
+    # blocks per 128-k window), partial final blocks in both column counts
+    (5, 40, 208, 128, "bf16", True, "ceil", [fw.PATH_FP8_GEMV, fw.PATH_FP8_GENERIC]),
+    (5, 40, 208, 128, "fp16", True, "floor", [fw.PATH_FP8_GEMV, fw.PATH_FP8_GENERIC]),
+    (4, 1000, 512, 64, "bf16", True, "ceil", [fw.PATH_FP8_GEMV]),
+    (8, 300, 5136, 64, "fp16", False, "ceil", [fw.PATH_FP8_GEMV]),
+    (3, 500, 4000, 192, "bf16", True, "floor", [fw.PATH_FP8_GEMV]),
+    (4, 300, 17424, 64, "bf16", True, "ceil", [fw.PATH_FP8_GEMV]),  # streamed activations
     (3, 21, 37, 16, "bf16", True, "ceil", [fw.PATH_FP8_GENERIC]),
     # GEMV activation modes: streamed from L2 (K = 17408), shallow ring (8 rows)
     (4, 300, 17408, 128, "bf16", True, "ceil", [fw.PATH_FP8_GEMV]),
@@ -250,6 +256,7 @@ def test_fp8_matmul_parity(M, N, K, bs, dtype, bias, partial, paths):
 
 @pytest.mark.parametrize("M,N,K,bs,path", [
     (8, 64, 512, 128, fw.PATH_FP8_GEMV), (3, 40, 384, 256, fw.PATH_FP8_GEMV),
+    (8, 64, 512, 64, fw.PATH_FP8_GEMV), (4, 40, 208, 64, fw.PATH_FP8_GEMV),
     (16, 300, 512, 128, fw.PATH_FP8_GEMM), (40, 64, 208, 128, fw.PATH_FP8_GENERIC),
     (24, 64, 512, 128, fw.PATH_FP8_SKINNY), (50, 33, 640, 128, fw.PATH_FP8_SKINNY),
 ])
@@ -262,6 +269,22 @@ def test_fp8_one_hot_probe_bit_exact(M, N, K, bs, path):
     want = ref.dequant_fp8_output_bits(p.B, p.b_scale, bs, "bf16")[:, ks].T
     got = run_fp8(p, path=path)
     assert_bits_equal(got, want, f"one-hot fp8 path {path}", zero_sign=False)
+
+
+@pytest.mark.parametrize("K,bs", [(208, 128), (144, 64), (5136, 64)])
+def test_fp8_gemv_partial_window_masks_next_row_weights(K, bs):
+    """K % 128 != 0: the last 128-k window of a weight row reads the bytes
+    past the row, which are the next row's first E4M3 codes.  Every odd row
+    starts with 64 NaN codes (0x7F): the odd rows' outputs are NaN (their own
+    codes), and the even rows' outputs must stay finite and within tolerance
+    (the kernel zeroes the bytes past K before decoding them)."""
+    require_gpu()
+    p = workloads.make_fp8(4, 96, K, bs, "bf16", seed=K, with_bias=True)
+    p.B[1::2, :64] = 0x7F
+    Y_ref, S = ref_fp8(p)
+    assert np.isnan(Y_ref[:, 1::2]).all() and np.isfinite(Y_ref[:, 0::2]).all()
+    for path in (fw.PATH_FP8_GEMV, fw.PATH_FP8_GENERIC):
+        assert_parity(run_fp8(p, path=path), "bf16", Y_ref, S, f"fp8 K={K} bs={bs} NaN next-row codes path {path}")
 
 
 @pytest.mark.parametrize("M,K,row_powers,paths", [
