@@ -13,11 +13,16 @@ steps each, so host launch overhead does not sit between the kernels.
                activations, bias, output) per launch / mean launch time
                (timed region / launches, HIP events on the launch stream),
                against the 8 TB/s HBM3E peak
-    cpu_baseline = the CPU oracle on the same workload (GB/s of weights)
+    cpu_baseline = the CPU oracle on the same workload (GB/s of weights), plus
+               one oracle call on 64 rows of each M = 8192 prefill workload
+               (TFLOP/s of that sample, full-size time extrapolated)
 
-"extra" reports the other workloads (small FP16 GEMV, FP4 prefill GEMM with
-the dequant + hipBLASLt baseline beside it, FP8 GEMV and prefill, wide-output
-GEMV, the dequant kernel) and a measured HBM copy bandwidth.
+"extra" reports the spread of the headline (each graph replay timed on its
+own), the other workloads (small FP16 GEMV, FP4 prefill GEMM with the dequant
++ hipBLASLt baseline beside it, FP8 GEMV and prefill, wide-output GEMV, the
+dequant kernel; prefill timed over 200 dispatches after 50 warm-up ones) and
+measured HBM read and copy rates, the read rate also at each GEMV's weight
+bytes per launch.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        [--no-extra] [--profile-kernel fp4_gemv|copy]
@@ -193,6 +198,20 @@ def gemv_decode(steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_step = start.elapsed_time(stop) / 1e3 / steps
+    # spread: each replay of a G-step graph timed on its own (events between
+    # replays), as mean microseconds per launch within that replay
+    n_rep = max(64, steps // G)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_rep)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        groups[i % n_groups].replay()
+        b.record()
+    torch.cuda.synchronize()
+    per_launch = np.array([a.elapsed_time(b) * 1e3 / (G * len(Ms)) for a, b in evs])
+    per_replay = {"replays": n_rep, "launches_per_replay": G * len(Ms),
+                  "us_per_launch_p10": round(float(np.percentile(per_launch, 10)), 3),
+                  "us_per_launch_p50": round(float(np.percentile(per_launch, 50)), 3),
+                  "us_per_launch_p90": round(float(np.percentile(per_launch, 90)), 3)}
     del groups, singles
     # algorithmic bytes of one step (four launches)
     alg = 0
@@ -210,7 +229,7 @@ def gemv_decode(steps, warmup):
         per_m[str(M)] = {"us": round(t * 1e6, 3), "weight_GBps": round(weight_bytes / t / 1e9, 1)}
         del gs
     return dict(workload=w, Ms=Ms, weight_bytes=weight_bytes, R=R, per_step=per_step, wall=wall,
-                alg_bytes_step=alg, per_m=per_m)
+                alg_bytes_step=alg, per_m=per_m, per_replay=per_replay)
 
 
 # ------------------------------------------------------------------ CPU baseline
@@ -235,10 +254,30 @@ def cpu_baseline(min_seconds=10.0):
         el = time.perf_counter() - t0
         if el >= min_seconds:
             break
-    return {"value": round(done * wb / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} oracle calls (M in {list(w.Ms)}, N=K=5120, full output) in {el:.1f} s; "
-                      f"float64 dequant + numpy BLAS dgemm; cores = BLAS threads; host has "
-                      f"{os.cpu_count()} logical CPUs, affinity {len(os.sched_getaffinity(0))}"}
+    res = {"value": round(done * wb / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"{done} oracle calls (M in {list(w.Ms)}, N=K=5120, full output) in {el:.1f} s; "
+                     f"float64 dequant + numpy BLAS dgemm; cores = BLAS threads; host has "
+                     f"{os.cpu_count()} logical CPUs, affinity {len(os.sched_getaffinity(0))}"}
+    # prefill: one oracle call on 64 rows of each M = 8192 prefill workload
+    rows = 64
+    pre = {}
+    for name, wl in (("fp4_prefill", workloads.WORKLOADS["fp4_prefill"]),
+                     ("fp8_prefill", workloads.WORKLOADS["fp8_gemv"])):
+        p = wl.make(M=rows)
+        t0 = time.perf_counter()
+        if wl.op == "fp4":
+            ref.matmul_fp4_reference(p.A, p.dtype, p.B, p.weight_scale, wl.block_size, p.weight_scale_2, p.bias)
+        else:
+            ref.matmul_fp8_reference(p.A, p.dtype, p.B, p.b_scale, wl.block_size, p.bias)
+        el = time.perf_counter() - t0
+        full_m = 8192
+        pre[name] = {"value": round(2.0 * rows * wl.N * wl.K / el / 1e12, 6), "unit": "TFLOP/s",
+                     "sample_rows": rows, "sample_s": round(el, 2),
+                     "extrapolated_full_call_s": round(el * full_m / rows, 1),
+                     "extrapolation": f"linear in M from {rows} to {full_m} rows (the oracle's weight decode, "
+                                      f"paid once per call, is counted {full_m // rows} times: an upper bound)"}
+    res["prefill_sampled"] = pre
+    return res
 
 
 # ------------------------------------------------------------------ extra workloads
@@ -252,12 +291,13 @@ def hbm_copy_gbps():
     return round(2 * n * 20 / t / 1e9, 1)
 
 
-def hbm_read(weight_bytes):
+def hbm_read(sizes):
     """Measured HBM read rate from this repository's read-stream kernel
-    (libhbmprobe.so): the peak over a 4 GiB buffer, and the rate at the
-    headline's weight bytes per launch over 72 rotated slices (1.06 GB, past
-    the last-level cache) launched back to back from a HIP graph.  Each is the
-    best over grid sizes and loads in flight per thread."""
+    (libhbmprobe.so): the peak over a 4 GiB buffer, and for each entry of
+    `sizes` (name -> bytes per launch) the rate at that many bytes per launch
+    over enough rotated slices to pass 1 GiB (past the last-level cache),
+    launched back to back from a HIP graph.  Each is the best over grid sizes
+    and loads in flight per thread."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "fp8_weight_only_fp4w_amd", "libhbmprobe.so"))
     lib.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_uint32,
@@ -280,29 +320,32 @@ def hbm_read(weight_bytes):
         for u in unrolls:
             t = time_calls([lambda g=g, u=u: launch(buf.data_ptr(), big_bytes, g, u)], 10, 2)
             peak[f"grid{g}_u{u}"] = round(big_bytes * 10 / t / 1e9, 1)
-    nb = weight_bytes - weight_bytes % 16
-    slices = 72
-    at_size = {}
-    for g in grids:
-        for u in unrolls:
-            def body(g=g, u=u):
-                for i in range(slices):
-                    launch(buf.data_ptr() + i * nb, nb, g, u)
-            body()
-            torch.cuda.synchronize()
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
+    res = {"peak_GBps": max(peak.values()), "peak_config": max(peak, key=peak.get), "buffer_bytes": big_bytes,
+           "sweep_4GiB": peak, "at_size": {}}
+    for name, nbytes in sizes.items():
+        nb = nbytes - nbytes % 16
+        slices = max(2, -(-ROTATE_BYTES // nb))
+        assert slices * nb <= big_bytes
+        sweep = {}
+        for g in grids:
+            for u in unrolls:
+                def body(g=g, u=u):
+                    for i in range(slices):
+                        launch(buf.data_ptr() + i * nb, nb, g, u)
                 body()
-            graph.replay()
-            torch.cuda.synchronize()
-            t = time_calls([graph.replay], 5, 1)
-            at_size[f"grid{g}_u{u}"] = round(nb * slices * 5 / t / 1e9, 1)
+                torch.cuda.synchronize()
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph):
+                    body()
+                graph.replay()
+                torch.cuda.synchronize()
+                t = time_calls([graph.replay], 5, 1)
+                sweep[f"grid{g}_u{u}"] = round(nb * slices * 5 / t / 1e9, 1)
+                del graph
+        res["at_size"][name] = {"bytes": nb, "slices": slices, "GBps": max(sweep.values()),
+                                "config": max(sweep, key=sweep.get), "sweep": sweep}
     del buf, sink
-    best = max(peak.values())
-    best_sz = max(at_size.values())
-    return {"peak_GBps": best, "peak_config": max(peak, key=peak.get), "buffer_bytes": big_bytes,
-            "at_headline_size_GBps": best_sz, "at_headline_size_config": max(at_size, key=at_size.get),
-            "at_headline_size_bytes": nb, "sweep_4GiB": peak, "sweep_headline_size": at_size}
+    return res
 
 
 def extra_small_gemv(steps, warmup):
@@ -315,7 +358,7 @@ def extra_small_gemv(steps, warmup):
     return {"us_per_call": round(t * 1e6, 3), "note": "75 KB working set, L2-resident"}
 
 
-def extra_prefill_fp4(reps=10, warmup=3):
+def extra_prefill_fp4(reps=200, warmup=50):
     w = workloads.WORKLOADS["fp4_prefill"]
     p = w.make()
     d = fp4_on_device(p)
@@ -324,8 +367,7 @@ def extra_prefill_fp4(reps=10, warmup=3):
     t = time_calls([lambda: fw.fp4w_matmul(d["A"], d["B"][0], d["ws"][0], d["ws2"], None, 16, out=out)],
                    reps, warmup) / reps
     res = {"fused_ms": round(t * 1e3, 3), "fused_TFLOPs": round(flops / t / 1e12, 1),
-           "fused_frac_of_bf16_peak": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4),
-           "clocks_after_fused": read_clocks()}
+           "fused_frac_of_bf16_peak": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
     # baseline: dequant to a [N, K] scratch, then hipBLASLt (torch.matmul)
     scratch = torch.empty(p.N, p.K, dtype=torch.bfloat16, device="cuda")
 
@@ -335,16 +377,17 @@ def extra_prefill_fp4(reps=10, warmup=3):
 
     tb = time_calls([base], reps, warmup) / reps
     td = time_calls([lambda: fw.fp4w_dequant(d["B"][0], d["ws"][0], d["ws2"], 16, out=scratch)],
-                    reps * 5, warmup) / (reps * 5)
+                    reps, warmup) / reps
     dq_bytes = p.B.nbytes + p.weight_scale.nbytes + scratch.numel() * 2
     res.update({"baseline_dequant_plus_hipblaslt_ms": round(tb * 1e3, 3),
                 "baseline_TFLOPs": round(flops / tb / 1e12, 1),
+                "fused_over_baseline_time": round(t / tb, 4), "dispatches": {"warmup": warmup, "timed": reps},
                 "dequant_ms": round(td * 1e3, 4), "dequant_GBps": round(dq_bytes / td / 1e9, 1)})
     del scratch
     return res
 
 
-def extra_fp8(steps, warmup, reps=10):
+def extra_fp8(steps, warmup, reps=200, pre_warmup=50):
     w = workloads.WORKLOADS["fp8_gemv"]
     p = w.make(M=4)
     wb = p.B.nbytes + p.b_scale.nbytes
@@ -358,8 +401,11 @@ def extra_fp8(steps, warmup, reps=10):
     d = fp8_on_device(p8)
     out = torch.empty(8192, p8.N, dtype=torch.bfloat16, device="cuda")
     flops = 2.0 * p8.M * p8.N * p8.K
-    tp = time_calls([lambda: fw.fp8w_matmul(d["A"], d["B"][0], d["bs"][0], None, 128, out=out)], reps, 3) / reps
-    res.update({"prefill_ms": round(tp * 1e3, 3), "prefill_TFLOPs": round(flops / tp / 1e12, 1)})
+    tp = time_calls([lambda: fw.fp8w_matmul(d["A"], d["B"][0], d["bs"][0], None, 128, out=out)],
+                    reps, pre_warmup) / reps
+    res.update({"prefill_ms": round(tp * 1e3, 3), "prefill_TFLOPs": round(flops / tp / 1e12, 1),
+                "prefill_frac_of_bf16_peak": round(flops / tp / 1e12 / BF16_PEAK_TFLOPS, 4),
+                "prefill_dispatches": {"warmup": pre_warmup, "timed": reps}})
     # the pages' default path: dequant to an [N, K] scratch, then hipBLASLt (torch.matmul)
     scratch = torch.empty(p8.N, p8.K, dtype=torch.bfloat16, device="cuda")
 
@@ -367,11 +413,12 @@ def extra_fp8(steps, warmup, reps=10):
         fw.fp8w_dequant(d["B"][0], d["bs"][0], 128, out=scratch)
         torch.matmul(d["A"], scratch.t(), out=out)
 
-    tb = time_calls([base], reps, 3) / reps
-    td = time_calls([lambda: fw.fp8w_dequant(d["B"][0], d["bs"][0], 128, out=scratch)], reps * 5, 3) / (reps * 5)
+    tb = time_calls([base], reps, pre_warmup) / reps
+    td = time_calls([lambda: fw.fp8w_dequant(d["B"][0], d["bs"][0], 128, out=scratch)], reps, pre_warmup) / reps
     dq_bytes = p8.B.nbytes + p8.b_scale.nbytes + scratch.numel() * 2
     res.update({"prefill_baseline_dequant_plus_hipblaslt_ms": round(tb * 1e3, 3),
                 "prefill_baseline_TFLOPs": round(flops / tb / 1e12, 1),
+                "prefill_over_baseline_time": round(tp / tb, 4),
                 "dequant_ms": round(td * 1e3, 4), "dequant_GBps": round(dq_bytes / td / 1e9, 1)})
     del scratch
     return res
@@ -519,26 +566,6 @@ def extra_decode_step(steps, warmup):
 
 # ------------------------------------------------------------------ profiling mode
 
-def read_clocks():
-    """Shader (per XCD) and memory clocks from amd-smi, run as a child
-    process right after a timed region; None where amd-smi is unavailable."""
-    import subprocess
-    try:
-        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True, text=True,
-                           timeout=30)
-        data = json.loads(r.stdout)
-        gpu = data["gpu_data"][0] if isinstance(data, dict) else data[0]
-        clk = gpu["clock"]
-        val = lambda e, k: e.get(k, {}).get("value") if isinstance(e.get(k), dict) else None
-        gfx = [val(e, "clk") for k, e in sorted(clk.items()) if k.startswith("gfx")]
-        out = {"gfx_MHz": gfx, "gfx_max_MHz": next((val(e, "max_clk") for k, e in clk.items() if k.startswith("gfx")), None),
-               "mem_MHz": next((val(e, "clk") for k, e in clk.items() if k.startswith("mem")), None),
-               "source": "amd-smi metric -c, sampled right after a timed region"}
-        return out
-    except Exception as e:  # noqa: BLE001 - a missing tool only loses this record
-        return {"error": f"{type(e).__name__}: {e}"[:200]}
-
-
 def profile_kernel(which, launches=50):
     """Launch one kernel `launches` times without graphs, for rocprofv3 runs
     (kernel trace or PMC counters).  Weight copies rotate as in the timed runs."""
@@ -670,10 +697,13 @@ def main():
                 "kernel": "fp4_gemv_kernel (MFMA decode GEMV)",
                 "alg_bytes_per_launch": round(alg_per_launch), "mean_launch_us": round(mean_launch * 1e6, 3)}
 
-    extra = {"per_M": h["per_m"], "weight_copies": h["R"], "clocks": read_clocks()}
-    rd = hbm_read(h["weight_bytes"])
+    extra = {"per_M": h["per_m"], "weight_copies": h["R"], "per_replay": h["per_replay"]}
+    w8, ww = workloads.WORKLOADS["fp8_gemv"], workloads.WORKLOADS["fp4_gemv_wide"]
+    rd = hbm_read({"fp4_gemv_decode": h["weight_bytes"],
+                   "fp8_gemv": w8.N * w8.K + w8.N * (w8.K // w8.block_size) * 4,
+                   "fp4_gemv_wide": ww.N * ww.K // 2 + ww.N * (ww.K // 16)})
     rd["headline_frac_of_peak"] = round(value / rd["peak_GBps"], 4)
-    rd["headline_frac_at_size"] = round(value / rd["at_headline_size_GBps"], 4)
+    rd["headline_frac_at_size"] = round(value / rd["at_size"]["fp4_gemv_decode"]["GBps"], 4)
     extra["hbm_read"] = rd
     torch.cuda.empty_cache()
     log(f"hbm_read: {rd}")
@@ -695,11 +725,15 @@ def main():
             log(f"{name}: {extra[name]} ({time.perf_counter() - t0:.1f} s)")
 
     # the bandwidth-bound GEMV extras against the measured read peak
-    peak_rd = extra["hbm_read"]["peak_GBps"]
+    peak_rd = rd["peak_GBps"]
     if "fp4_gemv_wide" in extra:
-        extra["fp4_gemv_wide"]["frac_of_measured_read_peak"] = round(extra["fp4_gemv_wide"]["weight_GBps"] / peak_rd, 4)
+        gb = extra["fp4_gemv_wide"]["weight_GBps"]
+        extra["fp4_gemv_wide"]["frac_of_measured_read_peak"] = round(gb / peak_rd, 4)
+        extra["fp4_gemv_wide"]["frac_of_read_at_size"] = round(gb / rd["at_size"]["fp4_gemv_wide"]["GBps"], 4)
     if "fp8" in extra:
-        extra["fp8"]["gemv_M4_frac_of_measured_read_peak"] = round(extra["fp8"]["gemv_M4_weight_GBps"] / peak_rd, 4)
+        gb = extra["fp8"]["gemv_M4_weight_GBps"]
+        extra["fp8"]["gemv_M4_frac_of_measured_read_peak"] = round(gb / peak_rd, 4)
+        extra["fp8"]["gemv_M4_frac_of_read_at_size"] = round(gb / rd["at_size"]["fp8_gemv"]["GBps"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:
