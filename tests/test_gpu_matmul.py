@@ -41,14 +41,20 @@ FP4_CASES = [
     (8, 777, 1024, 16, "bf16", False, "ceil", [fw.PATH_FP4_GEMV, fw.PATH_FP4_GEMM]),
     (5, 65590, 128, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMV]),  # 2 tiles per wave, ragged N
     (9, 300, 128, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMM, fw.PATH_FP4_GENERIC]),
-    # ragged M and N; 2 x 3 tiles and K % 128 == 0, so every tile is split over
-    # two workgroups (row halves, K halves added in LDS), one half past M
+    # GEMM tiles are 256 x 256; a last round of at most half the CUs' worth
+    # of tiles runs as 256 x 128 halves.  Ragged M and N in 2 x 3 tiles (all
+    # halves, the last column's second half past N); one tile row past M.
     (300, 700, 640, 16, "fp16", True, "ceil", [fw.PATH_FP4_GEMM]),
     (513, 256, 64, 16, "bf16", False, "ceil", [fw.PATH_FP4_GEMM]),
-    # 3 x 8 = 24 tiles of 256 x 256 (a multiple of 8: the XCD tile remap is
-    # active), ragged M and N, an odd number of K steps; the last column tile
-    # takes the element-wise epilogue, the others the 16-byte one
+    # 3 x 8 = 24 tiles, an odd number of K steps; the last column tile takes
+    # the element-wise epilogue, the others the 16-byte one
     (700, 1800, 448, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMM]),
+    # 2 x 70 = 140 tiles: more than half of 256 CUs, all whole tiles (the XCD
+    # tile remap is active: 140 % 8 != 0 leaves it off, so also below)
+    (300, 17920, 128, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMM]),
+    # 3 x 102 = 306 tiles: 256 whole ones (grid a multiple of 8: XCD remap
+    # on) and 50 as halves, among them the ragged last tile column
+    (600, 26012, 192, 16, "fp16", True, "ceil", [fw.PATH_FP4_GEMM]),
     # skinny kernel: 1, 2 and 4 row tiles, ragged M and N, one window per
     # wave (K = 128), long K, the persistent loop over many tiles
     (9, 300, 256, 16, "bf16", True, "ceil", [fw.PATH_FP4_SKINNY, fw.PATH_FP4_GEMM]),
