@@ -41,6 +41,12 @@ Pins (tests/test_oracle_*.py, run with -m "not gpu"):
                                  and invariants (K-block permutation, sign
                                  flip, ws2 doubling, bias shift).
 * ``reference.matmul_tolerance`` exact result passes, perturbed result fails.
+* ``nvfp4.*``                    (the W4A4 path of [FP4 doc] §6) hand-derived
+                                 blocks (tests/golden), a brute-force E2M1
+                                 nearest-value search, exact round trips of
+                                 representable activations, the quantization
+                                 error bound, block independence, NaN / inf
+                                 confinement, and exact rational W4A4 sums.
 
 No function here is "parity unpinned".
 """
@@ -66,4 +72,10 @@ from .reference import (  # noqa: F401
     matmul_tolerance,
     scale_column,
     unpack_e2m1_codes,
+)
+from .nvfp4 import (  # noqa: F401
+    e2m1_encode,
+    matmul_w4a4_reference,
+    qdq_activation_nvfp4_bits,
+    quantize_activation_nvfp4,
 )
