@@ -20,7 +20,8 @@ steps each, so host launch overhead does not sit between the kernels.
 "extra" reports the spread of the headline (each graph replay timed on its
 own), the other workloads (small FP16 GEMV, FP4 prefill GEMM with the dequant
 + hipBLASLt baseline beside it, FP8 GEMV and prefill, wide-output GEMV, the
-dequant kernel; prefill timed over 200 dispatches after 50 warm-up ones) and
+dequant kernel, the W8A8 and W4A4 modes; prefill timed over 200 dispatches
+after 50 warm-up ones) and
 measured HBM read and copy rates, the read rate also at each GEMV's weight
 bytes per launch.
 
@@ -494,6 +495,45 @@ def extra_w8a8(steps, warmup):
     return res
 
 
+def extra_w4a4(steps, warmup, reps=50):
+    """W4A4 ([FP4 doc] §6): the NVFP4 activation kernels alone at the prefill
+    activation shape (M = 8192, K = 5120), and the whole W4A4 matmul (QDQ
+    into a workspace + the FP4 matmul) at the prefill workload and at the
+    decode workload (M = 4)."""
+    res = {}
+    A = torch.randn(8192, 5120, device="cuda").to(torch.bfloat16)
+    work = torch.empty_like(A)
+    codes = torch.empty(8192, 2560, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(8192, 320, dtype=torch.uint8, device="cuda")
+    tq = time_calls([lambda: fw.fp4w_qdq_activation(A, out=work)], reps, 5) / reps
+    tp = time_calls([lambda: fw.fp4w_quantize_activation(A, codes, scales)], reps, 5) / reps
+    n = A.numel()
+    res["qdq_M8192_K5120"] = {"us": round(tq * 1e6, 2), "GBps": round(4 * n / tq / 1e9, 1)}
+    res["quantize_M8192_K5120"] = {"us": round(tp * 1e6, 2), "GBps": round((2 * n + n / 2 + n / 16) / tp / 1e9, 1)}
+    del A, work, codes, scales
+    p = workloads.WORKLOADS["fp4_prefill"].make()
+    d = fp4_on_device(p)
+    work = torch.empty_like(d["A"])
+    out = torch.empty(p.M, p.N, dtype=torch.bfloat16, device="cuda")
+    flops = 2.0 * p.M * p.N * p.K
+    tw = time_calls([lambda: fw.fp4w_matmul_w4a4(d["A"], d["B"][0], d["ws"][0], d["ws2"], None, 16, out=out,
+                                                 workspace=work)], 20, 5) / 20
+    res["prefill_ms"] = round(tw * 1e3, 3)
+    res["prefill_TFLOPs"] = round(flops / tw / 1e12, 1)
+    del d, work, out
+    w = workloads.WORKLOADS["fp4_gemv_decode"]
+    p4 = w.make(M=4)
+    wb = p4.B.nbytes + p4.weight_scale.nbytes
+    R = copies_for(wb)
+    d = fp4_on_device(p4, copies=R)
+    work = torch.empty_like(d["A"])
+    out = torch.empty(4, w.N, dtype=torch.bfloat16, device="cuda")
+    t4 = time_rotating(lambda r: fw.fp4w_matmul_w4a4(d["A"], d["B"][r], d["ws"][r], d["ws2"], d["bias"], 16,
+                                                      out=out, workspace=work), R, steps)
+    res["decode_M4_N5120_K5120_us"] = round(t4 * 1e6, 2)
+    return res
+
+
 def extra_mid_m(steps, warmup):
     """FP4 matmul through the default dispatch at prompt-chunk sizes M = 64 ..
     1024 (N = 17408, K = 5120): where the skinny kernel hands over to the
@@ -713,6 +753,7 @@ def main():
                          ("fp4_gemv_wide", lambda: extra_wide(args.steps, args.warmup)),
                          ("fp8", lambda: extra_fp8(args.steps, args.warmup)),
                          ("fp8_w8a8", lambda: extra_w8a8(args.steps, args.warmup)),
+                         ("fp4_w4a4", lambda: extra_w4a4(args.steps, args.warmup)),
                          ("skinny", lambda: extra_skinny(args.steps, args.warmup)),
                          ("decode_step", lambda: extra_decode_step(args.steps, args.warmup)),
                          ("mid_m", lambda: extra_mid_m(args.steps, args.warmup)),

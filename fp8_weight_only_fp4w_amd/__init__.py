@@ -23,6 +23,12 @@ The functions carry the C ABI's names (include/fp4w.h):
   document §6).
 * ``fp8w_matmul_w8a8(A, B, b_scale, a_scale, bias=None, block_size=128)``:
   that step into a workspace, then ``fp8w_matmul`` on it.
+* ``fp4w_quantize_activation(A)``: (codes [M, K/2], scales [M, K/16]), the
+  NVFP4 activation of the FP4 operator's native FP4 x FP4 path (FP4 document
+  §6, Native SM120 FP4 x FP4 Path); ``fp4w_qdq_activation(A)``: the same,
+  decoded back to A's dtype.
+* ``fp4w_matmul_w4a4(A, B, weight_scale, weight_scale_2, bias=None,
+  block_size=16)``: that activation times the FP4 weights (W4A4).
 
 A keeps any leading dimensions; Y has A's leading dimensions, last dimension
 N and A's dtype.
@@ -46,14 +52,17 @@ PATH_DEQUANT_VEC, PATH_DEQUANT_GENERIC = 8, 9
 PATH_QDQ_VEC, PATH_QDQ_GENERIC = 10, 11
 PATH_FP4_SKINNY, PATH_FP8_SKINNY = 12, 13
 PATH_FP8_DEQUANT_VEC, PATH_FP8_DEQUANT_GENERIC = 14, 15
+PATH_NVFP4_VEC, PATH_NVFP4_GENERIC = 16, 17
 # operations (fp4w_op)
-OP_FP4_MATMUL, OP_FP8_MATMUL, OP_FP4_DEQUANT, OP_FP8_QDQ, OP_FP8_DEQUANT = 0, 1, 2, 3, 4
+OP_FP4_MATMUL, OP_FP8_MATMUL, OP_FP4_DEQUANT, OP_FP8_QDQ, OP_FP8_DEQUANT, OP_NVFP4_ACT = 0, 1, 2, 3, 4, 5
 # dtypes (fp4w_dtype)
 F16, BF16 = 0, 1
 
 EXPORTED = (
     "fp4w_matmul", "fp4w_matmul_ex", "fp8w_matmul", "fp8w_matmul_ex", "fp4w_dequant",
     "fp4w_dequant_ex", "fp8w_dequant", "fp8w_dequant_ex", "fp8w_qdq_activation", "fp8w_qdq_activation_ex", "fp8w_matmul_w8a8",
+    "fp4w_quantize_activation", "fp4w_quantize_activation_ex", "fp4w_qdq_activation", "fp4w_qdq_activation_ex",
+    "fp4w_matmul_w4a4",
     "fp4w_select_path", "fp4w_status_string", "fp4w_path_name",
 )
 
@@ -98,6 +107,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp8w_qdq_activation.restype = i32
     lib.fp8w_matmul_w8a8.argtypes = [vp, i64, i64, vp, i64, vp, i64, i64, vp, vp, vp, vp, i32, vp]
     lib.fp8w_matmul_w8a8.restype = i32
+    lib.fp4w_quantize_activation_ex.argtypes = [vp, i64, i64, vp, vp, i32, vp, i32]
+    lib.fp4w_quantize_activation_ex.restype = i32
+    lib.fp4w_quantize_activation.argtypes = [vp, i64, i64, vp, vp, i32, vp]
+    lib.fp4w_quantize_activation.restype = i32
+    lib.fp4w_qdq_activation_ex.argtypes = [vp, i64, i64, vp, i32, vp, i32]
+    lib.fp4w_qdq_activation_ex.restype = i32
+    lib.fp4w_qdq_activation.argtypes = [vp, i64, i64, vp, i32, vp]
+    lib.fp4w_qdq_activation.restype = i32
+    lib.fp4w_matmul_w4a4.argtypes = [vp, i64, i64, vp, i64, vp, i64, i64, vp, vp, vp, vp, i32, vp]
+    lib.fp4w_matmul_w4a4.restype = i32
     lib.fp4w_select_path.argtypes = [i32, i64, i64, i64, i64, i64]
     lib.fp4w_select_path.restype = i32
     lib.fp4w_status_string.argtypes = [i32]
@@ -318,4 +337,84 @@ def fp8w_dequant(B: torch.Tensor, b_scale: torch.Tensor, block_size: int = 128,
     st = lib.fp8w_dequant_ex(_ptr(B), N, K, _ptr(b_scale), b_scale.shape[1], block_size, _ptr(out),
                              _dtype_code(out.dtype), _stream(dev), path)
     _check(st, "fp8w_dequant")
+    return out
+
+
+def _rows_k(A: torch.Tensor):
+    K = A.shape[-1] if A.dim() else 1
+    return (A.numel() // K if K else 0), K
+
+
+def fp4w_quantize_activation(A: torch.Tensor, codes: torch.Tensor = None, scales: torch.Tensor = None,
+                             path: int = PATH_AUTO):
+    """NVFP4 activation: (codes uint8 [..., K/2], scales uint8 [..., K/16])."""
+    lib = load_library()
+    dev = A.device
+    M, K = _rows_k(A)
+    _need(A, "A", dev)
+    if codes is None:
+        codes = torch.empty(*A.shape[:-1], K // 2, dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(*A.shape[:-1], K // 16, dtype=torch.uint8, device=dev)
+    for t, name, n in ((codes, "codes", K // 2), (scales, "scales", K // 16)):
+        _need(t, name, dev)
+        if t.dtype != torch.uint8 or t.numel() != M * n:
+            raise ValueError(f"{name} must be uint8 with {M * n} elements")
+    st = lib.fp4w_quantize_activation_ex(_ptr(A), M, K, _ptr(codes), _ptr(scales), _dtype_code(A.dtype),
+                                         _stream(dev), path)
+    _check(st, "fp4w_quantize_activation")
+    return codes, scales
+
+
+def fp4w_qdq_activation(A: torch.Tensor, out: torch.Tensor = None, path: int = PATH_AUTO) -> torch.Tensor:
+    """The NVFP4 activation decoded back to A's dtype; ``out`` may be ``A``."""
+    lib = load_library()
+    dev = A.device
+    M, K = _rows_k(A)
+    _need(A, "A", dev)
+    if out is None:
+        out = torch.empty_like(A)
+    _need(out, "out", dev)
+    if out.shape != A.shape or out.dtype != A.dtype:
+        raise ValueError("out must have A's shape and dtype")
+    st = lib.fp4w_qdq_activation_ex(_ptr(A), M, K, _ptr(out), _dtype_code(A.dtype), _stream(dev), path)
+    _check(st, "fp4w_qdq_activation")
+    return out
+
+
+def fp4w_matmul_w4a4(A: torch.Tensor, B: torch.Tensor, weight_scale: torch.Tensor,
+                     weight_scale_2: torch.Tensor, bias: torch.Tensor = None, block_size: int = 16,
+                     out: torch.Tensor = None, workspace: torch.Tensor = None) -> torch.Tensor:
+    """W4A4: fp4w_matmul on the NVFP4 activation of A.  ``workspace`` (A's
+    shape and dtype, or ``A`` itself) receives that activation; it is
+    allocated here when not given."""
+    lib = load_library()
+    dev = A.device
+    B, weight_scale = _bytes(B), _bytes(weight_scale)
+    K = A.shape[-1]
+    M = A.numel() // K if K else int(torch.tensor(A.shape[:-1]).prod().item())
+    N = B.shape[0]
+    if B.dim() != 2 or B.shape[1] * 2 != K:
+        raise ValueError(f"B must be [N, K/2] = [N, {K // 2}], got {tuple(B.shape)}")
+    if weight_scale.dim() != 2 or weight_scale.shape[0] != N:
+        raise ValueError("weight_scale must be [N, scale_cols]")
+    _scalar_f32(weight_scale_2, "weight_scale_2")
+    for t, name in ((A, "A"), (B, "B"), (weight_scale, "weight_scale"), (weight_scale_2, "weight_scale_2")):
+        _need(t, name, dev)
+    if bias is not None:
+        _need(bias, "bias", dev)
+        if bias.dtype != A.dtype or bias.numel() != N:
+            raise ValueError("bias must be [N] with A's dtype")
+    if workspace is None:
+        workspace = torch.empty_like(A)
+    _need(workspace, "workspace", dev)
+    if workspace.shape != A.shape or workspace.dtype != A.dtype:
+        raise ValueError("workspace must have A's shape and dtype")
+    if out is None:
+        out = torch.empty(*A.shape[:-1], N, dtype=A.dtype, device=dev)
+    _need(out, "out", dev)
+    st = lib.fp4w_matmul_w4a4(_ptr(A), M, K, _ptr(B), N, _ptr(weight_scale), weight_scale.shape[1], block_size,
+                              _ptr(weight_scale_2), _ptr(bias), _ptr(workspace), _ptr(out),
+                              _dtype_code(A.dtype), _stream(dev))
+    _check(st, "fp4w_matmul_w4a4")
     return out

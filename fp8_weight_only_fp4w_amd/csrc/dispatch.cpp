@@ -19,6 +19,7 @@ using fp4w::Act;
 using fp4w::DequantArgs;
 using fp4w::Fp8DequantArgs;
 using fp4w::MatmulArgs;
+using fp4w::Nvfp4Args;
 using fp4w::QdqArgs;
 
 // Element counts (M * K, N * K, M * N, N * scale_cols) are capped at 2^60, so
@@ -243,6 +244,50 @@ int launch_qdq(int chosen, const QdqArgs& q) {
   return rc == 0 ? FP4W_OK : FP4W_ERR_LAUNCH;
 }
 
+// NVFP4 activation quantization (W4A4 path, [FP4 doc] §6): blocks of 16
+// along K.  Validates and picks the path; *chosen_out = FP4W_PATH_NONE when
+// there is nothing to do.  packed: codes / scales are written, else out.
+bool nvfp4_shape_ok(int64_t M, int64_t K) {
+  return M >= 0 && K >= 0 && K % 16 == 0 && mul_ok(M, K) && mul_ok(M * K, 2);
+}
+
+int plan_nvfp4(const Nvfp4Args& q, int64_t M, int64_t K, bool packed, int path, int* chosen_out) {
+  const int dtype = static_cast<int>(q.act);
+  if (dtype != FP4W_F16 && dtype != FP4W_BF16) return FP4W_ERR_DTYPE;
+  if (!nvfp4_shape_ok(M, K)) return FP4W_ERR_SHAPE;
+  if (path != FP4W_PATH_AUTO && path != FP4W_PATH_NVFP4_VEC && path != FP4W_PATH_NVFP4_GENERIC)
+    return FP4W_ERR_PATH;
+  *chosen_out = FP4W_PATH_NONE;
+  if (M == 0 || K == 0) return FP4W_OK;
+  if (q.A == nullptr) return FP4W_ERR_NULL;
+  const int64_t abytes = M * K * 2;
+  bool vec = aligned(q.A, 16);
+  if (packed) {
+    if (q.codes == nullptr || q.scales == nullptr) return FP4W_ERR_NULL;
+    const int64_t cbytes = M * K / 2, sbytes = M * K / 16;
+    if (overlaps(q.codes, cbytes, q.A, abytes) || overlaps(q.scales, sbytes, q.A, abytes) ||
+        overlaps(q.codes, cbytes, q.scales, sbytes))
+      return FP4W_ERR_ALIAS;
+    vec = vec && aligned(q.codes, 8);
+  } else {
+    if (q.out == nullptr) return FP4W_ERR_NULL;
+    if (q.out != q.A && overlaps(q.out, abytes, q.A, abytes)) return FP4W_ERR_ALIAS;
+    vec = vec && aligned(q.out, 16);
+  }
+  int chosen = path;
+  if (path == FP4W_PATH_AUTO) chosen = vec ? FP4W_PATH_NVFP4_VEC : FP4W_PATH_NVFP4_GENERIC;
+  if (chosen == FP4W_PATH_NVFP4_VEC && !vec) return FP4W_ERR_PATH;
+  *chosen_out = chosen;
+  return FP4W_OK;
+}
+
+int launch_nvfp4(int chosen, const Nvfp4Args& q, bool packed) {
+  if (chosen == FP4W_PATH_NONE) return FP4W_OK;
+  const bool vec = chosen == FP4W_PATH_NVFP4_VEC;
+  const int rc = packed ? fp4w::launch_nvfp4_quantize(q, vec) : fp4w::launch_nvfp4_qdq(q, vec);
+  return rc == 0 ? FP4W_OK : FP4W_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -320,6 +365,62 @@ int fp8w_matmul_w8a8(const void* A, int64_t M, int64_t K, const uint8_t* B, int6
   return launch_matmul(mm_path, a);
 }
 
+int fp4w_quantize_activation_ex(const void* A, int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
+                                int dtype, void* stream, int path) {
+  const int64_t blocks = nvfp4_shape_ok(M, K) ? M * (K / 16) : 0;
+  Nvfp4Args q{A, codes, scales, nullptr, blocks, static_cast<Act>(dtype), stream};
+  int chosen = FP4W_PATH_NONE;
+  const int st = plan_nvfp4(q, M, K, true, path, &chosen);
+  return st != FP4W_OK ? st : launch_nvfp4(chosen, q, true);
+}
+
+int fp4w_quantize_activation(const void* A, int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
+                             int dtype, void* stream) {
+  return fp4w_quantize_activation_ex(A, M, K, codes, scales, dtype, stream, FP4W_PATH_AUTO);
+}
+
+int fp4w_qdq_activation_ex(const void* A, int64_t M, int64_t K, void* out, int dtype, void* stream,
+                           int path) {
+  const int64_t blocks = nvfp4_shape_ok(M, K) ? M * (K / 16) : 0;
+  Nvfp4Args q{A, nullptr, nullptr, out, blocks, static_cast<Act>(dtype), stream};
+  int chosen = FP4W_PATH_NONE;
+  const int st = plan_nvfp4(q, M, K, false, path, &chosen);
+  return st != FP4W_OK ? st : launch_nvfp4(chosen, q, false);
+}
+
+int fp4w_qdq_activation(const void* A, int64_t M, int64_t K, void* out, int dtype, void* stream) {
+  return fp4w_qdq_activation_ex(A, M, K, out, dtype, stream, FP4W_PATH_AUTO);
+}
+
+int fp4w_matmul_w4a4(const void* A, int64_t M, int64_t K, const uint8_t* B, int64_t N,
+                     const uint8_t* weight_scale, int64_t scale_cols, int64_t block_size,
+                     const float* weight_scale_2, const void* bias, void* A_work, void* Y, int dtype,
+                     void* stream) {
+  // The matmul reads A_work; validate it as the matmul's activation.
+  MatmulArgs a{A_work, B, weight_scale, weight_scale_2, bias, Y, M, N, K, block_size, scale_cols,
+               static_cast<Act>(dtype), stream};
+  int mm_path = FP4W_PATH_NONE;
+  int st = plan_matmul(FP4W_OP_FP4_MATMUL, a, weight_scale, 1, FP4W_PATH_AUTO, &mm_path);
+  if (st != FP4W_OK) return st;
+  if (K % 16 != 0) return FP4W_ERR_SHAPE;  // activation blocks of 16
+  if (mm_path == FP4W_PATH_NONE) return FP4W_OK;  // empty output
+  Nvfp4Args q{A, nullptr, nullptr, A_work, M * (K / 16), static_cast<Act>(dtype), stream};
+  int q_path = FP4W_PATH_NONE;
+  st = plan_nvfp4(q, M, K, false, FP4W_PATH_AUTO, &q_path);
+  if (st != FP4W_OK) return st;
+  // The QDQ step writes A_work: it must not overlap the weights, scales,
+  // bias or Y (Y against A_work is checked by plan_matmul); Y must not
+  // overlap the original activation.
+  const int64_t abytes = M * K * 2;
+  if (overlaps(Y, M * N * 2, A, abytes) || overlaps(A_work, abytes, B, N * (K / 2)) ||
+      overlaps(A_work, abytes, weight_scale, N * scale_cols) || overlaps(A_work, abytes, weight_scale_2, 4) ||
+      overlaps(A_work, abytes, bias, N * 2))
+    return FP4W_ERR_ALIAS;
+  st = launch_nvfp4(q_path, q, false);
+  if (st != FP4W_OK) return st;
+  return launch_matmul(mm_path, a);
+}
+
 int fp4w_dequant_ex(const uint8_t* B, int64_t N, int64_t K, const uint8_t* weight_scale,
                     int64_t scale_cols, int64_t block_size, const float* weight_scale_2, void* out,
                     int dtype, void* stream, int path) {
@@ -383,6 +484,11 @@ int fp4w_dequant(const uint8_t* B, int64_t N, int64_t K, const uint8_t* weight_s
 
 int fp4w_select_path(int op, int64_t M, int64_t N, int64_t K, int64_t block_size,
                      int64_t scale_cols) {
+  if (op == FP4W_OP_NVFP4_ACT) {
+    if (!nvfp4_shape_ok(M, K)) return FP4W_ERR_SHAPE;
+    if (M == 0 || K == 0) return FP4W_PATH_NONE;
+    return FP4W_PATH_NVFP4_VEC;
+  }
   if (op == FP4W_OP_FP8_QDQ) {
     if (M < 0 || K < 0 || !mul_ok(M, K) || !mul_ok(M * K, 2)) return FP4W_ERR_SHAPE;
     if (M == 0 || K == 0) return FP4W_PATH_NONE;
@@ -429,6 +535,8 @@ const char* fp4w_path_name(int path) {
     case FP4W_PATH_FP8_SKINNY: return "fp8_skinny";
     case FP4W_PATH_FP8_DEQUANT_VEC: return "fp8_dequant_vec";
     case FP4W_PATH_FP8_DEQUANT_GENERIC: return "fp8_dequant_generic";
+    case FP4W_PATH_NVFP4_VEC: return "nvfp4_vec";
+    case FP4W_PATH_NVFP4_GENERIC: return "nvfp4_generic";
     default: return "unknown";
   }
 }

@@ -53,6 +53,19 @@ struct QdqArgs {
   void* stream;
 };
 
+// NVFP4 activation quantization (W4A4 path): `blocks` blocks of 16 elements
+// of T.  Packed mode writes `codes` (8 bytes per block) and `scales` (1 byte
+// per block); QDQ mode writes `out` (16 elements of T per block).
+struct Nvfp4Args {
+  const void* A;
+  uint8_t* codes;
+  uint8_t* scales;
+  void* out;
+  int64_t blocks;
+  Act act;
+  void* stream;
+};
+
 // Each launcher enqueues its kernel(s) and returns 0, or -1 when HIP reports
 // an error at enqueue time.  Preconditions (checked by the dispatcher, never
 // by the launcher) are stated next to each.
@@ -118,5 +131,11 @@ int launch_fp8_dequant_generic(const Fp8DequantArgs& a);
 int launch_qdq_vec(const QdqArgs& a);
 // any count > 0; out == A allowed.
 int launch_qdq_generic(const QdqArgs& a);
+
+// NVFP4 quantization, packed (codes and scales) or QDQ (out; out == A
+// allowed).  vec: A 16-byte aligned, and codes 8-byte aligned (packed) or
+// out 16-byte aligned (QDQ).  blocks > 0.
+int launch_nvfp4_quantize(const Nvfp4Args& a, bool vec);
+int launch_nvfp4_qdq(const Nvfp4Args& a, bool vec);
 
 }  // namespace fp4w

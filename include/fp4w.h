@@ -72,7 +72,9 @@ typedef enum {
   FP4W_PATH_FP4_SKINNY = 12,     /* MFMA skinny matmul: 1 <= M <= 64, block_size 16, K % 128 == 0 */
   FP4W_PATH_FP8_SKINNY = 13,     /* MFMA skinny matmul: 1 <= M <= 64, block_size % 128 == 0, K % 128 == 0 */
   FP4W_PATH_FP8_DEQUANT_VEC = 14,    /* vectorised FP8 dequant: K % 16 == 0, block_size % 16 == 0 */
-  FP4W_PATH_FP8_DEQUANT_GENERIC = 15 /* any legal FP8 dequant arguments */
+  FP4W_PATH_FP8_DEQUANT_GENERIC = 15, /* any legal FP8 dequant arguments */
+  FP4W_PATH_NVFP4_VEC = 16,     /* NVFP4 activation quantize / QDQ, 16-byte loads (aligned pointers) */
+  FP4W_PATH_NVFP4_GENERIC = 17  /* any legal NVFP4 activation arguments */
 } fp4w_path;
 
 /* Operation selector for fp4w_select_path. */
@@ -81,7 +83,8 @@ typedef enum {
   FP4W_OP_FP8_MATMUL = 1,
   FP4W_OP_FP4_DEQUANT = 2,
   FP4W_OP_FP8_QDQ = 3, /* fp8w_qdq_activation: only M and K are used */
-  FP4W_OP_FP8_DEQUANT = 4 /* fp8w_dequant: M is ignored */
+  FP4W_OP_FP8_DEQUANT = 4, /* fp8w_dequant: M is ignored */
+  FP4W_OP_NVFP4_ACT = 5 /* fp4w_quantize_activation / fp4w_qdq_activation: only M and K are used */
 } fp4w_op;
 
 /*
@@ -131,6 +134,79 @@ int fp8w_matmul(const void* A, int64_t M, int64_t K, const uint8_t* B, int64_t N
 int fp8w_matmul_ex(const void* A, int64_t M, int64_t K, const uint8_t* B, int64_t N,
                    const float* b_scale, int64_t scale_cols, int64_t block_size, const void* bias,
                    void* Y, int dtype, void* stream, int path);
+
+/*
+ * fp4w_quantize_activation - step 1 of the FP4 operator's native FP4 x FP4
+ * (W4A4) path ([FP4 doc] §6 Native SM120 FP4 x FP4 Path): the activation as
+ * packed E2M1 codes with one E4M3 scale per 16-element block (NVFP4).  The
+ * pages name the format but no rounding rule; this library uses, per block
+ * of 16 consecutive k of one row:
+ *   scale = e4m3( min( RNE_f32(amax / 6), 448 ) )   (NaN in the block -> NaN, 0x7F)
+ *   code  = e2m1( RNE_f32(a / scale) )               (scale == 0 -> code 0)
+ * amax = max |a|; both divisions are IEEE FP32 divisions; e4m3 and e2m1 give
+ * the nearest value with ties to the even code; e2m1 saturates at 6 and keeps
+ * the sign (a negative quotient rounding to zero gives code 0x8); a NaN
+ * quotient gives code 0.  Bit-exact.
+ *
+ *   A       T[M, K], K % 16 == 0.
+ *   codes   uint8[M, K/2] (written): two codes per byte, low nibble = even k
+ *           (the weight layout of [FP4 doc] §2).
+ *   scales  uint8[M, K/16] (written): E4M3 "fn" bytes.
+ * M == 0 or K == 0: FP4W_OK, nothing launched.  Errors: FP4W_ERR_NULL,
+ * FP4W_ERR_SHAPE (negative sizes, K % 16 != 0, overflow), FP4W_ERR_DTYPE,
+ * FP4W_ERR_ALIAS (codes or scales overlap A or each other),
+ * FP4W_ERR_LAUNCH.
+ */
+int fp4w_quantize_activation(const void* A, int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
+                             int dtype, void* stream);
+
+/* Path-forcing variant (FP4W_PATH_AUTO, _NVFP4_VEC, _NVFP4_GENERIC). */
+int fp4w_quantize_activation_ex(const void* A, int64_t M, int64_t K, uint8_t* codes, uint8_t* scales,
+                                int dtype, void* stream, int path);
+
+/*
+ * fp4w_qdq_activation - the same quantization, decoded back to T:
+ *   out[m, k] = e2m1(code) * e4m3(scale)
+ * which is exact in FP16 and BF16 (at most 6 significand bits; nonzero
+ * magnitudes within [2^-10, 2688]); NaN where the block's scale is NaN.
+ *
+ *   A    T[M, K], K % 16 == 0.
+ *   out  T[M, K] (written).  out == A is allowed (in place); any other
+ *        overlap with A is FP4W_ERR_ALIAS.
+ * Errors as fp4w_quantize_activation.
+ */
+int fp4w_qdq_activation(const void* A, int64_t M, int64_t K, void* out, int dtype, void* stream);
+
+/* Path-forcing variant (FP4W_PATH_AUTO, _NVFP4_VEC, _NVFP4_GENERIC). */
+int fp4w_qdq_activation_ex(const void* A, int64_t M, int64_t K, void* out, int dtype, void* stream,
+                           int path);
+
+/*
+ * fp4w_matmul_w4a4 - the FP4 operator's native FP4 x FP4 path ([FP4 doc] §6):
+ * the activation quantized as above, times the FP4 weights, plus bias,
+ * accumulated in FP32 and rounded once to T:
+ *   Y[m, n] = sum_k qdq(A)[m, k] * B_dq[n, k] + bias[n]
+ * gfx950's scaled MFMA takes power-of-two (E8M0) scales per 32 elements and
+ * cannot apply E4M3 scales per 16 exactly, so this runs as A_work =
+ * fp4w_qdq_activation(A) (exact in T), then fp4w_matmul(A_work, ...), whose
+ * kernels fold the weight scales into exact BF16/FP16 MFMA operands.  Both
+ * steps are enqueued on `stream`.  The pages' guards (block_size 16,
+ * K % 32, N % 32, M > 8) choose this path inside their operator; called
+ * directly it takes any arguments fp4w_matmul takes with K % 16 == 0.
+ *
+ *   A_work   T[M, K] caller-owned workspace that receives qdq(A) (the
+ *            library allocates nothing).  A_work == A is allowed and
+ *            overwrites A; any other overlap with A is FP4W_ERR_ALIAS, as is
+ *            an overlap of A_work with B, weight_scale, weight_scale_2, bias
+ *            or Y, or of Y with A.
+ *   Other arguments and errors as fp4w_matmul; K % 16 != 0 is
+ *   FP4W_ERR_SHAPE.  Every argument is validated before anything is
+ *   launched.
+ */
+int fp4w_matmul_w4a4(const void* A, int64_t M, int64_t K, const uint8_t* B, int64_t N,
+                     const uint8_t* weight_scale, int64_t scale_cols, int64_t block_size,
+                     const float* weight_scale_2, const void* bias, void* A_work, void* Y, int dtype,
+                     void* stream);
 
 /*
  * fp4w_dequant - expand packed FP4 weights to T[N, K] ([FP4 doc] §5 step 1;

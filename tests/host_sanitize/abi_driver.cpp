@@ -103,21 +103,37 @@ int main() {
   EXPECT(fp8w_matmul_w8a8(A, 4, 512, B, 300, reinterpret_cast<const float*>(S), 4, 128, ws2, nullptr, W, Y,
                           FP4W_BF16, nullptr) == FP4W_OK);
   EXPECT(strcmp(fp4w::g_last, "launch_fp8_gemv") == 0);
+  // NVFP4 activation and W4A4
+  uint8_t* C = reinterpret_cast<uint8_t*>(W);
+  EXPECT(fp4w_quantize_activation(A, 4, 64, C, C + 128, FP4W_BF16, nullptr) == FP4W_OK);
+  EXPECT(strcmp(fp4w::g_last, "launch_nvfp4_quantize_vec") == 0);
+  EXPECT(fp4w_quantize_activation(A + 1, 4, 64, C, C + 128, FP4W_BF16, nullptr) == FP4W_OK);  // unaligned
+  EXPECT(strcmp(fp4w::g_last, "launch_nvfp4_quantize_generic") == 0);
+  EXPECT(fp4w_quantize_activation(A, 4, 64, C, C + 64, FP4W_BF16, nullptr) == FP4W_ERR_ALIAS);
+  EXPECT(fp4w_qdq_activation(A, 4, 64, A, FP4W_F16, nullptr) == FP4W_OK);  // in place
+  EXPECT(strcmp(fp4w::g_last, "launch_nvfp4_qdq_vec") == 0);
+  EXPECT(fp4w_qdq_activation(A, 4, 48, A, FP4W_F16, nullptr) == FP4W_OK);
+  EXPECT(fp4w_qdq_activation(A, 4, 40, A, FP4W_F16, nullptr) == FP4W_ERR_SHAPE);
+  EXPECT(fp4w_quantize_activation(A, big, big, C, C + 128, FP4W_BF16, nullptr) == FP4W_ERR_SHAPE);
+  EXPECT(fp4w_matmul_w4a4(A, 4, 512, B, 300, S, 32, 16, ws2, nullptr, W, Y, FP4W_BF16, nullptr) == FP4W_OK);
+  EXPECT(strcmp(fp4w::g_last, "launch_fp4_gemv") == 0);
+  EXPECT(fp4w_matmul_w4a4(A, 4, 520, B, 300, S, 33, 16, ws2, nullptr, W, Y, FP4W_BF16, nullptr) ==
+         FP4W_ERR_SHAPE);
   // select_path over a sweep of sizes, including ones near the int64 limits
   const int64_t dims[] = {0, 1, 7, 8, 9, 64, 65, 128, 480, 5120, 17408, int64_t(1) << 22, int64_t(1) << 31,
                           int64_t(1) << 40, int64_t(1) << 62};
   const int64_t blocks[] = {1, 15, 16, 64, 128};
-  for (int op = 0; op <= 4; ++op)
+  for (int op = 0; op <= 5; ++op)
     for (int64_t M : dims)
       for (int64_t N : dims)
         for (int64_t K : dims)
           for (int64_t bs : blocks) {
             const int64_t cols = K == 0 ? 0 : K / bs + (K % bs != 0);
             const int r = fp4w_select_path(op, M, N, K, bs, cols);
-            EXPECT(r >= FP4W_ERR_ALIAS && r <= FP4W_PATH_FP8_DEQUANT_GENERIC);
+            EXPECT(r >= FP4W_ERR_ALIAS && r <= FP4W_PATH_NVFP4_GENERIC);
           }
   for (int s = -8; s <= 1; ++s) EXPECT(fp4w_status_string(s) != nullptr);
-  for (int p = -1; p <= 16; ++p) EXPECT(fp4w_path_name(p) != nullptr);
+  for (int p = -1; p <= 18; ++p) EXPECT(fp4w_path_name(p) != nullptr);
   if (failures == 0) printf("ok\n");
   return failures == 0 ? 0 : 1;
 }

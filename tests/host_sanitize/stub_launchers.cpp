@@ -30,4 +30,12 @@ STUB(launch_fp8_dequant_generic, Fp8DequantArgs)
 STUB(launch_qdq_vec, QdqArgs)
 STUB(launch_qdq_generic, QdqArgs)
 #undef STUB
+int launch_nvfp4_quantize(const Nvfp4Args&, bool vec) {
+  g_last = vec ? "launch_nvfp4_quantize_vec" : "launch_nvfp4_quantize_generic";
+  return 0;
+}
+int launch_nvfp4_qdq(const Nvfp4Args&, bool vec) {
+  g_last = vec ? "launch_nvfp4_qdq_vec" : "launch_nvfp4_qdq_generic";
+  return 0;
+}
 }  // namespace fp4w

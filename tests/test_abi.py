@@ -262,3 +262,56 @@ def test_dispatch_and_validation_fp8_dequant():
     assert d(B, 16, 37, S, 3, 16, O, fw.BF16, None, fw.PATH_FP8_DEQUANT_VEC) == fw.ERR_PATH
     assert d(B, 16, 256, S, 2, 128, O, fw.BF16, None, fw.PATH_DEQUANT_VEC) == fw.ERR_PATH
     assert d(None, 0, 256, None, 2, 128, None, fw.BF16, None, 0) == fw.OK
+
+
+def test_dispatch_and_validation_nvfp4_activation():
+    Q = fw.OP_NVFP4_ACT
+    assert fw.fp4w_select_path(Q, 8192, 0, 5120, 1, 1) == fw.PATH_NVFP4_VEC
+    assert fw.fp4w_select_path(Q, 0, 0, 64, 1, 1) == fw.PATH_NONE
+    assert fw.fp4w_select_path(Q, 4, 0, 40, 1, 1) == fw.ERR_SHAPE           # K % 16 != 0
+    assert fw.fp4w_select_path(Q, -1, 0, 64, 1, 1) == fw.ERR_SHAPE
+    assert fw.fp4w_path_name(fw.PATH_NVFP4_VEC) == "nvfp4_vec"
+    assert fw.fp4w_path_name(fw.PATH_NVFP4_GENERIC) == "nvfp4_generic"
+    lib = fw.load_library()
+    vp = ctypes.c_void_p
+    A, C, S, O = vp(0x100000), vp(0x300000), vp(0x380000), vp(0x500000)   # A: 4 x 64 bf16 = 512 B
+    q = lib.fp4w_quantize_activation_ex
+    assert q(A, 4, 64, C, S, 7, None, 0) == fw.ERR_DTYPE
+    assert q(A, 4, 40, C, S, fw.BF16, None, 0) == fw.ERR_SHAPE
+    assert q(A, -4, 64, C, S, fw.BF16, None, 0) == fw.ERR_SHAPE
+    assert q(None, 4, 64, C, S, fw.BF16, None, 0) == fw.ERR_NULL
+    assert q(A, 4, 64, None, S, fw.BF16, None, 0) == fw.ERR_NULL
+    assert q(A, 4, 64, C, None, fw.BF16, None, 0) == fw.ERR_NULL
+    assert q(A, 4, 64, vp(0x100000 + 256), S, fw.BF16, None, 0) == fw.ERR_ALIAS     # codes inside A
+    assert q(A, 4, 64, C, vp(0x100000 + 500), fw.BF16, None, 0) == fw.ERR_ALIAS     # scales inside A
+    assert q(A, 4, 64, C, vp(0x300000 + 64), fw.BF16, None, 0) == fw.ERR_ALIAS      # scales inside codes
+    assert q(vp(0x100002), 4, 64, C, S, fw.BF16, None, fw.PATH_NVFP4_VEC) == fw.ERR_PATH   # unaligned A
+    assert q(A, 4, 64, vp(0x300004), S, fw.BF16, None, fw.PATH_NVFP4_VEC) == fw.ERR_PATH   # codes % 8
+    assert q(A, 4, 64, C, S, fw.BF16, None, fw.PATH_QDQ_VEC) == fw.ERR_PATH        # not an NVFP4 path
+    assert q(None, 0, 64, None, None, fw.BF16, None, 0) == fw.OK                    # empty: no launch
+    d = lib.fp4w_qdq_activation_ex
+    assert d(A, 4, 40, O, fw.BF16, None, 0) == fw.ERR_SHAPE
+    assert d(A, 4, 64, None, fw.BF16, None, 0) == fw.ERR_NULL
+    assert d(A, 4, 64, vp(0x100000 + 32), fw.BF16, None, 0) == fw.ERR_ALIAS         # partial overlap
+    assert d(A, 4, 64, vp(0x500008), fw.F16, None, fw.PATH_NVFP4_VEC) == fw.ERR_PATH  # out % 16
+    assert d(None, 4, 0, None, fw.F16, None, fw.PATH_NVFP4_GENERIC) == fw.OK
+
+
+def test_w4a4_validation_before_any_launch():
+    lib = fw.load_library()
+    vp = ctypes.c_void_p
+    A, B, S, W2, W, Y = (vp(x) for x in (0x100000, 0x200000, 0x300000, 0x380000, 0x400000, 0x500000))
+    m = lib.fp4w_matmul_w4a4
+    # M=4, K=256, N=16, bs=16, cols=16
+    assert m(A, 4, 256, B, 16, S, 15, 16, W2, None, W, Y, fw.BF16, None) == fw.ERR_SHAPE
+    assert m(A, 4, 40, B, 16, S, 3, 16, W2, None, W, Y, fw.BF16, None) == fw.ERR_SHAPE    # K % 16
+    assert m(A, 4, 256, B, 16, S, 16, 16, None, None, W, Y, fw.BF16, None) == fw.ERR_NULL
+    assert m(A, 4, 256, B, 16, S, 16, 16, W2, None, None, Y, fw.BF16, None) == fw.ERR_NULL
+    assert m(None, 4, 256, B, 16, S, 16, 16, W2, None, W, Y, fw.BF16, None) == fw.ERR_NULL
+    assert m(A, 4, 256, B, 16, S, 16, 16, W2, None, vp(0x100000 + 32), Y, fw.BF16, None) == fw.ERR_ALIAS
+    assert m(A, 4, 256, B, 16, S, 16, 16, W2, None, W, vp(0x400000 + 64), fw.BF16, None) == fw.ERR_ALIAS
+    assert m(A, 4, 256, B, 16, S, 16, 16, W2, None, W, vp(0x100000 + 64), fw.BF16, None) == fw.ERR_ALIAS
+    assert m(A, 4, 256, B, 16, S, 16, 16, W2, None, vp(0x200000 + 64), Y, fw.BF16, None) == fw.ERR_ALIAS
+    assert m(A, 4, 256, B, 16, S, 16, 16, W2, None, vp(0x380000 - 64), Y, fw.BF16, None) == fw.ERR_ALIAS
+    assert m(A, 4, 256, B, 16, S, 16, 16, W2, None, W, Y, 9, None) == fw.ERR_DTYPE
+    assert m(None, 0, 256, None, 16, None, 16, 16, None, None, None, None, fw.BF16, None) == fw.OK
