@@ -648,6 +648,20 @@ def profile_kernel(which, launches=50):
         out = torch.empty(p.M, p.N, dtype=torch.bfloat16, device="cuda")
         for _ in range(min(launches, 10)):
             fw.fp4w_matmul(d["A"], d["B"][0], d["ws"][0], d["ws2"], None, 16, out=out)
+    elif which == "fp8_gemm":
+        p = workloads.WORKLOADS["fp8_gemv"].make(M=8192)
+        d = fp8_on_device(p)
+        out = torch.empty(p.M, p.N, dtype=torch.bfloat16, device="cuda")
+        for _ in range(min(launches, 10)):
+            fw.fp8w_matmul(d["A"], d["B"][0], d["bs"][0], None, 128, out=out)
+    elif which == "w4a4":
+        # the W4A4 prefill: NVFP4 activation QDQ + the FP4 GEMM
+        p = workloads.WORKLOADS["fp4_prefill"].make()
+        d = fp4_on_device(p)
+        work = torch.empty_like(d["A"])
+        out = torch.empty(p.M, p.N, dtype=torch.bfloat16, device="cuda")
+        for _ in range(min(launches, 10)):
+            fw.fp4w_matmul_w4a4(d["A"], d["B"][0], d["ws"][0], d["ws2"], None, 16, out=out, workspace=work)
     elif which == "skinny":
         # batched decode, M = 16, 32, 64 at N = 17408, K = 5120 (FP4 then FP8)
         for M in (16, 32, 64):
@@ -704,8 +718,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--extra", default="", help="comma-separated subset of the extra workloads to run")
-    ap.add_argument("--profile-kernel", choices=["fp4_gemv", "fp4_gemv_wide", "fp8_gemv", "fp4_gemm", "dequant", "copy",
-                                                          "decode_step", "skinny", "qdq", "fp8_dequant"])
+    ap.add_argument("--profile-kernel", choices=["fp4_gemv", "fp4_gemv_wide", "fp8_gemv", "fp4_gemm", "fp8_gemm", "w4a4",
+                                                 "dequant", "copy", "decode_step", "skinny", "qdq", "fp8_dequant"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library runs on a single MI355X and has no "
