@@ -16,7 +16,8 @@
 //    The E4M3 block scale is folded into the decoded BF16/FP16 operand, which
 //    is exact (E2M1 x E4M3 needs 6 significand bits; [FP4 doc] §4);
 //    weight_scale_2 and the bias are applied once in the epilogue.  The
-//    tiles of a last, partial round are launched as 256 x 128 halves.
+//    tiles of a last, partial round are launched as 256 x 128 halves.  Up to
+//    M = 128 the tiles are 128 rows high (4 MFMA row tiles per wave).
 //  * gemm_fp8_kernel: 8 waves, tile 128 x 256, waves in a 2 (M) x 4 (N) grid,
 //    each 64 x 64 = 2 x 2 MFMA tiles.  E4M3 -> T is exact; the FP32 block
 //    scale is not representable in the operand, so every scale block
@@ -115,10 +116,12 @@ __device__ __forceinline__ void wait_barrier() {
 __device__ __forceinline__ void wait_all_but(int n) {
   switch (n) {
     case 4: wait_barrier<4>(); break;
+    case 6: wait_barrier<6>(); break;
     case 8: wait_barrier<8>(); break;
     case 10: wait_barrier<10>(); break;
     case 12: wait_barrier<12>(); break;
     case 14: wait_barrier<14>(); break;
+    case 16: wait_barrier<16>(); break;
     case 20: wait_barrier<20>(); break;
     default: wait_barrier<0>(); break;
   }
@@ -167,32 +170,32 @@ __device__ __forceinline__ void store_tile(const T* out, int pitch, T* Y, int m0
 
 // ------------------------------------------------------------------ FP4
 
-template <int NT>
+template <int NT, int MS>
 struct F4Shape {
-  static constexpr int kTM = 256, kTN = 128 * NT;  // tile (NT = 1: half of a 256-column tile)
-  static constexpr int kMS = 8;                    // MFMA row tiles per wave
-  static constexpr int kAL = 8;                    // activation loads per wave and step
+  static constexpr int kTM = 32 * MS, kTN = 128 * NT;  // tile (NT = 1: half of a 256-column tile)
+  static constexpr int kMS = MS;                       // MFMA row tiles per wave
+  static constexpr int kAL = MS;                       // activation loads per wave and step
   static constexpr int kBL = 2 * NT;               // weight loads per wave and slot (two steps)
   static constexpr int kSL = 4 * NT;               // scale loads per wave and slot (eight steps)
   static constexpr int kGM = 4;                    // tile rows per group of the tile order
 };
 
-template <typename T, int NT>
+template <typename T, int NT, int MS>
 struct F4Lds {
-  T a[3][256 * kLdsRow];        // 3 x 32 KiB
+  T a[3][32 * MS * kLdsRow];    // 3 x 32 KiB (MS = 8)
   uint8_t b[2][128 * NT * 64];  // 2 slots of two steps
   uint8_t s[2][128 * NT * 32];  // 2 slots of eight steps
 };
 
-template <typename T, int NT>
+template <typename T, int NT, int MS_>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_fp4_kernel(
     const T* __restrict__ A, const uint8_t* __restrict__ B, const uint8_t* __restrict__ scales,
     const float* __restrict__ ws2p, const T* __restrict__ bias, T* __restrict__ Y, int M, int N, int K, int cols,
     int tiles_m, int tiles_n, int t_first) {
   typedef ActTraits<T> Tr;
   typedef typename Tr::vec8 V;
-  typedef F4Shape<NT> Sh;
-  __shared__ __attribute__((aligned(16))) F4Lds<T, NT> L;
+  typedef F4Shape<NT, MS_> Sh;
+  __shared__ __attribute__((aligned(16))) F4Lds<T, NT, MS_> L;
   constexpr int MS = Sh::kMS, TN = Sh::kTN;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = uniform(tid >> 6);
@@ -646,14 +649,14 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const T* __restrict__ A, 
 // Offsets inside the kernels are 32-bit and relative to the workgroup's
 // first row of A, B and the scales: 256 rows of A, 256 rows of B and of the
 // scales must each span less than 2^31 bytes (K < 2^22 covers all three).
-template <typename T>
-int launch_fp4(const MatmulArgs& a) {
-  if (a.M > 0x7fffffff || a.N > 0x7fffffff || a.K >= (int64_t(1) << 22)) return -1;
-  const int64_t tiles_m = (a.M + 255) / 256, tiles_n = (a.N + 255) / 256;
+template <typename T, int MS>
+int launch_fp4_ms(const MatmulArgs& a) {
+  constexpr int TM = 32 * MS;
+  const int64_t tiles_m = (a.M + TM - 1) / TM, tiles_n = (a.N + 255) / 256;
   const int64_t ntiles = tiles_m * tiles_n;
   if (ntiles > 0x3fffffff) return -1;
   // The tiles of a last, partial round (at most half the CUs' worth) go to a
-  // second launch as two 256 x 128 halves each, so that round takes about
+  // second launch as two TM x 128 halves each, so that round takes about
   // half as long.
   const int64_t cus = device_cus(), rest = ntiles % cus;
   const bool halves = rest > 0 && 2 * rest <= cus;
@@ -666,13 +669,21 @@ int launch_fp4(const MatmulArgs& a) {
   const int M = static_cast<int>(a.M), N = static_cast<int>(a.N), K = static_cast<int>(a.K);
   const int cols = static_cast<int>(a.scale_cols);
   if (n_full > 0)
-    hipLaunchKernelGGL((gemm_fp4_kernel<T, 2>), dim3(static_cast<unsigned>(n_full)), dim3(256), 0, st, A, a.B, S,
-                       a.ws2, bias, Y, M, N, K, cols, static_cast<int>(tiles_m), static_cast<int>(tiles_n), 0);
+    hipLaunchKernelGGL((gemm_fp4_kernel<T, 2, MS>), dim3(static_cast<unsigned>(n_full)), dim3(256), 0, st, A, a.B,
+                       S, a.ws2, bias, Y, M, N, K, cols, static_cast<int>(tiles_m), static_cast<int>(tiles_n), 0);
   if (halves)
-    hipLaunchKernelGGL((gemm_fp4_kernel<T, 1>), dim3(static_cast<unsigned>(2 * rest)), dim3(256), 0, st, A, a.B, S,
-                       a.ws2, bias, Y, M, N, K, cols, static_cast<int>(tiles_m), static_cast<int>(tiles_n),
+    hipLaunchKernelGGL((gemm_fp4_kernel<T, 1, MS>), dim3(static_cast<unsigned>(2 * rest)), dim3(256), 0, st, A, a.B,
+                       S, a.ws2, bias, Y, M, N, K, cols, static_cast<int>(tiles_m), static_cast<int>(tiles_n),
                        static_cast<int>(n_full));
   return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// 256-row tiles (8 MFMA row tiles per wave); up to 128 rows, 128-row tiles,
+// which halve a prompt chunk's padding and per-workgroup work
+template <typename T>
+int launch_fp4(const MatmulArgs& a) {
+  if (a.M > 0x7fffffff || a.N > 0x7fffffff || a.K >= (int64_t(1) << 22)) return -1;
+  return a.M <= 128 ? launch_fp4_ms<T, 4>(a) : launch_fp4_ms<T, 8>(a);
 }
 
 template <typename T>

@@ -55,6 +55,9 @@ FP4_CASES = [
     # 3 x 102 = 306 tiles: 256 whole ones (grid a multiple of 8: XCD remap
     # on) and 50 as halves, among them the ragged last tile column
     (600, 26012, 192, 16, "fp16", True, "ceil", [fw.PATH_FP4_GEMM]),
+    # M <= 128 takes 128-row tiles: 300 of them, 256 whole and 44 halves
+    (128, 76760, 64, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMM]),
+    (97, 2000, 320, 16, "fp16", False, "ceil", [fw.PATH_FP4_GEMM]),
     # skinny kernel: 1, 2 and 4 row tiles, ragged M and N, one window per
     # wave (K = 128), long K, the persistent loop over many tiles
     (9, 300, 256, 16, "bf16", True, "ceil", [fw.PATH_FP4_SKINNY, fw.PATH_FP4_GEMM]),
