@@ -8,16 +8,26 @@
 //   code  = e2m1( RNE_f32(a / scale) )                scale 0 -> code 0
 //
 // with e4m3 and e2m1 the nearest value, ties to the even code, e2m1
-// saturating at 6 and keeping the sign.  Both divisions are IEEE FP32
-// divisions.  The QDQ form writes e2m1 x e4m3 back in T, which is exact (at
-// most 6 significand bits, magnitudes within [2^-10, 2688]): a W4A4 matmul is
-// that activation times the dequantized weights, run by the FP4 GEMM.
+// saturating at 6 and keeping the sign.  Both quotients are IEEE FP32
+// divisions (the second one is decided without dividing, below).  The QDQ
+// form writes e2m1 x e4m3 back in T, which is exact (at most 6 significand
+// bits, magnitudes within [2^-10, 2688]): a W4A4 matmul is that activation
+// times the dequantized weights, run by the FP4 GEMM.
 //
 // gfx950 mapping: one thread per block (32 bytes of T in, 9 bytes or 32 bytes
 // out, contiguous across the wave), a flat grid-stride loop; v_cvt_pk_fp8_f32
 // encodes the scale (round to nearest even), v_cvt_f32_fp8 and
-// v_cvt_scalef32_pk_f32_fp4 decode scale and codes exactly.  HBM-bound
-// except for the 16 divisions per block.
+// v_cvt_scalef32_pk_f32_fp4 decode scale and codes exactly.
+//
+// The element code needs no division.  The E2M1 rounding boundaries of a / s
+// are the midpoints t in {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5}; t * s is
+// exact in FP32 (at most 3 + 4 significand bits), so |a| against t * s
+// decides the exact quotient's side of each boundary, ties included.  The
+// rounded quotient RNE_f32(a / s) falls on the same side: a (at most 11
+// significand bits for FP16, 8 for BF16; t * s is at least 2^-11) either
+// equals t * s or differs from it by at least 2^-13 of its size, far more
+// than half an FP32 ulp, so rounding the quotient never moves it onto or
+// across a boundary.
 //
 // [FP4 doc] = "MatMulBlockQuantizedFp4Weight - CUDA Operator Documentation"
 
@@ -31,16 +41,14 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// nearest E2M1 code of q (ties to the even code, saturating at 6, sign
-// kept); NaN -> 0
-__device__ __forceinline__ uint32_t e2m1_code(float q) {
-  const float m = fabsf(q);
-  // magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6: the boundaries are the midpoints,
-  // each tie going to the neighbour with the even code
-  const uint32_t c = (m > 0.25f) + (m >= 0.75f) + (m > 1.25f) + (m >= 1.75f) + (m > 2.5f) + (m >= 3.5f) +
-                     (m > 5.0f);
-  const uint32_t sign = (__float_as_uint(q) >> 28) & 8u;
-  return q != q ? 0u : (c | sign);
+// E2M1 code of a / s from the boundaries t * s (thr, see above): the
+// magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 and their midpoints, each tie going
+// to the neighbour with the even code; saturating at 6; the sign of a kept
+__device__ __forceinline__ uint32_t e2m1_code(float a, const float (&thr)[7]) {
+  const float m = fabsf(a);
+  const uint32_t c = (m > thr[0]) + (m >= thr[1]) + (m > thr[2]) + (m >= thr[3]) + (m > thr[4]) +
+                     (m >= thr[5]) + (m > thr[6]);
+  return c | ((__float_as_uint(a) >> 28) & 8u);
 }
 
 // one block: its 16 values -> scale byte, decoded scale and two words of
@@ -64,9 +72,10 @@ __device__ __forceinline__ void quant_block(const float (&v)[16], uint32_t& sbyt
   }
   w[0] = 0u;
   w[1] = 0u;
-  if (s != 0.0f) {
+  if (s > 0.0f) {  // a zero or NaN scale leaves every code 0
+    const float thr[7] = {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.0f * s};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) w[i >> 3] |= e2m1_code(v[i] / s) << (4 * (i & 7));
+    for (int i = 0; i < 16; ++i) w[i >> 3] |= e2m1_code(v[i], thr) << (4 * (i & 7));
   }
 }
 
