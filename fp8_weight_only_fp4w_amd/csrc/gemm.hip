@@ -74,10 +74,12 @@ __device__ __forceinline__ int b_swz(int col) { return (col >> 2) & 3; }
 //    The per-step advance of the activation and weight loads is a scalar
 //    offset and the LDS destination is wave-uniform, so issuing a load costs
 //    no vector ALU work.
-//  * The tiles of step t + 2 are requested at the start of step t; the only
-//    wait is, at the end of each step, for the tiles of step t + 1 (loads
-//    complete in order), then one barrier.  A slot is refilled only after the
-//    barrier that ends its last reader's step.
+//  * The tiles of step t + 2 are requested during step t (FP8: at its start;
+//    FP4: weights and scales at its start, the activation loads one per 8
+//    MFMAs, the last quarter of them just after the barrier that ends step
+//    t).  The only wait is, at the end of each step, for the tiles of step
+//    t + 1 (loads complete in order), then one barrier.  A slot is refilled
+//    only after the barrier that ends its last reader's step.
 //  * LDS layouts are XOR-swizzled in 16-byte pieces (applied on the global
 //    side, since one direct load writes its 64 lanes' data contiguously), so
 //    the operand reads of a 16-lane group hit distinct banks.
@@ -115,14 +117,17 @@ __device__ __forceinline__ void wait_barrier() {
 // wait_barrier<n> for the per-step load counts of the kernels below
 __device__ __forceinline__ void wait_all_but(int n) {
   switch (n) {
+    case 3: wait_barrier<3>(); break;
     case 4: wait_barrier<4>(); break;
+    case 5: wait_barrier<5>(); break;
     case 6: wait_barrier<6>(); break;
+    case 7: wait_barrier<7>(); break;
     case 8: wait_barrier<8>(); break;
+    case 9: wait_barrier<9>(); break;
     case 10: wait_barrier<10>(); break;
     case 12: wait_barrier<12>(); break;
-    case 14: wait_barrier<14>(); break;
-    case 16: wait_barrier<16>(); break;
-    case 20: wait_barrier<20>(); break;
+    case 15: wait_barrier<15>(); break;
+    case 18: wait_barrier<18>(); break;
     default: wait_barrier<0>(); break;
   }
 }
@@ -254,14 +259,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   const int nsteps = K / BK;
   auto loads_for = [&](int u) { return Sh::kAL + ((u & 1) ? 0 : Sh::kBL) + (u % kScaleSteps == 0 ? Sh::kSL : 0); };
-  // the loads of step u: activation and weight offsets stay in range at
+  // The loads of step u.  Activation and weight offsets stay in range at
   // every step, and lanes past the matrix are out of range on their per-lane
-  // offset alone, so the step's advance can be the scalar offset
-  auto issue = [&](int u) {
-    const uint32_t a_step = static_cast<uint32_t>(u * BK * 2);
-#pragma unroll
-    for (int j = 0; j < Sh::kAL; ++j)
-      lds_load16_so(a_rsrc, &L.a[u % 3][(4 * j + wave) * 8 * kLdsRow], a_off[j], a_step);
+  // offset alone, so the step's advance can be the scalar offset.
+  // Activation load j: live == false (steps past the end) reads nothing, an
+  // offset past the descriptor, and writes zeros into a stage no one reads
+  // any more; the epilogue waits for these loads before it reuses the LDS.
+  auto issue_a = [&](int u, int j, bool live) {
+    lds_load16_so(a_rsrc, &L.a[u % 3][(4 * j + wave) * 8 * kLdsRow], vgpr(live ? a_off[j] : kOutOfRange),
+                  static_cast<uint32_t>(u * BK * 2));
+  };
+  auto issue_bs = [&](int u) {
     if ((u & 1) == 0) {
 #pragma unroll
       for (int j = 0; j < Sh::kBL; ++j)
@@ -274,6 +282,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         buf_load_lds<4>(s_rsrc, s_off[j] + 32u * c, &L.s[c & 1][(Sh::kSL * wave + j) * 256]);
     }
   };
+  auto issue = [&](int u) {
+#pragma unroll
+    for (int j = 0; j < Sh::kAL; ++j) issue_a(u, j, true);
+    issue_bs(u);
+  };
+  constexpr int kAG = Sh::kAL / 4;  // activation loads per MFMA group
 
   // lane (c32, h): column c32 of each 32-wide N tile, k half h of every step
   const int c32 = lane & 31, h = lane >> 5;
@@ -324,6 +338,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       if (k < MS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, kVa, 0);            // vector ALU
+      if (k % (kMf / kAG) == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // activation load
     }
   };
 
@@ -339,12 +354,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   read_a(0, 0, aop);
   dec_b(0, bop);
   for (int u = 0; u < nsteps; ++u) {
-    if (u + 2 < nsteps) issue(u + 2);
+    const bool ahead = u + 2 < nsteps;
+    if (ahead) issue_bs(u + 2);
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
       V an[MS], bn[NT];
       read_a(u, i + 1, an);
       dec_b(i + 1, bn);
+#pragma unroll
+      for (int j = kAG * i; j < kAG * (i + 1); ++j) issue_a(u + 2, j, ahead);
       mfmas(aop, bop);
       interleave();
       __builtin_amdgcn_sched_barrier(0);
@@ -357,8 +375,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // barrier; its first operands are read and decoded while the last MFMAs
     // of step u run (their operands are already in registers).  After the
     // last step this re-reads that step's tiles, which go unused.
-    if (u + 2 < nsteps)
-      wait_all_but(loads_for(u + 2));
+    // step u + 2's last activation loads come after the barrier
+    if (ahead)
+      wait_all_but(loads_for(u + 2) - kAG);
     else
       wait_barrier<0>();
     {
@@ -367,6 +386,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       read_b(un);
       read_a(un, 0, an);
       dec_b(0, bn);
+#pragma unroll
+      for (int j = 3 * kAG; j < 4 * kAG; ++j) issue_a(u + 2, j, ahead);
       mfmas(aop, bop);
       interleave();
       __builtin_amdgcn_sched_barrier(0);
@@ -380,8 +401,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // Epilogue: lane (c, h) holds columns 32 NT wave + 32 nt + c and rows
   // 32 ms + 8 (r / 4) + 4 h + r % 4 of the tile.  Y = acc * ws2 + bias,
   // rounded once to T, is staged in LDS (the operand rings, free once every
-  // wave has passed the barrier below).
-  __syncthreads();
+  // wave has passed the barrier below and its last loads have landed).
+  wait_barrier<0>();
   const float ws2 = *ws2p;
   constexpr int kOutPitch = TN + 8;  // elements per staged row (breaks bank aliasing)
   static_assert(sizeof(L) >= Sh::kTM * kOutPitch * sizeof(T), "output staging exceeds LDS");
