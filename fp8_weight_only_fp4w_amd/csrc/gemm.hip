@@ -33,6 +33,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
 #include <type_traits>
 
 #include "device.h"
@@ -78,8 +79,14 @@ __device__ __forceinline__ int b_swz(int col) { return (col >> 2) & 3; }
 //    FP4: weights and scales at its start, the activation loads one per 8
 //    MFMAs, the last quarter of them just after the barrier that ends step
 //    t).  The only wait is, at the end of each step, for the tiles of step
-//    t + 1 (loads complete in order), then one barrier.  A slot is refilled
-//    only after the barrier that ends its last reader's step.
+//    t + 1 (loads complete in order; FP4 also lets the weights and scales
+//    of step t + 2 complete, so that the count is the same every step),
+//    then one barrier.  A slot is refilled only after the barrier that ends
+//    its last reader's step.  The FP4 step loop is unrolled six steps at a
+//    time (activation stage and weight-slot parity become constants) and
+//    its last two steps, which issue no loads, are peeled off: each issued
+//    instruction costs a wave with its SIMD to itself issue cycles that the
+//    matrix pipe then waits for.
 //  * LDS layouts are XOR-swizzled in 16-byte pieces (applied on the global
 //    side, since one direct load writes its 64 lanes' data contiguously), so
 //    the operand reads of a 16-lane group hit distinct banks.
@@ -187,9 +194,9 @@ struct F4Shape {
 
 template <typename T, int NT, int MS>
 struct F4Lds {
-  T a[3][32 * MS * kLdsRow];    // 3 x 32 KiB (MS = 8)
   uint8_t b[2][128 * NT * 64];  // 2 slots of two steps
   uint8_t s[2][128 * NT * 32];  // 2 slots of eight steps
+  T a[3][32 * MS * kLdsRow];    // 3 x 32 KiB (MS = 8)
 };
 
 template <typename T, int NT, int MS_>
@@ -200,7 +207,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   typedef ActTraits<T> Tr;
   typedef typename Tr::vec8 V;
   typedef F4Shape<NT, MS_> Sh;
-  __shared__ __attribute__((aligned(16))) F4Lds<T, NT, MS_> L;
+  typedef F4Lds<T, NT, MS_> Lds;
+  __shared__ __attribute__((aligned(16))) Lds L;
   constexpr int MS = Sh::kMS, TN = Sh::kTN;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = uniform(tid >> 6);
@@ -258,34 +266,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const rsrc_t s_rsrc = make_rsrc(scales + static_cast<size_t>(n0) * s_row, static_cast<uint32_t>(rows_n) * s_row);
 
   const int nsteps = K / BK;
-  auto loads_for = [&](int u) { return Sh::kAL + ((u & 1) ? 0 : Sh::kBL) + (u % kScaleSteps == 0 ? Sh::kSL : 0); };
-  // The loads of step u.  Activation and weight offsets stay in range at
-  // every step, and lanes past the matrix are out of range on their per-lane
-  // offset alone, so the step's advance can be the scalar offset.
-  // Activation load j: live == false (steps past the end) reads nothing, an
-  // offset past the descriptor, and writes zeros into a stage no one reads
-  // any more; the epilogue waits for these loads before it reuses the LDS.
-  auto issue_a = [&](int u, int j, bool live) {
-    lds_load16_so(a_rsrc, &L.a[u % 3][(4 * j + wave) * 8 * kLdsRow], vgpr(live ? a_off[j] : kOutOfRange),
+  // The loads of step u into activation stage `st` (= u % 3).  Activation
+  // and weight offsets stay in range at every step, and lanes past the
+  // matrix are out of range on their per-lane offset alone, so the step's
+  // advance can be the scalar offset.
+  T* const a_lds = &L.a[0][0] + wave * 8 * kLdsRow;
+  auto issue_a = [&](int st, int u, int j) {
+    lds_load16_so(a_rsrc, a_lds + st * (32 * MS * kLdsRow) + 4 * j * 8 * kLdsRow, a_off[j],
                   static_cast<uint32_t>(u * BK * 2));
   };
-  auto issue_bs = [&](int u) {
-    if ((u & 1) == 0) {
+  auto issue_b = [&](int u) {  // u even: the slot of steps u, u + 1
 #pragma unroll
-      for (int j = 0; j < Sh::kBL; ++j)
-        lds_load16_so(b_rsrc, &L.b[(u >> 1) & 1][(4 * j + wave) * 1024], b_off[j], 32u * u);
-    }
-    if (u % kScaleSteps == 0) {
-      const int c = u / kScaleSteps;
-#pragma unroll
-      for (int j = 0; j < Sh::kSL; ++j)
-        buf_load_lds<4>(s_rsrc, s_off[j] + 32u * c, &L.s[c & 1][(Sh::kSL * wave + j) * 256]);
-    }
+    for (int j = 0; j < Sh::kBL; ++j)
+      lds_load16_so(b_rsrc, &L.b[(u >> 1) & 1][(4 * j + wave) * 1024], b_off[j], 32u * u);
   };
-  auto issue = [&](int u) {
+  auto issue_s = [&](int u) {  // u % 8 == 0: the slot of steps u .. u + 7
+    const int c = u / kScaleSteps;
 #pragma unroll
-    for (int j = 0; j < Sh::kAL; ++j) issue_a(u, j, true);
-    issue_bs(u);
+    for (int j = 0; j < Sh::kSL; ++j)
+      buf_load_lds<4>(s_rsrc, s_off[j] + 32u * c, &L.s[c & 1][(Sh::kSL * wave + j) * 256]);
   };
   constexpr int kAG = Sh::kAL / 4;  // activation loads per MFMA group
 
@@ -300,24 +299,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // this lane's packed weights (16 bytes per column tile) and scales of a step
   u32x4 bw[NT];
   float sc[NT][2];
+  // Per-lane LDS byte addresses of the operand reads.  Weight piece
+  // (2 (u & 1) + h) ^ b_swz(col) of slot (u >> 1) & 1 and scale pair
+  // (u % 8) / 4 ^ ((col >> 3) & 1), byte 4 (u & 3) + 2 h, of slot (u / 8) & 1
+  // differ from the step-0 address only in bits that are zero there, so a
+  // step's address is the step-0 address XOR a wave-uniform value.
+  uint32_t b_rd[NT], s_rd[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int col = 32 * NT * wave + 32 * nt + c32;
+    b_rd[nt] = static_cast<uint32_t>(offsetof(Lds, b)) + col * 64 + 16 * (h ^ b_swz(col));
+    s_rd[nt] = static_cast<uint32_t>(offsetof(Lds, s)) + col * 32 + 16 * ((col >> 3) & 1) + 2 * h;
+  }
+  const char* lds_bytes = reinterpret_cast<const char*>(&L);
   auto read_b = [&](int u) {
-    const uint8_t* bsl = L.b[(u >> 1) & 1];
-    const uint8_t* ssl = L.s[(u / kScaleSteps) & 1];
+    const uint32_t ub = ((u & 1) << 5) | (((u >> 1) & 1) * sizeof(L.b[0]));
+    const uint32_t us = (((u % kScaleSteps) >> 2) << 4) | ((u & 3) << 2) | (((u / kScaleSteps) & 1) * sizeof(L.s[0]));
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int col = 32 * NT * wave + 32 * nt + c32;
-      bw[nt] = *reinterpret_cast<const u32x4*>(bsl + col * 64 + 16 * ((2 * (u & 1) + h) ^ b_swz(col)));
-      const uint32_t s2 = *reinterpret_cast<const uint16_t*>(
-          ssl + col * 32 + 16 * (((u % kScaleSteps) >> 2) ^ ((col >> 3) & 1)) + 4 * (u & 3) + 2 * h);
+      bw[nt] = *reinterpret_cast<const u32x4*>(lds_bytes + (b_rd[nt] ^ ub));
+      const uint32_t s2 = *reinterpret_cast<const uint16_t*>(lds_bytes + (s_rd[nt] ^ us));
       sc[nt][0] = e4m3_to_f32<0>(s2);
       sc[nt][1] = e4m3_to_f32<1>(s2);
     }
   };
-  auto read_a = [&](int u, int i, V (&aop)[MS]) {
-    const T* a_src = L.a[u % 3];
+  // activation fragment of chunk 4 h + i, row c32 of row tile 0, stage 0
+  uint32_t a_rd[4];
 #pragma unroll
-    for (int ms = 0; ms < MS; ++ms)
-      aop[ms] = *reinterpret_cast<const V*>(&a_src[lds_index(32 * ms + c32, 4 * h + i)]);
+  for (int i = 0; i < 4; ++i) a_rd[i] = 2 * lds_index(c32, 4 * h + i);
+  auto read_a = [&](int st, int i, V (&aop)[MS]) {
+    const char* a_src = reinterpret_cast<const char*>(&L.a[0][0]) + st * (2 * 32 * MS * kLdsRow) + a_rd[i];
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) aop[ms] = *reinterpret_cast<const V*>(a_src + ms * (2 * 32 * kLdsRow));
   };
   auto dec_b = [&](int i, V (&bop)[NT]) {
 #pragma unroll
@@ -330,41 +343,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int nt = 0; nt < NT; ++nt) acc[ms][nt] = mfma32<T>(aop[ms], bop[nt], acc[ms][nt]);
   };
   // scheduling: per MFMA, one LDS read (first MS MFMAs) and a share of the
-  // vector ALU work of the next group's operands
-  auto interleave = []() {
+  // vector ALU work of the next group's operands; with LOADS, one activation
+  // load per kMf / kAG MFMAs
+  auto interleave = [](auto loads_c) {
+    constexpr bool LOADS = decltype(loads_c)::value;
     constexpr int kMf = MS * NT, kVa = 32 * NT / kMf + 1;
 #pragma unroll
     for (int k = 0; k < kMf; ++k) {
       if (k < MS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, kVa, 0);            // vector ALU
-      if (k % (kMf / kAG) == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // activation load
+      if (LOADS && k % (kMf / kAG) == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // activation load
     }
   };
 
-  issue(0);
-  if (nsteps > 1) {
-    issue(1);
-    wait_all_but(loads_for(1));
-  } else {
-    wait_barrier<0>();
-  }
   V aop[MS], bop[NT];
-  read_b(0);
-  read_a(0, 0, aop);
-  dec_b(0, bop);
-  for (int u = 0; u < nsteps; ++u) {
-    const bool ahead = u + 2 < nsteps;
-    if (ahead) issue_bs(u + 2);
+  // One step u (activations in stage st = u % 3).  AHEAD: it issues the
+  // loads of step u + 2 (weights and scales at its start, activations one
+  // per kMf / kAG MFMAs, the last quarter after the barrier).  The MFMAs of
+  // group i run while the operands of group i + 1 are read and decoded; the
+  // last group's MFMAs run after the barrier that ends the step, together
+  // with the first reads of step u + 1.
+  auto step = [&](int u, int st, int par, auto ahead_c) {  // par: u & 1, or -1 (not known)
+    constexpr bool AHEAD = decltype(ahead_c)::value;
+    const int st1 = st == 2 ? 0 : st + 1;  // (u + 1) % 3
+    const int st2 = st == 0 ? 2 : st - 1;  // (u + 2) % 3
+    if (AHEAD) {
+      if (par >= 0 ? par == 0 : ((u + 2) & 1) == 0) issue_b(u + 2);
+      if ((u + 2) % kScaleSteps == 0) issue_s(u + 2);
+    }
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
       V an[MS], bn[NT];
-      read_a(u, i + 1, an);
+      read_a(st, i + 1, an);
       dec_b(i + 1, bn);
+      if (AHEAD) {
 #pragma unroll
-      for (int j = kAG * i; j < kAG * (i + 1); ++j) issue_a(u + 2, j, ahead);
+        for (int j = kAG * i; j < kAG * (i + 1); ++j) issue_a(st2, u + 2, j);
+      }
       mfmas(aop, bop);
-      interleave();
+      interleave(ahead_c);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ms = 0; ms < MS; ++ms) aop[ms] = an[ms];
@@ -372,30 +390,65 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int nt = 0; nt < NT; ++nt) bop[nt] = bn[nt];
     }
     // The tiles of step u + 1 have landed once every wave passes this
-    // barrier; its first operands are read and decoded while the last MFMAs
-    // of step u run (their operands are already in registers).  After the
-    // last step this re-reads that step's tiles, which go unused.
-    // step u + 2's last activation loads come after the barrier
-    if (ahead)
-      wait_all_but(loads_for(u + 2) - kAG);
+    // barrier.  With AHEAD the loads of step u + 2 issued so far may stay in
+    // flight except its weights and scales (issued first, a step ago).
+    if (AHEAD)
+      wait_barrier<3 * kAG>();
     else
       wait_barrier<0>();
     {
       V an[MS], bn[NT];
-      const int un = min(u + 1, nsteps - 1);
+      const int un = min(u + 1, nsteps - 1);  // after the last step: re-read, unused
       read_b(un);
-      read_a(un, 0, an);
+      read_a(u + 1 < nsteps ? st1 : st, 0, an);
       dec_b(0, bn);
+      if (AHEAD) {
 #pragma unroll
-      for (int j = 3 * kAG; j < 4 * kAG; ++j) issue_a(u + 2, j, ahead);
+        for (int j = 3 * kAG; j < 4 * kAG; ++j) issue_a(st2, u + 2, j);
+      }
       mfmas(aop, bop);
-      interleave();
+      interleave(ahead_c);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ms = 0; ms < MS; ++ms) aop[ms] = an[ms];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) bop[nt] = bn[nt];
     }
+  };
+
+  issue_b(0);
+  issue_s(0);
+#pragma unroll
+  for (int j = 0; j < Sh::kAL; ++j) issue_a(0, 0, j);
+  if (nsteps > 1) {
+    // step 1's weights share slot 0 with step 0's
+#pragma unroll
+    for (int j = 0; j < Sh::kAL; ++j) issue_a(1, 1, j);
+    wait_barrier<Sh::kAL>();
+  } else {
+    wait_barrier<0>();
+  }
+  read_b(0);
+  read_a(0, 0, aop);
+  dec_b(0, bop);
+  int u = 0, st = 0;
+  // six steps at a time (activation stage u % 3 and weight slot parity are
+  // then constants), then the rest one by one
+  for (; u + 7 < nsteps; u += 6) {
+    step(u, 0, 0, std::true_type{});
+    step(u + 1, 1, 1, std::true_type{});
+    step(u + 2, 2, 0, std::true_type{});
+    step(u + 3, 0, 1, std::true_type{});
+    step(u + 4, 1, 0, std::true_type{});
+    step(u + 5, 2, 1, std::true_type{});
+  }
+  for (; u + 2 < nsteps; ++u) {
+    step(u, st, -1, std::true_type{});
+    st = st == 2 ? 0 : st + 1;
+  }
+  for (; u < nsteps; ++u) {
+    step(u, st, -1, std::false_type{});
+    st = st == 2 ? 0 : st + 1;
   }
 
   // Epilogue: lane (c, h) holds columns 32 NT wave + 32 nt + c and rows
