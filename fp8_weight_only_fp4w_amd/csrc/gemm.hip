@@ -312,15 +312,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     s_rd[nt] = static_cast<uint32_t>(offsetof(Lds, s)) + col * 32 + 16 * ((col >> 3) & 1) + 2 * h;
   }
   const char* lds_bytes = reinterpret_cast<const char*>(&L);
-  auto read_b = [&](int u) {
+  // raw reads of step u's weights and scale bytes; set_b then makes them the
+  // current step's (the scale decode waits for nothing by then)
+  auto read_b = [&](int u, u32x4 (&w)[NT], uint32_t (&s2)[NT]) {
     const uint32_t ub = ((u & 1) << 5) | (((u >> 1) & 1) * sizeof(L.b[0]));
     const uint32_t us = (((u % kScaleSteps) >> 2) << 4) | ((u & 3) << 2) | (((u / kScaleSteps) & 1) * sizeof(L.s[0]));
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      bw[nt] = *reinterpret_cast<const u32x4*>(lds_bytes + (b_rd[nt] ^ ub));
-      const uint32_t s2 = *reinterpret_cast<const uint16_t*>(lds_bytes + (s_rd[nt] ^ us));
-      sc[nt][0] = e4m3_to_f32<0>(s2);
-      sc[nt][1] = e4m3_to_f32<1>(s2);
+      w[nt] = *reinterpret_cast<const u32x4*>(lds_bytes + (b_rd[nt] ^ ub));
+      s2[nt] = *reinterpret_cast<const uint16_t*>(lds_bytes + (s_rd[nt] ^ us));
+    }
+  };
+  auto set_b = [&](const u32x4 (&w)[NT], const uint32_t (&s2)[NT]) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      bw[nt] = w[nt];
+      sc[nt][0] = e4m3_to_f32<0>(s2[nt]);
+      sc[nt][1] = e4m3_to_f32<1>(s2[nt]);
     }
   };
   // activation fragment of chunk 4 h + i, row c32 of row tile 0, stage 0
@@ -345,12 +353,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // scheduling: per MFMA, one LDS read (first MS MFMAs) and a share of the
   // vector ALU work of the next group's operands; with LOADS, one activation
   // load per kMf / kAG MFMAs
-  auto interleave = [](auto loads_c) {
+  auto interleave = [](auto loads_c, auto reads_c) {
     constexpr bool LOADS = decltype(loads_c)::value;
+    constexpr int kReads = MS + decltype(reads_c)::value;  // LDS reads of the group
     constexpr int kMf = MS * NT, kVa = 32 * NT / kMf + 1;
 #pragma unroll
     for (int k = 0; k < kMf; ++k) {
-      if (k < MS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      if (k < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, kVa, 0);            // vector ALU
       if (LOADS && k % (kMf / kAG) == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // activation load
@@ -372,18 +381,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       if (par >= 0 ? par == 0 : ((u + 2) & 1) == 0) issue_b(u + 2);
       if ((u + 2) % kScaleSteps == 0) issue_s(u + 2);
     }
+    // step u + 1's weights and scales are in LDS since the barrier that
+    // ended step u - 1; they are read in group 1, long before their use
+    u32x4 bwn[NT];
+    uint32_t s2n[NT];
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
       V an[MS], bn[NT];
       read_a(st, i + 1, an);
+      if (i == 1) read_b(min(u + 1, nsteps - 1), bwn, s2n);
       dec_b(i + 1, bn);
       if (AHEAD) {
 #pragma unroll
         for (int j = kAG * i; j < kAG * (i + 1); ++j) issue_a(st2, u + 2, j);
       }
       mfmas(aop, bop);
-      interleave(ahead_c);
+      if (i == 1)
+        interleave(ahead_c, std::integral_constant<int, 2 * NT>{});
+      else
+        interleave(ahead_c, std::integral_constant<int, 0>{});
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the next group's operand reads
 #pragma unroll
       for (int ms = 0; ms < MS; ++ms) aop[ms] = an[ms];
 #pragma unroll
@@ -398,17 +416,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       wait_barrier<0>();
     {
       V an[MS], bn[NT];
-      const int un = min(u + 1, nsteps - 1);  // after the last step: re-read, unused
-      read_b(un);
-      read_a(u + 1 < nsteps ? st1 : st, 0, an);
+      set_b(bwn, s2n);                           // after the last step: unused
+      read_a(u + 1 < nsteps ? st1 : st, 0, an);  // after the last step: re-read, unused
       dec_b(0, bn);
       if (AHEAD) {
 #pragma unroll
         for (int j = 3 * kAG; j < 4 * kAG; ++j) issue_a(st2, u + 2, j);
       }
       mfmas(aop, bop);
-      interleave(ahead_c);
+      interleave(ahead_c, std::integral_constant<int, 0>{});
       __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the next group's operand reads
 #pragma unroll
       for (int ms = 0; ms < MS; ++ms) aop[ms] = an[ms];
 #pragma unroll
@@ -428,7 +446,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   } else {
     wait_barrier<0>();
   }
-  read_b(0);
+  {
+    u32x4 w[NT];
+    uint32_t s2[NT];
+    read_b(0, w, s2);
+    set_b(w, s2);
+  }
   read_a(0, 0, aop);
   dec_b(0, bop);
   int u = 0, st = 0;
