@@ -384,7 +384,20 @@ def extra_prefill_fp4(reps=200, warmup=50):
                 "baseline_TFLOPs": round(flops / tb / 1e12, 1),
                 "fused_over_baseline_time": round(t / tb, 4), "dispatches": {"warmup": warmup, "timed": reps},
                 "dequant_ms": round(td * 1e3, 4), "dequant_GBps": round(dq_bytes / td / 1e9, 1)})
-    del scratch
+    # The same calls on all-zero activations and weights: the shader clock
+    # follows the chip's power draw, which depends on the operand bits, so a
+    # shorter time here means the random-data time is power-limited.
+    zA, zB = torch.zeros_like(d["A"]), torch.zeros_like(d["B"][0])
+    tz = time_calls([lambda: fw.fp4w_matmul(zA, zB, d["ws"][0], d["ws2"], None, 16, out=out)], 50, 10) / 50
+
+    def base_zero():
+        fw.fp4w_dequant(zB, d["ws"][0], d["ws2"], 16, out=scratch)
+        torch.matmul(zA, scratch.t(), out=out)
+
+    tbz = time_calls([base_zero], 50, 10) / 50
+    res["zero_operands"] = {"fused_ms": round(tz * 1e3, 3), "baseline_ms": round(tbz * 1e3, 3),
+                            "dispatches": {"warmup": 10, "timed": 50}}
+    del scratch, zA, zB
     return res
 
 
@@ -421,7 +434,20 @@ def extra_fp8(steps, warmup, reps=200, pre_warmup=50):
                 "prefill_baseline_TFLOPs": round(flops / tb / 1e12, 1),
                 "prefill_over_baseline_time": round(tp / tb, 4),
                 "dequant_ms": round(td * 1e3, 4), "dequant_GBps": round(dq_bytes / td / 1e9, 1)})
-    del scratch
+    # The same calls on all-zero activations and weights: the shader clock
+    # follows the chip's power draw, which depends on the operand bits, so a
+    # shorter time here means the random-data time is power-limited.
+    zA, zB = torch.zeros_like(d["A"]), torch.zeros_like(d["B"][0])
+    tz = time_calls([lambda: fw.fp8w_matmul(zA, zB, d["bs"][0], None, 128, out=out)], 50, 10) / 50
+
+    def base_zero():
+        fw.fp8w_dequant(zB, d["bs"][0], 128, out=scratch)
+        torch.matmul(zA, scratch.t(), out=out)
+
+    tbz = time_calls([base_zero], 50, 10) / 50
+    res["prefill_zero_operands"] = {"fused_ms": round(tz * 1e3, 3), "baseline_ms": round(tbz * 1e3, 3),
+                                    "dispatches": {"warmup": 10, "timed": 50}}
+    del scratch, zA, zB
     return res
 
 
