@@ -112,7 +112,12 @@ int shape_path(int op, int64_t M, int64_t N, int64_t K, int64_t bs) {
   if (M == 0 || N == 0) return FP4W_PATH_NONE;
   if (op == FP4W_OP_FP4_MATMUL) {
     if (fp4_gemv_ok(M, N, K, bs)) return FP4W_PATH_FP4_GEMV;
-    if (M > 8 && fp4_skinny_ok(M, N, K, bs)) return FP4W_PATH_FP4_SKINNY;
+    // Above 32 rows the skinny kernel needs its 4-row-tile variant; with
+    // N >= 16384 the GEMM then has at least 128 workgroups (128-row tiles,
+    // 128-column halves) and is the faster of the two (47.5 against 57-62 us
+    // at N = 17408, K = 5120, M = 40..64; 46 against 23 us at N = 5120).
+    const bool wide_gemm = M > 32 && N >= 16384 && fp4_gemm_ok(M, N, K, bs);
+    if (M > 8 && !wide_gemm && fp4_skinny_ok(M, N, K, bs)) return FP4W_PATH_FP4_SKINNY;
     if (M > 8 && fp4_gemm_ok(M, N, K, bs)) return FP4W_PATH_FP4_GEMM;
     return FP4W_PATH_FP4_GENERIC;
   }

@@ -77,6 +77,11 @@ def test_dispatch_fp4():
     assert sel(F, 9, 5120, 5120, 16) == fw.PATH_FP4_SKINNY
     assert sel(F, 64, 5120, 5120, 16) == fw.PATH_FP4_SKINNY
     assert sel(F, 65, 5120, 5120, 16) == fw.PATH_FP4_GEMM
+    # above 32 rows a wide N (>= 16384) takes the GEMM, which then fills the GPU
+    assert sel(F, 32, 17408, 5120, 16) == fw.PATH_FP4_SKINNY
+    assert sel(F, 33, 17408, 5120, 16) == fw.PATH_FP4_GEMM
+    assert sel(F, 64, 16384, 4096, 16) == fw.PATH_FP4_GEMM
+    assert sel(F, 64, 16383, 4096, 16) == fw.PATH_FP4_SKINNY
     assert sel(F, 16, 5120, 5184, 16) == fw.PATH_FP4_GEMM       # K % 128 != 0, K % 64 == 0
     assert sel(F, 8192, 17408, 5120, 16) == fw.PATH_FP4_GEMM
     # outside the fast predicates -> generic ([Blog] "Existing FP4 tests did not

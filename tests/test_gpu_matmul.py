@@ -67,6 +67,8 @@ FP4_CASES = [
     (64, 256, 5120, 16, "bf16", True, "ceil", [fw.PATH_FP4_SKINNY, fw.PATH_FP4_GEMM]),
     (1, 40, 128, 16, "bf16", True, "ceil", [fw.PATH_FP4_SKINNY]),
     (5, 65590, 256, 16, "fp16", False, "ceil", [fw.PATH_FP4_SKINNY]),
+    # 32 < M <= 64 with N >= 16384: AUTO takes the 128-row-tile GEMM (ragged N)
+    (40, 16400, 256, 16, "bf16", True, "ceil", [fw.PATH_FP4_SKINNY]),
     (40, 96, 96, 16, "bf16", True, "ceil", [fw.PATH_FP4_GENERIC]),  # K % 64 != 0
     (6, 50, 40, 16, "fp16", True, "floor", [fw.PATH_FP4_GENERIC]),  # partial block, floor cols
     (4, 33, 30, 15, "bf16", True, "ceil", [fw.PATH_FP4_GENERIC]),   # odd block size
