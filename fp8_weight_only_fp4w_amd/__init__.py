@@ -28,7 +28,9 @@ The functions carry the C ABI's names (include/fp4w.h):
   §6, Native SM120 FP4 x FP4 Path); ``fp4w_qdq_activation(A)``: the same,
   decoded back to A's dtype.
 * ``fp4w_matmul_w4a4(A, B, weight_scale, weight_scale_2, bias=None,
-  block_size=16)``: that activation times the FP4 weights (W4A4).
+  block_size=16)``: that activation times the FP4 weights (W4A4);
+  ``fp4w_matmul_w4a4_noalloc(...)``: the same with the activation staged in
+  the library's own device scratch, for callers that cannot allocate.
 
 A keeps any leading dimensions; Y has A's leading dimensions, last dimension
 N and A's dtype.
@@ -62,7 +64,7 @@ EXPORTED = (
     "fp4w_matmul", "fp4w_matmul_ex", "fp8w_matmul", "fp8w_matmul_ex", "fp4w_dequant",
     "fp4w_dequant_ex", "fp8w_dequant", "fp8w_dequant_ex", "fp8w_qdq_activation", "fp8w_qdq_activation_ex", "fp8w_matmul_w8a8",
     "fp4w_quantize_activation", "fp4w_quantize_activation_ex", "fp4w_qdq_activation", "fp4w_qdq_activation_ex",
-    "fp4w_matmul_w4a4",
+    "fp4w_matmul_w4a4", "fp4w_matmul_w4a4_noalloc",
     "fp4w_select_path", "fp4w_status_string", "fp4w_path_name",
 )
 
@@ -117,6 +119,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fp4w_qdq_activation.restype = i32
     lib.fp4w_matmul_w4a4.argtypes = [vp, i64, i64, vp, i64, vp, i64, i64, vp, vp, vp, vp, i32, vp]
     lib.fp4w_matmul_w4a4.restype = i32
+    lib.fp4w_matmul_w4a4_noalloc.argtypes = [vp, i64, i64, vp, i64, vp, i64, i64, vp, vp, vp, i32, vp]
+    lib.fp4w_matmul_w4a4_noalloc.restype = i32
     lib.fp4w_select_path.argtypes = [i32, i64, i64, i64, i64, i64]
     lib.fp4w_select_path.restype = i32
     lib.fp4w_status_string.argtypes = [i32]
@@ -417,4 +421,41 @@ def fp4w_matmul_w4a4(A: torch.Tensor, B: torch.Tensor, weight_scale: torch.Tenso
                               _ptr(weight_scale_2), _ptr(bias), _ptr(workspace), _ptr(out),
                               _dtype_code(A.dtype), _stream(dev))
     _check(st, "fp4w_matmul_w4a4")
+    return out
+
+
+STATIC_SCRATCH_BYTES = 32 * 1024 * 1024  # FP4W_STATIC_SCRATCH_BYTES
+
+
+def fp4w_matmul_w4a4_noalloc(A: torch.Tensor, B: torch.Tensor, weight_scale: torch.Tensor,
+                             weight_scale_2: torch.Tensor, bias: torch.Tensor = None, block_size: int = 16,
+                             out: torch.Tensor = None) -> torch.Tensor:
+    """fp4w_matmul_w4a4 with the activation staged in the library's own
+    device scratch (STATIC_SCRATCH_BYTES per device) instead of a workspace:
+    the C call allocates nothing.  Calls that overlap on one device race on
+    that scratch.  ``out`` is allocated here when not given."""
+    lib = load_library()
+    dev = A.device
+    B, weight_scale = _bytes(B), _bytes(weight_scale)
+    K = A.shape[-1]
+    M = A.numel() // K if K else int(torch.tensor(A.shape[:-1]).prod().item())
+    N = B.shape[0]
+    if B.dim() != 2 or B.shape[1] * 2 != K:
+        raise ValueError(f"B must be [N, K/2] = [N, {K // 2}], got {tuple(B.shape)}")
+    if weight_scale.dim() != 2 or weight_scale.shape[0] != N:
+        raise ValueError("weight_scale must be [N, scale_cols]")
+    _scalar_f32(weight_scale_2, "weight_scale_2")
+    for t, name in ((A, "A"), (B, "B"), (weight_scale, "weight_scale"), (weight_scale_2, "weight_scale_2")):
+        _need(t, name, dev)
+    if bias is not None:
+        _need(bias, "bias", dev)
+        if bias.dtype != A.dtype or bias.numel() != N:
+            raise ValueError("bias must be [N] with A's dtype")
+    if out is None:
+        out = torch.empty(*A.shape[:-1], N, dtype=A.dtype, device=dev)
+    _need(out, "out", dev)
+    st = lib.fp4w_matmul_w4a4_noalloc(_ptr(A), M, K, _ptr(B), N, _ptr(weight_scale), weight_scale.shape[1],
+                                      block_size, _ptr(weight_scale_2), _ptr(bias), _ptr(out),
+                                      _dtype_code(A.dtype), _stream(dev))
+    _check(st, "fp4w_matmul_w4a4_noalloc")
     return out

@@ -426,6 +426,28 @@ int fp4w_matmul_w4a4(const void* A, int64_t M, int64_t K, const uint8_t* B, int6
   return launch_matmul(mm_path, a);
 }
 
+int fp4w_matmul_w4a4_noalloc(const void* A, int64_t M, int64_t K, const uint8_t* B, int64_t N,
+                             const uint8_t* weight_scale, int64_t scale_cols, int64_t block_size,
+                             const float* weight_scale_2, const void* bias, void* Y, int dtype,
+                             void* stream) {
+  static_assert(fp4w::kStaticScratchBytes == FP4W_STATIC_SCRATCH_BYTES, "scratch size");
+  // Validate as fp4w_matmul_w4a4 would, with A standing in for the
+  // workspace (the scratch overlaps no caller buffer), before the scratch's
+  // address is taken.
+  MatmulArgs a{A, B, weight_scale, weight_scale_2, bias, Y, M, N, K, block_size, scale_cols,
+               static_cast<Act>(dtype), stream};
+  int mm_path = FP4W_PATH_NONE;
+  int st = plan_matmul(FP4W_OP_FP4_MATMUL, a, weight_scale, 1, FP4W_PATH_AUTO, &mm_path);
+  if (st != FP4W_OK) return st;
+  if (K % 16 != 0) return FP4W_ERR_SHAPE;
+  if (mm_path == FP4W_PATH_NONE) return FP4W_OK;  // empty output
+  if (K > 0 && M > FP4W_STATIC_SCRATCH_BYTES / 2 / K) return FP4W_ERR_SHAPE;
+  void* work = nullptr;
+  if (fp4w::static_scratch(&work) != 0) return FP4W_ERR_LAUNCH;
+  return fp4w_matmul_w4a4(A, M, K, B, N, weight_scale, scale_cols, block_size, weight_scale_2, bias, work, Y,
+                          dtype, stream);
+}
+
 int fp4w_dequant_ex(const uint8_t* B, int64_t N, int64_t K, const uint8_t* weight_scale,
                     int64_t scale_cols, int64_t block_size, const float* weight_scale_2, void* out,
                     int dtype, void* stream, int path) {

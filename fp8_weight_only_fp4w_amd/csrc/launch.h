@@ -138,4 +138,11 @@ int launch_qdq_generic(const QdqArgs& a);
 int launch_nvfp4_quantize(const Nvfp4Args& a, bool vec);
 int launch_nvfp4_qdq(const Nvfp4Args& a, bool vec);
 
+// Library-owned device scratch of the allocation-free entry point (its size
+// is FP4W_STATIC_SCRATCH_BYTES of the public header): the address of the
+// current device's copy, taken once per device.  0, or -1 when HIP cannot
+// provide it.
+constexpr int64_t kStaticScratchBytes = int64_t(32) << 20;
+int static_scratch(void** out);
+
 }  // namespace fp4w

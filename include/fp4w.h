@@ -2,7 +2,8 @@
  * fp4w.h - block-scaled weight-only FP4 / FP8 matmul for AMD MI355X (gfx950).
  *
  * C ABI.  Plain pointers and sizes only; the library never allocates, frees or
- * synchronises.  Every call validates its arguments, enqueues its kernel(s) on
+ * synchronises (fp4w_matmul_w4a4_noalloc uses a device array that is part of
+ * the library's code object).  Every call validates its arguments, enqueues its kernel(s) on
  * `stream` (a hipStream_t, NULL = the default stream) and returns.  Faults in a
  * kernel surface at the caller's next synchronisation.
  *
@@ -31,7 +32,9 @@
  *     generic kernel; correctness never depends on the fast path.
  *   - Accumulation is FP32.  The result is rounded once to T (round to
  *     nearest even) after the tensor scale and bias are applied.
- *   - Re-entrant and stateless; calls on different streams may overlap.
+ *   - Re-entrant and stateless; calls on different streams may overlap
+ *     (except fp4w_matmul_w4a4_noalloc calls on one device, which share that
+ *     device's scratch).
  */
 #ifndef FP4W_H
 #define FP4W_H
@@ -207,6 +210,31 @@ int fp4w_matmul_w4a4(const void* A, int64_t M, int64_t K, const uint8_t* B, int6
                      const uint8_t* weight_scale, int64_t scale_cols, int64_t block_size,
                      const float* weight_scale_2, const void* bias, void* A_work, void* Y, int dtype,
                      void* stream);
+
+/* Size of the library-owned device scratch of fp4w_matmul_w4a4_noalloc. */
+#define FP4W_STATIC_SCRATCH_BYTES (32 * 1024 * 1024)
+
+/*
+ * fp4w_matmul_w4a4_noalloc - fp4w_matmul_w4a4 for callers that cannot
+ * allocate: code under HIP graph capture, serving loops that make no
+ * allocations, harnesses that forbid hipMalloc.  The quantized activation
+ * goes to a library-owned device array of FP4W_STATIC_SCRATCH_BYTES instead
+ * of a caller workspace; the call allocates nothing.
+ *
+ *   Arguments, results and errors as fp4w_matmul_w4a4 without A_work.
+ *   M * K * 2 > FP4W_STATIC_SCRATCH_BYTES is FP4W_ERR_SHAPE.
+ *   Each device the library runs on holds its own copy of the array until
+ *   the process ends.  Its address is taken on the first call on a device,
+ *   with that device current (FP4W_ERR_LAUNCH if HIP cannot provide it).
+ *   Every call writes the part it reads before reading it, but all calls on
+ *   one device share that device's copy: calls that overlap on one device
+ *   (on two streams, or from two threads) race on it, and the caller must
+ *   order them.
+ */
+int fp4w_matmul_w4a4_noalloc(const void* A, int64_t M, int64_t K, const uint8_t* B, int64_t N,
+                             const uint8_t* weight_scale, int64_t scale_cols, int64_t block_size,
+                             const float* weight_scale_2, const void* bias, void* Y, int dtype,
+                             void* stream);
 
 /*
  * fp4w_dequant - expand packed FP4 weights to T[N, K] ([FP4 doc] §5 step 1;

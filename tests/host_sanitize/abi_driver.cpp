@@ -119,6 +119,20 @@ int main() {
   EXPECT(strcmp(fp4w::g_last, "launch_fp4_gemv") == 0);
   EXPECT(fp4w_matmul_w4a4(A, 4, 520, B, 300, S, 33, 16, ws2, nullptr, W, Y, FP4W_BF16, nullptr) ==
          FP4W_ERR_SHAPE);
+  // the allocation-free variant: same dispatch, the library's scratch as the
+  // workspace, sizes past the scratch rejected before anything is launched
+  fp4w::g_last = "";
+  EXPECT(fp4w_matmul_w4a4_noalloc(A, 4, 512, B, 300, S, 32, 16, ws2, nullptr, Y, FP4W_BF16, nullptr) == FP4W_OK);
+  EXPECT(strcmp(fp4w::g_last, "launch_fp4_gemv") == 0);
+  fp4w::g_last = "";
+  EXPECT(fp4w_matmul_w4a4_noalloc(A, 4096, 8192, B, 300, S, 512, 16, ws2, nullptr, Y, FP4W_BF16, nullptr) ==
+         FP4W_ERR_SHAPE);  // 64 MiB of activation > FP4W_STATIC_SCRATCH_BYTES
+  EXPECT(strcmp(fp4w::g_last, "") == 0);
+  EXPECT(fp4w_matmul_w4a4_noalloc(A, 4, 520, B, 300, S, 33, 16, ws2, nullptr, Y, FP4W_BF16, nullptr) ==
+         FP4W_ERR_SHAPE);
+  EXPECT(fp4w_matmul_w4a4_noalloc(nullptr, 4, 512, B, 300, S, 32, 16, ws2, nullptr, Y, FP4W_BF16, nullptr) ==
+         FP4W_ERR_NULL);
+  EXPECT(fp4w_matmul_w4a4_noalloc(A, 0, 512, B, 300, S, 32, 16, ws2, nullptr, Y, FP4W_BF16, nullptr) == FP4W_OK);
   // select_path over a sweep of sizes, including ones near the int64 limits
   const int64_t dims[] = {0, 1, 7, 8, 9, 64, 65, 128, 480, 5120, 17408, int64_t(1) << 22, int64_t(1) << 31,
                           int64_t(1) << 40, int64_t(1) << 62};

@@ -38,4 +38,10 @@ int launch_nvfp4_qdq(const Nvfp4Args&, bool vec) {
   g_last = vec ? "launch_nvfp4_qdq_vec" : "launch_nvfp4_qdq_generic";
   return 0;
 }
+// a host array stands in for the device scratch (the stubs touch no memory)
+int static_scratch(void** out) {
+  alignas(256) static unsigned char scratch[256];
+  *out = scratch;
+  return 0;
+}
 }  // namespace fp4w

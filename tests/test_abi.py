@@ -320,3 +320,26 @@ def test_w4a4_validation_before_any_launch():
     assert m(A, 4, 256, B, 16, S, 16, 16, W2, None, vp(0x380000 - 64), Y, fw.BF16, None) == fw.ERR_ALIAS
     assert m(A, 4, 256, B, 16, S, 16, 16, W2, None, W, Y, 9, None) == fw.ERR_DTYPE
     assert m(None, 0, 256, None, 16, None, 16, 16, None, None, None, None, fw.BF16, None) == fw.OK
+
+
+def test_w4a4_noalloc_validation_before_any_launch():
+    """The allocation-free W4A4 entry point validates like fp4w_matmul_w4a4
+    and rejects activations larger than its scratch before it touches the
+    device (no GPU is used here)."""
+    lib = fw.load_library()
+    vp = ctypes.c_void_p
+    A, B, S, W2, Y = (vp(x) for x in (0x100000, 0x200000, 0x300000, 0x380000, 0x500000))
+    m = lib.fp4w_matmul_w4a4_noalloc
+    assert m(A, 4, 256, B, 16, S, 15, 16, W2, None, Y, fw.BF16, None) == fw.ERR_SHAPE   # scale_cols
+    assert m(A, 4, 40, B, 16, S, 3, 16, W2, None, Y, fw.BF16, None) == fw.ERR_SHAPE     # K % 16
+    assert m(None, 4, 256, B, 16, S, 16, 16, W2, None, Y, fw.BF16, None) == fw.ERR_NULL
+    assert m(A, 4, 256, B, 16, S, 16, 16, None, None, Y, fw.BF16, None) == fw.ERR_NULL
+    assert m(A, 4, 256, B, 16, S, 16, 16, W2, None, vp(0x100000 + 64), fw.BF16, None) == fw.ERR_ALIAS
+    assert m(A, 4, 256, B, 16, S, 16, 16, W2, None, Y, 9, None) == fw.ERR_DTYPE
+    assert m(None, 0, 256, None, 16, None, 16, 16, None, None, None, fw.BF16, None) == fw.OK
+    # M * K * 2 beyond the scratch: one row past it
+    K = 8192
+    rows = fw.STATIC_SCRATCH_BYTES // (2 * K)
+    big_B, big_S = vp(0x10000000), vp(0x30000000)
+    big_Y = vp(0x40000000)
+    assert m(A, rows + 1, K, big_B, 16, big_S, K // 16, 16, W2, None, big_Y, fw.BF16, None) == fw.ERR_SHAPE
