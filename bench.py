@@ -349,6 +349,40 @@ def hbm_read(sizes):
     return res
 
 
+def mfma_peak():
+    """Measured dense BF16 MFMA rate from this repository's probe
+    (libmfmaprobe.so): back-to-back independent 32x32x16 MFMAs on 512
+    workgroups, one or two waves per SIMD, with operands that change every
+    instruction (random BF16 bits) or constant ones.  Under this load the
+    clock follows the operand bits, so the random-operand rate is the
+    ceiling a GEMM on random data can approach."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "fp8_weight_only_fp4w_amd", "libmfmaprobe.so"))
+    lib.mfma_peak_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32,
+                                    ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.mfma_peak_probe.restype = ctypes.c_int64
+    grid, iters = 512, 4000
+    sink = torch.empty(grid * 512, dtype=torch.float32, device="cuda")
+    key = 0x7FC00123  # a NaN payload no sum of these finite products has: nothing is stored
+    res = {"grid": grid, "iters": iters}
+    for waves in (1, 2):
+        for rnd, label in ((1, "random"), (0, "constant")):
+            mfmas = [0]
+
+            def launch(waves=waves, rnd=rnd):
+                n = lib.mfma_peak_probe(grid, waves, iters, rnd, 12345, key, ctypes.c_void_p(sink.data_ptr()),
+                                        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                if n <= 0:
+                    raise RuntimeError(f"mfma_peak_probe failed ({n})")
+                mfmas[0] = n
+
+            t = time_calls([launch], 20, 5)  # about 50 ms timed, so the clock has settled
+            res[f"{label}_{waves}wave_TFLOPs"] = round(mfmas[0] * 32768 * 20 / t / 1e12, 1)
+    res["random_best_TFLOPs"] = max(res["random_1wave_TFLOPs"], res["random_2wave_TFLOPs"])
+    del sink
+    return res
+
+
 def extra_small_gemv(steps, warmup):
     w = workloads.WORKLOADS["fp4_gemv_small"]
     p = w.make()
@@ -797,6 +831,7 @@ def main():
                          ("skinny", lambda: extra_skinny(args.steps, args.warmup)),
                          ("decode_step", lambda: extra_decode_step(args.steps, args.warmup)),
                          ("mid_m", lambda: extra_mid_m(args.steps, args.warmup)),
+                         ("mfma_peak", mfma_peak),
                          ("fp4_prefill", extra_prefill_fp4)):
             if args.extra and name not in args.extra.split(","):
                 continue
@@ -811,6 +846,15 @@ def main():
         gb = extra["fp4_gemv_wide"]["weight_GBps"]
         extra["fp4_gemv_wide"]["frac_of_measured_read_peak"] = round(gb / peak_rd, 4)
         extra["fp4_gemv_wide"]["frac_of_read_at_size"] = round(gb / rd["at_size"]["fp4_gemv_wide"]["GBps"], 4)
+    # the prefill GEMMs against the MFMA rate measured on random operands
+    if "mfma_peak" in extra:
+        mp = extra["mfma_peak"]["random_best_TFLOPs"]
+        if "fp4_prefill" in extra:
+            extra["fp4_prefill"]["fused_frac_of_mfma_probe_random"] = round(extra["fp4_prefill"]["fused_TFLOPs"] / mp, 4)
+            extra["fp4_prefill"]["baseline_frac_of_mfma_probe_random"] = round(
+                extra["fp4_prefill"]["baseline_TFLOPs"] / mp, 4)
+        if "fp8" in extra:
+            extra["fp8"]["prefill_frac_of_mfma_probe_random"] = round(extra["fp8"]["prefill_TFLOPs"] / mp, 4)
     if "fp8" in extra:
         gb = extra["fp8"]["gemv_M4_weight_GBps"]
         extra["fp8"]["gemv_M4_frac_of_measured_read_peak"] = round(gb / peak_rd, 4)

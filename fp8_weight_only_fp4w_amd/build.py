@@ -16,6 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfp4w.so")
 PROBE_LIB = os.path.join(HERE, "libhbmprobe.so")
+MFMA_PROBE_LIB = os.path.join(HERE, "libmfmaprobe.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
@@ -81,6 +82,10 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     tmp = PROBE_LIB + ".tmp"
     _run([HIPCC, *HIP_FLAGS, "-shared", os.path.join(HERE, "probe", "hbm_read.hip"), "-o", tmp], verbose)
     os.replace(tmp, PROBE_LIB)
+    # the bench's MFMA-rate probe, a library of its own
+    tmp = MFMA_PROBE_LIB + ".tmp"
+    _run([HIPCC, *HIP_FLAGS, "-shared", os.path.join(HERE, "probe", "mfma_peak.hip"), "-o", tmp], verbose)
+    os.replace(tmp, MFMA_PROBE_LIB)
     return LIB
 
 

@@ -50,6 +50,29 @@ def test_hbm_probe_library_exports_its_entry_point():
     assert exported == ["hbm_read_probe"], exported
 
 
+def test_mfma_probe_library_exports_its_entry_point():
+    # the bench's MFMA-rate probe, likewise, with arguments checked before
+    # any launch (no GPU is used here)
+    import ctypes
+    import os
+    import subprocess
+    path = os.path.join(os.path.dirname(fw.LIB_PATH), "libmfmaprobe.so")
+    assert os.path.exists(path), "build() also builds libmfmaprobe.so"
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+    exported = sorted(line.split()[-1] for line in out.splitlines() if " T " in line)
+    assert exported == ["mfma_peak_probe"], exported
+    lib = ctypes.CDLL(path)
+    f = lib.mfma_peak_probe
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_uint32, ctypes.c_uint32,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int64
+    sink = ctypes.c_void_p(0x100000)
+    assert f(256, 3, 10, 1, 0, 0, sink, None) == 0      # waves must be 1 or 2
+    assert f(0, 1, 10, 1, 0, 0, sink, None) == 0        # grid
+    assert f(256, 1, 0, 1, 0, 0, sink, None) == 0       # iters
+    assert f(256, 1, 10, 1, 0, 0, None, None) == 0      # sink
+
+
 def test_status_and_path_strings():
     assert fw.fp4w_status_string(fw.OK) == "ok"
     for st in (fw.ERR_NULL, fw.ERR_SHAPE, fw.ERR_DTYPE, fw.ERR_BLOCK, fw.ERR_PATH, fw.ERR_LAUNCH, fw.ERR_ALIAS):
