@@ -58,6 +58,13 @@ FP4_CASES = [
     # M <= 128 takes 128-row tiles: 300 of them, 256 whole and 44 halves
     (128, 76760, 64, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMM]),
     (97, 2000, 320, 16, "fp16", False, "ceil", [fw.PATH_FP4_GEMM]),
+    # K steps of 64 through the GEMM's step loop (six steps at a time while
+    # eight remain, then single steps, then the last two, which issue no
+    # loads): 13 = 6 + 5 + 2, 14 = 2 x 6 + 2, 15 = 2 x 6 + 1 + 2, 9 = 6 + 1 + 2
+    (300, 600, 832, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMM]),
+    (260, 300, 896, 16, "fp16", True, "ceil", [fw.PATH_FP4_GEMM]),
+    (129, 520, 960, 16, "bf16", False, "ceil", [fw.PATH_FP4_GEMM]),
+    (100, 700, 576, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMM]),
     # skinny kernel: 1, 2 and 4 row tiles, ragged M and N, one window per
     # wave (K = 128), long K, the persistent loop over many tiles
     (9, 300, 256, 16, "bf16", True, "ceil", [fw.PATH_FP4_SKINNY, fw.PATH_FP4_GEMM]),
