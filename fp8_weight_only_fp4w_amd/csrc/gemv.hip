@@ -479,46 +479,53 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
           *reinterpret_cast<u32x4*>(stage + (kRowsPerLoad * b + st_row) * st_pitch + st_pos) = r.a[b];
       }
       wait_vm<D * LPU>();  // this unit's weights have landed
+      // Every LDS read of the unit's two windows is issued before either
+      // window's arithmetic, so that the second window's reads overlap the
+      // first window's work.
+      u32x2 sb[2];
+      u32x4 av[2][R][4];
+      u32x4 wv[2];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        const int w = 2 * u + s2;
-        const int wa = min(w, NW - 1);  // windows past NW meet zero scales (zeroed in the slice)
-        const u32x2 sb = *reinterpret_cast<const u32x2*>(slice + kSlicePitch * li + 8 * (2 * (j % SU) + s2));
+        const int wa = min(2 * u + s2, NW - 1);  // windows past NW meet zero scales (zeroed in the slice)
+        sb[s2] = *reinterpret_cast<const u32x2*>(slice + kSlicePitch * li + 8 * (2 * (j % SU) + s2));
         // activations of the lane: 4 x 16 bytes per row half; chunk i = 2s + p
         // holds k 32g + 16s + 8p .. + 7 of the window (piece p of set s)
-        u32x4 av[R][4];
 #pragma unroll
         for (int h = 0; h < R; ++h) {
           if constexpr (ACT_LDS) {
             const lds_cbytes q = a_win0[h] + __umul24(a_wstep[h], static_cast<uint32_t>(wa));
 #pragma unroll
-            for (int i = 0; i < 4; ++i) av[h][i] = *reinterpret_cast<const lds_u32x4*>(q + 16u * i);
+            for (int i = 0; i < 4; ++i) av[s2][h][i] = *reinterpret_cast<const lds_u32x4*>(q + 16u * i);
           } else {
             const unsigned char* q = stage + (a_valid[h] ? a_off[h] + 256u * s2 : 4u * R * kStagePitch4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) av[h][i] = *reinterpret_cast<const u32x4*>(q + 16u * i);
+            for (int i = 0; i < 4; ++i) av[s2][h][i] = *reinterpret_cast<const u32x4*>(q + 16u * i);
           }
         }
         // weights of the lane: chunk 4 s2 + g of row li (32 codes); dword
         // 2s + p holds piece p of set s (block 2g + s)
-        const u32x4 wv = *reinterpret_cast<const u32x4*>(slot + 128 * li + 16 * ((4 * s2 + g) ^ sw));
+        wv[s2] = *reinterpret_cast<const u32x4*>(slot + 128 * li + 16 * ((4 * s2 + g) ^ sw));
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
         V bw[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bw[i] = Tr::decode8_fp4(wv[i]);
+        for (int i = 0; i < 4; ++i) bw[i] = Tr::decode8_fp4(wv[s2][i]);
         const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
         f32x4 d[R][2];
 #pragma unroll
         for (int h = 0; h < R; ++h)
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
-            d[h][s] = Tr::mfma(__builtin_bit_cast(V, av[h][2 * s]), bw[2 * s], zero);
-            d[h][s] = Tr::mfma(__builtin_bit_cast(V, av[h][2 * s + 1]), bw[2 * s + 1], d[h][s]);
+            d[h][s] = Tr::mfma(__builtin_bit_cast(V, av[s2][h][2 * s]), bw[2 * s], zero);
+            d[h][s] = Tr::mfma(__builtin_bit_cast(V, av[s2][h][2 * s + 1]), bw[2 * s + 1], d[h][s]);
           }
         // result row r of set s is block 2r + s: scale byte 2r + s
-        const f32x2 s01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb.x), false);
-        const f32x2 s23 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb.x), true);
-        const f32x2 s45 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb.y), false);
-        const f32x2 s67 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb.y), true);
+        const f32x2 s01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb[s2].x), false);
+        const f32x2 s23 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb[s2].x), true);
+        const f32x2 s45 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb[s2].y), false);
+        const f32x2 s67 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb[s2].y), true);
         const float sc[8] = {s01.x, s01.y, s23.x, s23.y, s45.x, s45.y, s67.x, s67.y};
 #pragma unroll
         for (int h = 0; h < R; ++h)
