@@ -79,9 +79,9 @@ __device__ __forceinline__ int b_swz(int col) { return (col >> 2) & 3; }
 //    FP4: weights and scales at its start, the activation loads one per 8
 //    MFMAs, the last quarter of them just after the barrier that ends step
 //    t).  The only wait is, at the end of each step, for the tiles of step
-//    t + 1 (loads complete in order; FP4 also lets the weights and scales
-//    of step t + 2 complete, so that the count is the same every step),
-//    then one barrier.  A slot is refilled only after the barrier that ends
+//    t + 1 (loads complete in order; the loads of step t + 2 that are issued
+//    first, FP4's weights and scales and FP8's scales, complete too, so that
+//    the count is the same every step), then one barrier.  A slot is refilled only after the barrier that ends
 //    its last reader's step.  The FP4 step loop is unrolled six steps at a
 //    time (activation stage and weight-slot parity become constants) and
 //    its last two steps, which issue no loads, are peeled off: each issued
@@ -121,24 +121,6 @@ __device__ __forceinline__ void wait_barrier() {
   __builtin_amdgcn_s_barrier();
   __asm__ volatile("" ::: "memory");
 }
-// wait_barrier<n> for the per-step load counts of the kernels below
-__device__ __forceinline__ void wait_all_but(int n) {
-  switch (n) {
-    case 3: wait_barrier<3>(); break;
-    case 4: wait_barrier<4>(); break;
-    case 5: wait_barrier<5>(); break;
-    case 6: wait_barrier<6>(); break;
-    case 7: wait_barrier<7>(); break;
-    case 8: wait_barrier<8>(); break;
-    case 9: wait_barrier<9>(); break;
-    case 10: wait_barrier<10>(); break;
-    case 12: wait_barrier<12>(); break;
-    case 15: wait_barrier<15>(); break;
-    case 18: wait_barrier<18>(); break;
-    default: wait_barrier<0>(); break;
-  }
-}
-
 // direct 16-byte buffer -> LDS load with a per-lane and a scalar offset; the
 // range check is only guaranteed to see the per-lane offset
 __device__ __forceinline__ void lds_load16_so(rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
@@ -577,28 +559,38 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const T* __restrict__ A, 
   }
   const rsrc_t s_rsrc = make_rsrc(scales + static_cast<size_t>(n0) * s_row, static_cast<uint32_t>(rows_n) * s_row);
   const int spb = bs / BK;  // steps per scale block (block_size % 64 == 0)
-  // scale column of step u, and the first scale column of the slot holding
-  // steps 8c .. 8c + 7
-  auto step_col = [&](int u) { return min(u / spb, cols - 1); };
-  auto slot_col = [&](int c) { return min(kScaleSteps * c / spb, cols - 1); };
+  // the first scale column of the slot holding steps 8c .. 8c + 7
+  auto slot_col = [&](int c) {
+    return min(static_cast<int>(static_cast<uint32_t>(kScaleSteps * c) / static_cast<uint32_t>(spb)), cols - 1);
+  };
 
   const int nsteps = K / BK;
-  auto loads_for = [&](int u) { return Sh::kAL + Sh::kBL + (u % kScaleSteps == 0 ? Sh::kSL : 0); };
-  auto issue = [&](int u) {
+  int slot_first0 = 0, slot_first1 = 0;  // first scale column of scale slots 0 and 1, set when loaded
+  // The loads of step u into stage st (= u % 3): the scale slot first (every
+  // eighth step), then activations and weights, so that waiting until only
+  // those of the last issued step are in flight (a count that is the same
+  // every step) also covers its scales, issued a step earlier.
+  auto issue = [&](int u, int st) {
     const uint32_t step = static_cast<uint32_t>(u * BK);
-#pragma unroll
-    for (int j = 0; j < Sh::kAL; ++j)
-      lds_load16_so(a_rsrc, &L.a[u % 3][(8 * j + wave) * 8 * kLdsRow], a_off[j], 2u * step);
-#pragma unroll
-    for (int j = 0; j < Sh::kBL; ++j) lds_load16_so(b_rsrc, &L.b[u % 3][(8 * j + wave) * 1024], b_off[j], step);
     if (u % kScaleSteps == 0) {
       const int c = u / kScaleSteps;
-      const uint32_t base = 4u * static_cast<uint32_t>(slot_col(c));
+      const int first = slot_col(c);
+      if (c & 1)
+        slot_first1 = first;
+      else
+        slot_first0 = first;
+      const uint32_t base = 4u * static_cast<uint32_t>(first);
 #pragma unroll
       for (int j = 0; j < Sh::kSL; ++j)
         buf_load_lds<4>(s_rsrc, s_off[j] + base, &L.s[c & 1][(Sh::kSL * wave + j) * 256]);
     }
+#pragma unroll
+    for (int j = 0; j < Sh::kAL; ++j)
+      lds_load16_so(a_rsrc, &L.a[st][(8 * j + wave) * 8 * kLdsRow], a_off[j], 2u * step);
+#pragma unroll
+    for (int j = 0; j < Sh::kBL; ++j) lds_load16_so(b_rsrc, &L.b[st][(8 * j + wave) * 1024], b_off[j], step);
   };
+  constexpr int kStepLoads = Sh::kAL + Sh::kBL;
 
   const int c32 = lane & 31, h = lane >> 5;
   const int a_row0 = Sh::kWaveM * wm;  // this wave's first row in an activation stage
@@ -611,25 +603,35 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const T* __restrict__ A, 
       acc[i][j] = f32x16{};
       blk[i][j] = f32x16{};
     }
+  // per-lane LDS byte offsets of the operand reads within a stage:
+  // activation chunk 4h + i of row a_row0 + c32 (row tile ms adds 32 rows),
+  // weight pieces 2h and 2h + 1 of column 64 wn + 32 nt + c32
+  uint32_t a_rd[4], b_rd[2][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a_rd[i] = 2u * static_cast<uint32_t>(lds_index(a_row0 + c32, 4 * h + i));
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int col = 64 * wn + 32 * nt + c32;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) b_rd[nt][p] = static_cast<uint32_t>(col * 64 + 16 * ((2 * h + p) ^ b_swz(col)));
+  }
 
-  // The MFMAs of step u.  FRESH = u starts a scale block (its first MFMAs
-  // start from zero).
-  auto compute = [&](int u, auto fresh_c) {
+  // The MFMAs of step u (stage st).  FRESH = u starts a scale block (its
+  // first MFMAs start from zero).
+  auto compute = [&](int st, auto fresh_c) {
     constexpr bool FRESH = decltype(fresh_c)::value;
-    const T* a_src = L.a[u % 3];
+    const char* a_src = reinterpret_cast<const char*>(&L.a[0][0]) + st * sizeof(L.a[0]);
+    const char* b_src = reinterpret_cast<const char*>(&L.b[0][0]) + st * sizeof(L.b[0]);
     // lane (c32, h): k 32h .. 32h + 31 of its 2 columns (32 bytes)
     u32x4 bw[2][2];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int col = 64 * wn + 32 * nt + c32;
-      const uint8_t* bp = &L.b[u % 3][col * 64];
-      bw[nt][0] = *reinterpret_cast<const u32x4*>(bp + 16 * ((2 * h) ^ b_swz(col)));
-      bw[nt][1] = *reinterpret_cast<const u32x4*>(bp + 16 * ((2 * h + 1) ^ b_swz(col)));
-    }
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) bw[nt][p] = *reinterpret_cast<const u32x4*>(b_src + b_rd[nt][p]);
     auto read_a = [&](int i, V (&aop)[MS]) {
 #pragma unroll
       for (int ms = 0; ms < MS; ++ms)
-        aop[ms] = *reinterpret_cast<const V*>(&a_src[lds_index(a_row0 + 32 * ms + c32, 4 * h + i)]);
+        aop[ms] = *reinterpret_cast<const V*>(a_src + a_rd[i] + ms * (2 * 32 * kLdsRow));
     };
     auto dec_b = [&](int i, V (&bop)[2]) {
 #pragma unroll
@@ -668,11 +670,11 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const T* __restrict__ A, 
       for (int nt = 0; nt < 2; ++nt) bop[nt] = bn[nt];
     }
   };
-  // after the last step of a scale block: running sum += block sum * b_scale
-  // (FP32), column by column
-  auto flush = [&](int u) {
+  // after the last step u of the block with scale column c: running sum +=
+  // block sum * b_scale (FP32), column by column
+  auto flush = [&](int u, int c) {
     const uint8_t* s_src = L.s[(u / kScaleSteps) & 1];
-    const int idx = step_col(u) - slot_col(u / kScaleSteps);  // 0 .. 7
+    const int idx = c - ((u / kScaleSteps) & 1 ? slot_first1 : slot_first0);  // 0 .. 7
     float sc[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -686,34 +688,39 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const T* __restrict__ A, 
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[ms][nt][r] = fmaf(blk[ms][nt][r], sc[nt], acc[ms][nt][r]);
   };
-  // one step: its loads of step u + 2, its MFMAs, then the wait for the
-  // tiles of step u + 1
-  auto step_body = [&](int u, auto fresh_c) {
+  // one step u (stage st) of the block with scale column c ending before
+  // step `end`: its loads of step u + 2, its MFMAs, the flush after the
+  // block's last step, then the wait for the tiles of step u + 1
+  auto step_body = [&](int u, int st, int c, int end, auto fresh_c) {
     const bool ahead = u + 2 < nsteps;
-    if (ahead) issue(u + 2);
-    compute(u, fresh_c);
-    if (u == nsteps - 1 || step_col(u + 1) != step_col(u)) flush(u);
+    if (ahead) issue(u + 2, st == 0 ? 2 : st - 1);
+    compute(st, fresh_c);
+    if (u == end - 1) flush(u, c);
     if (ahead)
-      wait_all_but(loads_for(u + 2));  // the tiles of step u + 1 have landed
+      wait_barrier<kStepLoads>();  // the tiles of step u + 1 have landed
     else
       wait_barrier<0>();
   };
 
-  issue(0);
+  issue(0, 0);
   if (nsteps > 1) {
-    issue(1);
-    wait_all_but(loads_for(1));
+    issue(1, 1);
+    wait_barrier<kStepLoads>();
   } else {
     wait_barrier<0>();
   }
   // scale block by scale block: the first step of a block starts its sum
   // from zero, the last one flushes it (the last column also takes the
-  // partial final block)
-  for (int u0 = 0; u0 < nsteps;) {
-    const int c = step_col(u0);
+  // partial final block); st is the stage of step u, u % 3
+  int st = 0;
+  for (int u0 = 0, c = 0; u0 < nsteps; ++c) {  // block c starts at step c * spb
     const int end = c == cols - 1 ? nsteps : min(nsteps, (c + 1) * spb);
-    step_body(u0, std::true_type{});
-    for (int u = u0 + 1; u < end; ++u) step_body(u, std::false_type{});
+    step_body(u0, st, c, end, std::true_type{});
+    st = st == 2 ? 0 : st + 1;
+    for (int u = u0 + 1; u < end; ++u) {
+      step_body(u, st, c, end, std::false_type{});
+      st = st == 2 ? 0 : st + 1;
+    }
     u0 = end;
   }
 
