@@ -298,12 +298,16 @@ def hbm_read(sizes):
     `sizes` (name -> bytes per launch) the rate at that many bytes per launch
     over enough rotated slices to pass 1 GiB (past the last-level cache),
     launched back to back from a HIP graph.  Each is the best over grid sizes
-    and loads in flight per thread."""
+    and loads in flight per thread.  For each size it also streams the same
+    slices with the decode GEMV's load structure alone (no arithmetic)."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "fp8_weight_only_fp4w_amd", "libhbmprobe.so"))
     lib.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_uint32,
                                    ctypes.c_void_p, ctypes.c_void_p]
     lib.hbm_read_probe.restype = ctypes.c_int
+    lib.hbm_lds_stream_probe.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_uint32,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+    lib.hbm_lds_stream_probe.restype = ctypes.c_int
     grids, unrolls = (256, 512, 1024, 2048), (4, 8)
     big_bytes = 4 << 30
     buf = torch.full((big_bytes,), 1, dtype=torch.uint8, device="cuda")  # every thread's XOR is 0
@@ -345,6 +349,33 @@ def hbm_read(sizes):
                 del graph
         res["at_size"][name] = {"bytes": nb, "slices": slices, "GBps": max(sweep.values()),
                                 "config": max(sweep, key=sweep.get), "sweep": sweep}
+        # the decode GEMV's load structure alone (8-wave workgroups, 2 KiB
+        # units through per-wave LDS rings, 4 in flight), same slices
+        lsweep = {}
+        for g in (160, 256):
+            units = nb // (g * 8 * 2048)
+            if units < 1:
+                continue
+            sb = g * 8 * units * 2048
+
+            def lbody(g=g, units=units):
+                for i in range(slices):
+                    rc = lib.hbm_lds_stream_probe(ctypes.c_void_p(buf.data_ptr() + i * nb), nb, g, units, key,
+                                                  ctypes.c_void_p(sink.data_ptr()),
+                                                  ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                    if rc != 0:
+                        raise RuntimeError(f"hbm_lds_stream_probe failed ({rc})")
+            lbody()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                lbody()
+            graph.replay()
+            torch.cuda.synchronize()
+            t = time_calls([graph.replay], 5, 1)
+            lsweep[f"grid{g}"] = {"bytes": sb, "us": round(t / 5 / slices * 1e6, 2), "GBps": round(sb * slices * 5 / t / 1e9, 1)}
+            del graph
+        res["at_size"][name]["gemv_structure"] = lsweep
     del buf, sink
     return res
 

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_hbm_probe_library_exports_its_entry_point():
     # the bench's read-stream probe is built beside the matmul library and
-    # exports nothing but its one entry point
+    # exports nothing but its two entry points
     import ctypes
     import os
     import subprocess
@@ -47,7 +47,7 @@ def test_hbm_probe_library_exports_its_entry_point():
     assert hasattr(lib, "hbm_read_probe")
     out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
     exported = sorted(line.split()[-1] for line in out.splitlines() if " T " in line)
-    assert exported == ["hbm_read_probe"], exported
+    assert exported == ["hbm_lds_stream_probe", "hbm_read_probe"], exported
 
 
 def test_mfma_probe_library_exports_its_entry_point():
