@@ -19,14 +19,25 @@
 // instruction per pair) and every 16-k scale block gets its own FP32 dot,
 // scaled by its E4M3 value with one FMA.  Four blocks share each MFMA: lane
 // group g holds blocks 2g and 2g + 1 of the window, so in MFMA (s, p) the
-// four lane groups supply piece p (8 k) of blocks 2g + s, g = 0..3.  Row
-// i = 4 m' + q of the A operand carries activation row m = m' (+ 4 for the
-// second row half) in the k slots of lane group q only, and zeros elsewhere;
-// summing the two pieces p therefore leaves in result row (m', q) the full
-// dot of row m with block 2q + s.  The result lane (column n, group g) holds
-// rows 4g .. 4g + 3 = the four blocks of one activation row, so a window
-// costs 4 MFMAs and 8 FMAs per row half, with no data exchange between lanes.
-// weight_scale_2 and the bias are applied once in the epilogue.
+// four lane groups supply piece p (8 k) of blocks 2g + s, g = 0..3.  For
+// M <= 4, row i = 4 m' + q of the A operand carries activation row m' in the
+// k slots of lane group q only, and zeros elsewhere; summing the two pieces
+// p therefore leaves in result row (m', q) the full dot of row m' with block
+// 2q + s.  The result lane (column n, group g) holds rows 4g .. 4g + 3 = the
+// four blocks of one activation row, so a window costs 4 MFMAs and 8 FMAs,
+// with no data exchange between lanes.  weight_scale_2 and the bias are
+// applied once in the epilogue.
+//
+// FP4 with 5 <= M <= 8 ("row pairs").  Four activation rows per MFMA would
+// take two sets of MFMAs per window, each a quarter useful.  Instead, in MFMA
+// t (t = 0 .. 3) lane groups 0 and 1 supply the two 8-k pieces of block t of
+// the window and groups 2 and 3 those of block 4 + t, so a block's 16 k
+// meet in one MFMA; row i = 2m + h of the A operand carries activation row m
+// in the k slots of half h (groups 2h, 2h + 1) only.  Result row 2m + h is
+// then the dot of row m with block 4h + t, and the lane (n, g) holds rows
+// 2g and 2g + 1, each with two blocks: a window costs 4 MFMAs (half useful)
+// and 16 FMAs.  Lane group g's weights are piece g & 1 of four blocks, two
+// dwords from each of two 16-byte chunks (two ds_read2_b32).
 //
 // FP8 (16x16x32 MFMA).  E4M3 -> T is exact and the FP32 block scale is
 // applied to a window (128 k, inside one scale block: block_size % 128 == 0)
@@ -93,11 +104,11 @@ constexpr int kActLoads = FP8 ? 2 : 2 * R;
 constexpr uint32_t kStagePitch4 = 528;  // FP4: bytes per staged row (512 + 16)
 constexpr uint32_t kStagePitch8 = 272;  // FP8: bytes per staged row (256 + 16)
 
-// Staging bytes per wave: FP4 4R rows and a 64-byte zero block for the lanes
-// that carry no row; FP8 8 rows.
+// Staging bytes per wave: FP4 4R rows and a 128-byte zero block for the
+// lanes that carry no row; FP8 8 rows.
 template <bool FP8, int R>
 constexpr uint32_t stage_bytes() {
-  return FP8 ? 8u * kStagePitch8 : 4u * R * kStagePitch4 + 64u;
+  return FP8 ? 8u * kStagePitch8 : 4u * R * kStagePitch4 + 128u;
 }
 
 // Register part of one unit for one lane: the scale piece (first unit of
@@ -159,8 +170,9 @@ struct Pos {
 //    to whole 128-k windows; for FP4 a 256-byte zero block follows the M rows
 //    and serves the lanes that carry no row), so the loop issues weight loads
 //    only.
-// R: FP4 - row halves (1: M <= 4, 2: M <= 8); FP8 - result rows a lane
-// scales (1, 2 or 4).  D: units in flight ahead of the multiply.
+// R: FP4 - activation rows per lane (1: M <= 4, four rows per MFMA; 2:
+// M <= 8, row pairs); FP8 - result rows a lane scales (1, 2 or 4).  D: units
+// in flight ahead of the multiply.
 //
 // LDS: [kWaves][D + 1] unit slots, [kWaves] scale slices (a wave's slice also
 // takes its part of the K-split reduction at the end of a tile), then the
@@ -206,36 +218,35 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
   const uint32_t a_bytes = static_cast<uint32_t>(M) * static_cast<uint32_t>(K) * 2u;
   const rsrc_t a_rsrc = make_rsrc(A, a_bytes);
 
-  // Per-lane activation offsets (bytes, window 0).  FP4: lane (li = 4m' + q,
-  // g) carries row m = m' + 4h of half h when q == g, else zeros (the zero
-  // block in LDS, or an out-of-range offset).  FP8: row li (rows >= M are
-  // never stored, so lanes li >= M may read any valid row).
+  // Per-lane activation offset (bytes, window 0).  FP4, M <= 4: lane
+  // (li = 4m' + q, g) carries row m' when q == g; M <= 8: see the row pairs
+  // below; a lane that carries no row reads zeros (the zero block in LDS or
+  // in the staging area).  FP8: row li (rows >= M are never stored, so
+  // lanes li >= M may read any valid row).
   // In the staging area (ACT_REG) the same holds with the staged row pitch.
-  uint32_t a_off[FP8 ? 1 : R];
-  bool a_valid[FP8 ? 1 : R];
+  uint32_t a_off;
+  bool a_valid;
   if constexpr (FP8) {
-    a_off[0] = static_cast<uint32_t>(li % M) * (ACT_LDS ? lds_pitch : kStagePitch8);
-    a_valid[0] = true;
+    a_off = static_cast<uint32_t>(li % M) * (ACT_LDS ? lds_pitch : kStagePitch8);
+    a_valid = true;
+  } else if constexpr (R == 1) {
+    const int m = li >> 2;
+    a_valid = (li & 3) == g && m < M;
+    a_off = static_cast<uint32_t>(a_valid ? m : 0) * (ACT_LDS ? lds_pitch : kStagePitch4) + 64u * g;
   } else {
-#pragma unroll
-    for (int h = 0; h < R; ++h) {
-      const int m = (li >> 2) + 4 * h;
-      const bool valid = (li & 3) == g && m < M;
-      a_valid[h] = valid;
-      a_off[h] = static_cast<uint32_t>(valid ? m : 0) * (ACT_LDS ? lds_pitch : kStagePitch4) + 64u * g;
-    }
+    // row pairs: lane (li, g) carries row li >> 1 in the half (li & 1) of
+    // the window that its lane group serves (g >> 1), piece g & 1
+    const int m = li >> 1;
+    a_valid = (li & 1) == (g >> 1) && m < M;
+    a_off = static_cast<uint32_t>(a_valid ? m : 0) * (ACT_LDS ? lds_pitch : kStagePitch4) + 128u * (g >> 1) +
+            16u * (g & 1);
   }
   // ACT_LDS: the lane's LDS address of window 0 and its step per window; a
   // lane that carries no row keeps reading the zero block (step 0), so the
   // window loop computes each address with one multiply-add
   // (32-bit LDS addresses)
-  lds_cbytes a_win0[FP8 ? 1 : R];
-  uint32_t a_wstep[FP8 ? 1 : R];
-#pragma unroll
-  for (int h = 0; h < (FP8 ? 1 : R); ++h) {
-    a_win0[h] = (lds_cbytes)(a_lds + (a_valid[h] ? a_off[h] : zero_off));
-    a_wstep[h] = a_valid[h] ? 256u : 0u;
-  }
+  const lds_cbytes a_win0 = (lds_cbytes)(a_lds + (a_valid ? a_off : zero_off));
+  const uint32_t a_wstep = a_valid ? 256u : 0u;
   // ACT_REG: this wave's staging area, the lane's global offset (unit 0) in
   // the row-major loads and its place in the staging area.  FP4 load b:
   // rows 2b + (lane >> 5), 16 bytes at 16 (lane & 31) of the row's 512;
@@ -371,7 +382,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
   } else {
     // FP4: the staging area's zero block (wave-private: no barrier)
     if constexpr (!FP8)
-      if (lane < 4) *reinterpret_cast<u32x4*>(stage + 4u * R * kStagePitch4 + 16u * lane) = u32x4{0u, 0u, 0u, 0u};
+      if (lane < 8) *reinterpret_cast<u32x4*>(stage + 4u * R * kStagePitch4 + 16u * lane) = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       load(raw[d], ring + d * kUnitBytes);
@@ -404,7 +415,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
         for (int b = 0; b < kActLoads<FP8, R>; ++b)
           *reinterpret_cast<u32x4*>(stage + (kRowsPerLoad * b + st_row) * st_pitch + st_pos) = r.a[b];
       }
-      const unsigned char* q = (ACT_LDS ? a_lds + 256u * w : stage) + a_off[0] + 32u * g;
+      const unsigned char* q = (ACT_LDS ? a_lds + 256u * w : stage) + a_off + 32u * g;
       V a[4];
       a[0] = *reinterpret_cast<const V*>(q);
       a[1] = *reinterpret_cast<const V*>(q + 16u);
@@ -483,29 +494,37 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
       // window's arithmetic, so that the second window's reads overlap the
       // first window's work.
       u32x2 sb[2];
-      u32x4 av[2][R][4];
+      u32x4 av[2][4];
       u32x4 wv[2];
+      // activation fragment i of a window: 16 bytes at 16 i (M <= 4) or 32 i
+      // (row pairs) from the lane's offset
+      constexpr uint32_t kAStep = R == 1 ? 16u : 32u;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const int wa = min(2 * u + s2, NW - 1);  // windows past NW meet zero scales (zeroed in the slice)
         sb[s2] = *reinterpret_cast<const u32x2*>(slice + kSlicePitch * li + 8 * (2 * (j % SU) + s2));
-        // activations of the lane: 4 x 16 bytes per row half; chunk i = 2s + p
-        // holds k 32g + 16s + 8p .. + 7 of the window (piece p of set s)
+        if constexpr (ACT_LDS) {
+          const lds_cbytes q = a_win0 + __umul24(a_wstep, static_cast<uint32_t>(wa));
 #pragma unroll
-        for (int h = 0; h < R; ++h) {
-          if constexpr (ACT_LDS) {
-            const lds_cbytes q = a_win0[h] + __umul24(a_wstep[h], static_cast<uint32_t>(wa));
+          for (int i = 0; i < 4; ++i) av[s2][i] = *reinterpret_cast<const lds_u32x4*>(q + kAStep * i);
+        } else {
+          const unsigned char* q = stage + (a_valid ? a_off + 256u * s2 : 4u * R * kStagePitch4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) av[s2][h][i] = *reinterpret_cast<const lds_u32x4*>(q + 16u * i);
-          } else {
-            const unsigned char* q = stage + (a_valid[h] ? a_off[h] + 256u * s2 : 4u * R * kStagePitch4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) av[s2][h][i] = *reinterpret_cast<const u32x4*>(q + 16u * i);
-          }
+          for (int i = 0; i < 4; ++i) av[s2][i] = *reinterpret_cast<const u32x4*>(q + kAStep * i);
         }
-        // weights of the lane: chunk 4 s2 + g of row li (32 codes); dword
-        // 2s + p holds piece p of set s (block 2g + s)
-        wv[s2] = *reinterpret_cast<const u32x4*>(slot + 128 * li + 16 * ((4 * s2 + g) ^ sw));
+        if constexpr (R == 1) {
+          // chunk 4 s2 + g of row li (32 codes, blocks 2g and 2g + 1 of the
+          // window); dword 2s + p holds piece p of block 2g + s
+          wv[s2] = *reinterpret_cast<const u32x4*>(slot + 128 * li + 16 * ((4 * s2 + g) ^ sw));
+        } else {
+          // row pairs: dword t is piece g & 1 of block 4 (g >> 1) + t, from
+          // chunks 4 s2 + 2 (g >> 1) (t = 0, 1) and the next (t = 2, 3)
+          const int c = 4 * s2 + 2 * (g >> 1);
+          const unsigned char* p0 = slot + 128 * li + 16 * (c ^ sw) + 4 * (g & 1);
+          const unsigned char* p1 = slot + 128 * li + 16 * ((c + 1) ^ sw) + 4 * (g & 1);
+          wv[s2] = u32x4{*reinterpret_cast<const uint32_t*>(p0), *reinterpret_cast<const uint32_t*>(p0 + 8),
+                         *reinterpret_cast<const uint32_t*>(p1), *reinterpret_cast<const uint32_t*>(p1 + 8)};
+        }
       }
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
@@ -513,26 +532,41 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) bw[i] = Tr::decode8_fp4(wv[s2][i]);
         const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
-        f32x4 d[R][2];
-#pragma unroll
-        for (int h = 0; h < R; ++h)
+        // scale of block b of the window: byte b
+        auto scales = [&](float (&sc)[8]) {
+          const f32x2 s01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb[s2].x), false);
+          const f32x2 s23 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb[s2].x), true);
+          const f32x2 s45 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb[s2].y), false);
+          const f32x2 s67 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb[s2].y), true);
+          sc[0] = s01.x; sc[1] = s01.y; sc[2] = s23.x; sc[3] = s23.y;
+          sc[4] = s45.x; sc[5] = s45.y; sc[6] = s67.x; sc[7] = s67.y;
+        };
+        float sc[8];
+        if constexpr (R == 1) {
+          f32x4 d[2];
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
-            d[h][s] = Tr::mfma(__builtin_bit_cast(V, av[s2][h][2 * s]), bw[2 * s], zero);
-            d[h][s] = Tr::mfma(__builtin_bit_cast(V, av[s2][h][2 * s + 1]), bw[2 * s + 1], d[h][s]);
+            d[s] = Tr::mfma(__builtin_bit_cast(V, av[s2][2 * s]), bw[2 * s], zero);
+            d[s] = Tr::mfma(__builtin_bit_cast(V, av[s2][2 * s + 1]), bw[2 * s + 1], d[s]);
           }
-        // result row r of set s is block 2r + s: scale byte 2r + s
-        const f32x2 s01 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb[s2].x), false);
-        const f32x2 s23 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb[s2].x), true);
-        const f32x2 s45 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb[s2].y), false);
-        const f32x2 s67 = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(sb[s2].y), true);
-        const float sc[8] = {s01.x, s01.y, s23.x, s23.y, s45.x, s45.y, s67.x, s67.y};
-#pragma unroll
-        for (int h = 0; h < R; ++h)
+          scales(sc);
+          // result row rr of set s is block 2 rr + s of row g
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
-            for (int s = 0; s < 2; ++s) acc[h] = fmaf(d[h][s][rr], sc[2 * rr + s], acc[h]);
+            for (int s = 0; s < 2; ++s) acc[0] = fmaf(d[s][rr], sc[2 * rr + s], acc[0]);
+        } else {
+          // MFMA t: result row r is block 4 (r & 1) + t of row 2g + (r >> 1)
+          scales(sc);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const f32x4 d = Tr::mfma(__builtin_bit_cast(V, av[s2][t]), bw[t], zero);
+            acc[0] = fmaf(d[0], sc[t], acc[0]);
+            acc[0] = fmaf(d[1], sc[4 + t], acc[0]);
+            acc[1] = fmaf(d[2], sc[t], acc[1]);
+            acc[1] = fmaf(d[3], sc[4 + t], acc[1]);
+          }
+        }
       }
     }
     if (j == nus - 1) {
@@ -562,7 +596,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
           } else {
 #pragma unroll
             for (int h = 0; h < R; ++h) {
-              const int m = g + 4 * h;
+              const int m = R == 1 ? g : 2 * g + h;  // the lane's rows
               if (m < M) Y[static_cast<size_t>(m) * N + n] = round_to<T>(fmaf(acc[h], ws2, b));
             }
           }
@@ -771,7 +805,7 @@ int launch_t(const MatmulArgs& a) {
     return -1;
   const int M = static_cast<int>(a.M);
   const int NW = static_cast<int>((a.K + 127) / 128);
-  // FP8: result rows a lane scales; FP4: row halves
+  // FP8: result rows a lane scales; FP4: activation rows per lane
   const int R = FP8 ? (M >= 3 ? 4 : M) : (M > 4 ? 2 : 1);
   const Plan p = cached_plan<T, FP8>(a.N, M, R, NW);
   const int tiles = static_cast<int>((a.N + 15) / 16);

@@ -38,6 +38,9 @@ FP4_CASES = [
     (1, 77, 32, 16, "bf16", False, "ceil", [fw.PATH_FP4_GEMV]),
     (5, 4100, 5152, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMV]),
     (4, 300, 17440, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMV]),  # streamed activations, 137 windows
+    # M = 5 .. 8 (row pairs) with streamed activations, one with a last window of 32 k
+    (8, 300, 17440, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMV]),
+    (6, 200, 12320, 16, "fp16", False, "ceil", [fw.PATH_FP4_GEMV]),
     (8, 777, 1024, 16, "bf16", False, "ceil", [fw.PATH_FP4_GEMV, fw.PATH_FP4_GEMM]),
     (5, 65590, 128, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMV]),  # 2 tiles per wave, ragged N
     (9, 300, 128, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMM, fw.PATH_FP4_GENERIC]),
@@ -132,7 +135,8 @@ def test_fp4_one_hot_probe_bit_exact(M, N, K, path, dtype):
 
 
 @pytest.mark.parametrize("M,N,K,path", [
-    (4, 64, 256, fw.PATH_FP4_GEMV), (24, 64, 256, fw.PATH_FP4_SKINNY), (130, 520, 256, fw.PATH_FP4_GEMM),
+    (4, 64, 256, fw.PATH_FP4_GEMV), (8, 64, 256, fw.PATH_FP4_GEMV), (24, 64, 256, fw.PATH_FP4_SKINNY),
+    (130, 520, 256, fw.PATH_FP4_GEMM),
     (4, 64, 256, fw.PATH_FP4_GENERIC),
 ])
 def test_fp4_fp16_overflow_rounds_to_inf(M, N, K, path):
@@ -158,14 +162,15 @@ def test_fp4_fp16_overflow_rounds_to_inf(M, N, K, path):
     assert_parity(got, "fp16", Y_ref, S, f"fp16 overflow path {path}")
 
 
+@pytest.mark.parametrize("M", [4, 7])
 @pytest.mark.parametrize("K", [480, 352, 160])
-def test_fp4_gemv_partial_window_masks_next_row_scales(K):
+def test_fp4_gemv_partial_window_masks_next_row_scales(K, M):
     """K % 128 != 0: the last 128-k window of a row reads scale bytes past the
     row's last column, which belong to the next row.  Every odd row's first
     8 scale bytes hold the E4M3 NaN code 0x7F: the odd rows' outputs are NaN
     (their own scales), and the even rows' must not be touched by them."""
     require_gpu()
-    p = workloads.make_fp4(4, 96, K, 16, "bf16", seed=K, with_bias=True)
+    p = workloads.make_fp4(M, 96, K, 16, "bf16", seed=K + M, with_bias=True)
     p.weight_scale[1::2, :8] = 0x7F
     Y_ref, S = ref_fp4(p)
     assert np.isnan(Y_ref[:, 1::2]).all() and np.isfinite(Y_ref[:, 0::2]).all()
