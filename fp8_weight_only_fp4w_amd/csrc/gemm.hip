@@ -25,6 +25,9 @@
 //    which is then added to the running sum multiplied by its b_scale in FP32
 //    ([FP8 doc] §2: B_dq = e4m3 * b_scale).  The two sets take 128 registers
 //    per lane, which is why an FP8 wave holds half the outputs of an FP4 one.
+//    The two waves sharing a SIMD add their block sums at different times
+//    (one before, one after the barrier that ends the block), so that one's
+//    FMAs issue beside the other's MFMAs.
 //
 // [FP4 doc] = "MatMulBlockQuantizedFp4Weight - CUDA Operator Documentation"
 // [FP8 doc] = "MatMulBlockQuantizedFp8Weight - CUDA Operator Documentation"
@@ -596,6 +599,12 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const T* __restrict__ A, 
   const int a_row0 = Sh::kWaveM * wm;  // this wave's first row in an activation stage
   f32x16 acc[MS][2];
   f32x16 blk[MS][2];  // the current scale block's sum (fresh at the first step of a block)
+  // The two waves of a SIMD (wm = 0 and 1, same wn) flush at different
+  // times, so that one's flush FMAs issue beside the other's MFMAs: wm = 0
+  // after the block's last MFMAs, before the barrier that ends the step;
+  // wm = 1 after that barrier, while wm = 0 starts the next step.
+  const bool late = wm == 1;
+  float psc[2];  // the block's b_scales, per column tile
 #pragma unroll
   for (int i = 0; i < MS; ++i)
 #pragma unroll
@@ -616,6 +625,15 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const T* __restrict__ A, 
     for (int p = 0; p < 2; ++p) b_rd[nt][p] = static_cast<uint32_t>(col * 64 + 16 * ((2 * h + p) ^ b_swz(col)));
   }
 
+  // running sum += block sum * b_scale (FP32), column by column
+  auto flush_all = [&]() {
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[ms][nt][r] = fmaf(blk[ms][nt][r], psc[nt], acc[ms][nt][r]);
+  };
   // The MFMAs of step u (stage st).  FRESH = u starts a scale block (its
   // first MFMAs start from zero).
   auto compute = [&](int st, auto fresh_c) {
@@ -670,36 +688,32 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const T* __restrict__ A, 
       for (int nt = 0; nt < 2; ++nt) bop[nt] = bn[nt];
     }
   };
-  // after the last step u of the block with scale column c: running sum +=
-  // block sum * b_scale (FP32), column by column
-  auto flush = [&](int u, int c) {
+  // after the last step u of the block with scale column c: its b_scales;
+  // wm = 0 flushes now
+  auto block_end = [&](int u, int c) {
     const uint8_t* s_src = L.s[(u / kScaleSteps) & 1];
     const int idx = c - ((u / kScaleSteps) & 1 ? slot_first1 : slot_first0);  // 0 .. 7
-    float sc[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int col = 64 * wn + 32 * nt + c32;
-      sc[nt] = *reinterpret_cast<const float*>(&s_src[col * 32 + 16 * ((idx >> 2) ^ ((col >> 3) & 1)) + 4 * (idx & 3)]);
+      psc[nt] = *reinterpret_cast<const float*>(&s_src[col * 32 + 16 * ((idx >> 2) ^ ((col >> 3) & 1)) + 4 * (idx & 3)]);
     }
-#pragma unroll
-    for (int ms = 0; ms < MS; ++ms)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[ms][nt][r] = fmaf(blk[ms][nt][r], sc[nt], acc[ms][nt][r]);
+    if (!late) flush_all();
   };
   // one step u (stage st) of the block with scale column c ending before
-  // step `end`: its loads of step u + 2, its MFMAs, the flush after the
-  // block's last step, then the wait for the tiles of step u + 1
+  // step `end`: its loads of step u + 2, its MFMAs, the block's b_scales (and
+  // for wm = 0 its flush) after its last step, then the wait for the tiles of
+  // step u + 1
   auto step_body = [&](int u, int st, int c, int end, auto fresh_c) {
     const bool ahead = u + 2 < nsteps;
     if (ahead) issue(u + 2, st == 0 ? 2 : st - 1);
     compute(st, fresh_c);
-    if (u == end - 1) flush(u, c);
+    if (u == end - 1) block_end(u, c);
     if (ahead)
       wait_barrier<kStepLoads>();  // the tiles of step u + 1 have landed
     else
       wait_barrier<0>();
+    if (late && u == end - 1) flush_all();  // beside the other wave's next MFMAs
   };
 
   issue(0, 0);
@@ -710,8 +724,8 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const T* __restrict__ A, 
     wait_barrier<0>();
   }
   // scale block by scale block: the first step of a block starts its sum
-  // from zero, the last one flushes it (the last column also takes the
-  // partial final block); st is the stage of step u, u % 3
+  // from zero, the last one takes its b_scales (the last column also takes
+  // the partial final block); st is the stage of step u, u % 3
   int st = 0;
   for (int u0 = 0, c = 0; u0 < nsteps; ++c) {  // block c starts at step c * spb
     const int end = c == cols - 1 ? nsteps : min(nsteps, (c + 1) * spb);
