@@ -25,9 +25,8 @@
 //    which is then added to the running sum multiplied by its b_scale in FP32
 //    ([FP8 doc] §2: B_dq = e4m3 * b_scale).  The two sets take 128 registers
 //    per lane, which is why an FP8 wave holds half the outputs of an FP4 one.
-//    The two waves sharing a SIMD add their block sums at different times
-//    (one before, one after the barrier that ends the block), so that one's
-//    FMAs issue beside the other's MFMAs.
+//    A step's last MFMA group issues after the barrier that ends it, beside
+//    the next step's first operand reads.
 //
 // [FP4 doc] = "MatMulBlockQuantizedFp4Weight - CUDA Operator Documentation"
 // [FP8 doc] = "MatMulBlockQuantizedFp8Weight - CUDA Operator Documentation"
@@ -599,12 +598,6 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const T* __restrict__ A, 
   const int a_row0 = Sh::kWaveM * wm;  // this wave's first row in an activation stage
   f32x16 acc[MS][2];
   f32x16 blk[MS][2];  // the current scale block's sum (fresh at the first step of a block)
-  // The two waves of a SIMD (wm = 0 and 1, same wn) flush at different
-  // times, so that one's flush FMAs issue beside the other's MFMAs: wm = 0
-  // after the block's last MFMAs, before the barrier that ends the step;
-  // wm = 1 after that barrier, while wm = 0 starts the next step.
-  const bool late = wm == 1;
-  float psc[2];  // the block's b_scales, per column tile
 #pragma unroll
   for (int i = 0; i < MS; ++i)
 #pragma unroll
@@ -625,61 +618,76 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const T* __restrict__ A, 
     for (int p = 0; p < 2; ++p) b_rd[nt][p] = static_cast<uint32_t>(col * 64 + 16 * ((2 * h + p) ^ b_swz(col)));
   }
 
-  // running sum += block sum * b_scale (FP32), column by column
-  auto flush_all = [&]() {
+  // Operands carried from step to step: the raw weights of the current step
+  // (bw) and the decoded operands of its first MFMA group (aop, bop).  They
+  // are read after the barrier that ends the previous step, beside that
+  // step's last MFMA group, so a step never starts by waiting for LDS.
+  // Lane (c32, h) takes k 32h .. 32h + 31 of its 2 columns (32 bytes).
+  u32x4 bw[2][2];
+  V aop[MS], bop[2];
+  auto stage_a = [&](int st) { return reinterpret_cast<const char*>(&L.a[0][0]) + st * sizeof(L.a[0]); };
+  auto read_a = [&](const char* a_src, int i, V (&o)[MS]) {
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) o[ms] = *reinterpret_cast<const V*>(a_src + a_rd[i] + ms * (2 * 32 * kLdsRow));
+  };
+  auto read_bw = [&](int st) {
+    const char* b_src = reinterpret_cast<const char*>(&L.b[0][0]) + st * sizeof(L.b[0]);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) bw[nt][p] = *reinterpret_cast<const u32x4*>(b_src + b_rd[nt][p]);
+  };
+  auto dec_b = [&](int i, V (&o)[2]) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) o[nt] = Tr::decode8_fp8(bw[nt][i >> 1][2 * (i & 1)], bw[nt][i >> 1][2 * (i & 1) + 1]);
+  };
+  // after the last step u of the block with scale column c: running sum +=
+  // block sum * b_scale (FP32), column by column
+  auto flush = [&](int u, int c) {
+    const uint8_t* s_src = L.s[(u / kScaleSteps) & 1];
+    const int idx = c - ((u / kScaleSteps) & 1 ? slot_first1 : slot_first0);  // 0 .. 7
+    float sc[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int col = 64 * wn + 32 * nt + c32;
+      sc[nt] = *reinterpret_cast<const float*>(&s_src[col * 32 + 16 * ((idx >> 2) ^ ((col >> 3) & 1)) + 4 * (idx & 3)]);
+    }
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[ms][nt][r] = fmaf(blk[ms][nt][r], psc[nt], acc[ms][nt][r]);
+        for (int r = 0; r < 16; ++r) acc[ms][nt][r] = fmaf(blk[ms][nt][r], sc[nt], acc[ms][nt][r]);
   };
-  // The MFMAs of step u (stage st).  FRESH = u starts a scale block (its
-  // first MFMAs start from zero).
-  auto compute = [&](int st, auto fresh_c) {
+  // One step u (stage st) of the block with scale column c ending before
+  // step `end`: its loads of step u + 2; MFMA groups 0 - 2, each beside the
+  // reads and decode of the next group's operands (group 0 starts a block's
+  // sum from zero); the barrier after which the tiles of step u + 1 have
+  // landed and no wave reads stage st any more; group 3 beside the reads of
+  // step u + 1's first operands (after the last step: re-reads, unused);
+  // after the block's last step its flush.
+  auto step_body = [&](int u, int st, int c, int end, auto fresh_c) {
     constexpr bool FRESH = decltype(fresh_c)::value;
-    const char* a_src = reinterpret_cast<const char*>(&L.a[0][0]) + st * sizeof(L.a[0]);
-    const char* b_src = reinterpret_cast<const char*>(&L.b[0][0]) + st * sizeof(L.b[0]);
-    // lane (c32, h): k 32h .. 32h + 31 of its 2 columns (32 bytes)
-    u32x4 bw[2][2];
+    const bool ahead = u + 2 < nsteps;
+    if (ahead) issue(u + 2, st == 0 ? 2 : st - 1);
+    const char* a_src = stage_a(st);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int p = 0; p < 2; ++p) bw[nt][p] = *reinterpret_cast<const u32x4*>(b_src + b_rd[nt][p]);
-    auto read_a = [&](int i, V (&aop)[MS]) {
-#pragma unroll
-      for (int ms = 0; ms < MS; ++ms)
-        aop[ms] = *reinterpret_cast<const V*>(a_src + a_rd[i] + ms * (2 * 32 * kLdsRow));
-    };
-    auto dec_b = [&](int i, V (&bop)[2]) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        bop[nt] = Tr::decode8_fp8(bw[nt][i >> 1][2 * (i & 1)], bw[nt][i >> 1][2 * (i & 1) + 1]);
-    };
-    V aop[MS], bop[2];
-    read_a(0, aop);
-    dec_b(0, bop);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 3; ++i) {
       V an[MS], bn[2];
-      if (i < 3) {
-        read_a(i + 1, an);
-        dec_b(i + 1, bn);
-      }
+      read_a(a_src, i + 1, an);
+      dec_b(i + 1, bn);
 #pragma unroll
       for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
           blk[ms][nt] = mfma32<T>(aop[ms], bop[nt], FRESH && i == 0 ? f32x16{} : blk[ms][nt]);
-      if (i < 3) {
-        // per MFMA: one LDS read (first MS MFMAs), then a share of the next
-        // group's decode
+      // per MFMA: one LDS read (first MS MFMAs), then a share of the next
+      // group's decode
 #pragma unroll
-        for (int k = 0; k < 2 * MS; ++k) {
-          if (k < MS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);              // vector ALU
-        }
+      for (int k = 0; k < 2 * MS; ++k) {
+        if (k < MS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);              // vector ALU
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -687,33 +695,38 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const T* __restrict__ A, 
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) bop[nt] = bn[nt];
     }
-  };
-  // after the last step u of the block with scale column c: its b_scales;
-  // wm = 0 flushes now
-  auto block_end = [&](int u, int c) {
-    const uint8_t* s_src = L.s[(u / kScaleSteps) & 1];
-    const int idx = c - ((u / kScaleSteps) & 1 ? slot_first1 : slot_first0);  // 0 .. 7
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int col = 64 * wn + 32 * nt + c32;
-      psc[nt] = *reinterpret_cast<const float*>(&s_src[col * 32 + 16 * ((idx >> 2) ^ ((col >> 3) & 1)) + 4 * (idx & 3)]);
-    }
-    if (!late) flush_all();
-  };
-  // one step u (stage st) of the block with scale column c ending before
-  // step `end`: its loads of step u + 2, its MFMAs, the block's b_scales (and
-  // for wm = 0 its flush) after its last step, then the wait for the tiles of
-  // step u + 1
-  auto step_body = [&](int u, int st, int c, int end, auto fresh_c) {
-    const bool ahead = u + 2 < nsteps;
-    if (ahead) issue(u + 2, st == 0 ? 2 : st - 1);
-    compute(st, fresh_c);
-    if (u == end - 1) block_end(u, c);
     if (ahead)
-      wait_barrier<kStepLoads>();  // the tiles of step u + 1 have landed
+      wait_barrier<kStepLoads>();
     else
       wait_barrier<0>();
-    if (late && u == end - 1) flush_all();  // beside the other wave's next MFMAs
+    {
+      V a3[MS], b3[2];
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) a3[ms] = aop[ms];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) b3[nt] = bop[nt];
+      const int st1 = st == 2 ? 0 : st + 1;
+      read_bw(st1);
+      read_a(stage_a(st1), 0, aop);
+      dec_b(0, bop);
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) blk[ms][nt] = mfma32<T>(a3[ms], b3[nt], blk[ms][nt]);
+      // per MFMA: the next step's weight reads (first four) or activation
+      // reads, and a share of its first decode
+#pragma unroll
+      for (int k = 0; k < 2 * MS; ++k) {
+        if (k == 0)
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // LDS read
+        else
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              // MFMA
+        if (k >= 2) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // vector ALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (u == end - 1) flush(u, c);
   };
 
   issue(0, 0);
@@ -723,9 +736,12 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const T* __restrict__ A, 
   } else {
     wait_barrier<0>();
   }
+  read_bw(0);
+  read_a(stage_a(0), 0, aop);
+  dec_b(0, bop);
   // scale block by scale block: the first step of a block starts its sum
-  // from zero, the last one takes its b_scales (the last column also takes
-  // the partial final block); st is the stage of step u, u % 3
+  // from zero, the last one flushes it (the last column also takes the
+  // partial final block); st is the stage of step u, u % 3
   int st = 0;
   for (int u0 = 0, c = 0; u0 < nsteps; ++c) {  // block c starts at step c * spb
     const int end = c == cols - 1 ? nsteps : min(nsteps, (c + 1) * spb);
@@ -739,8 +755,9 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const T* __restrict__ A, 
   }
 
   // Epilogue: lane (c, h) holds columns 64 wn + 32 nt + c and rows
-  // 64 wm + 32 ms + 8 (r / 4) + 4 h + r % 4 of the tile; the last step ended
-  // with a barrier after every LDS read, so the operand rings are free.
+  // 64 wm + 32 ms + 8 (r / 4) + 4 h + r % 4 of the tile; after a barrier
+  // that follows every wave's last LDS reads, the operand rings are free.
+  __syncthreads();
   constexpr int kOutPitch = Sh::kTN + 8;
   static_assert(sizeof(L) >= Sh::kTM * kOutPitch * sizeof(T), "output staging exceeds LDS");
   T* out = reinterpret_cast<T*>(&L);
