@@ -115,12 +115,19 @@ def capture(fn):
     return g
 
 
-def time_graphs(graphs, steps, warmup):
-    """Replay graphs round-robin: warmup untimed, then exactly `steps` timed
-    replays bracketed by synchronisation; returns (wall s, event s)."""
+def time_graphs(graphs, steps, warmup, min_warm_s=0.0):
+    """Replay graphs round-robin: warmup untimed (at least `warmup` replays
+    and, in whole rounds over the graphs, at least `min_warm_s` seconds),
+    then exactly `steps` timed replays bracketed by synchronisation; returns
+    (wall s, event s)."""
     for i in range(warmup):
         graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < min_warm_s:
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record()
@@ -134,11 +141,14 @@ def time_graphs(graphs, steps, warmup):
 
 def time_rotating(call, R, launches, G=8):
     """Per-launch seconds of call(r) over rotating copies r = 0 .. R-1, from
-    graphs of G launches each (HIP events around the timed replays)."""
+    graphs of G launches each (HIP events around the timed replays).  The
+    untimed warm-up runs for at least 30 ms: right after the inputs are
+    built the GPU needs that long to reach its steady rate (the wide GEMV's
+    first 64 launches ran 16 % slower than the ones after them)."""
     n = -(-R // G)
     gs = [capture(lambda i=i: [call((i * G + k) % R) for k in range(G)]) for i in range(n)]
     reps = max(1, launches // G)
-    _, e = time_graphs(gs, reps, min(reps, 4))
+    _, e = time_graphs(gs, reps, min(reps, 4), min_warm_s=0.03)
     del gs
     return e / (reps * G)
 
