@@ -713,8 +713,8 @@ __global__ __launch_bounds__(512) void gemm_fp8_kernel(const T* __restrict__ A, 
       for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) blk[ms][nt] = mfma32<T>(a3[ms], b3[nt], blk[ms][nt]);
-      // per MFMA: the next step's weight reads (first four) or activation
-      // reads, and a share of its first decode
+      // per MFMA: some of the next step's six operand reads (three beside
+      // the first), and from the third on a share of its first decode
 #pragma unroll
       for (int k = 0; k < 2 * MS; ++k) {
         if (k == 0)
