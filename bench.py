@@ -169,7 +169,7 @@ def time_calls(fn_list, steps, warmup):
 
 # ------------------------------------------------------------------ headline
 
-STEPS_PER_GRAPH = 8   # steps captured in one graph (amortises the graph launch)
+STEPS_PER_GRAPH = 20  # steps captured in one graph (80 launches: amortises the graph launch, as a decode step's graph of ~120 GEMVs does)
 
 
 def gemv_decode(steps, warmup):
@@ -189,11 +189,11 @@ def gemv_decode(steps, warmup):
 
     # graphs of STEPS_PER_GRAPH consecutive steps (each step on the next copy
     # of the weights), and single-step graphs for a remainder
-    G = STEPS_PER_GRAPH
+    G = max(1, min(STEPS_PER_GRAPH, steps))
     n_groups = -(-R // G)
     groups = [capture(lambda i=i: [step((i * G + k) % R) for k in range(G)]) for i in range(n_groups)]
     singles = [capture(lambda r=r: step(r)) for r in range(min(R, G))]
-    for i in range(max(1, warmup // G)):
+    for i in range(warmup // G):
         groups[i % n_groups].replay()
     for i in range(warmup % G):
         singles[i % len(singles)].replay()
