@@ -139,9 +139,10 @@ def time_graphs(graphs, steps, warmup, min_warm_s=0.0):
     return wall, start.elapsed_time(stop) / 1e3
 
 
-def time_rotating(call, R, launches, G=8):
+def time_rotating(call, R, launches, G=20):
     """Per-launch seconds of call(r) over rotating copies r = 0 .. R-1, from
-    graphs of G launches each (HIP events around the timed replays).  The
+    graphs of G launches each (HIP events around the timed replays; 20, as
+    the headline's graphs hold 20 steps).  The
     untimed warm-up runs for at least 30 ms: right after the inputs are
     built the GPU needs that long to reach its steady rate (the wide GEMV's
     first 64 launches ran 16 % slower than the ones after them)."""
