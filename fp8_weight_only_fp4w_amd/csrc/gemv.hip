@@ -700,10 +700,9 @@ struct Plan {
 // L2 per window costs more load instructions than the weights themselves),
 // with the deep ring when it fits beside them.  The K split KS (and with it
 // TPW = 8 / KS tiles side by side) is the one with the least work on the
-// busiest wave: rounds of tile groups per workgroup (the grid is the number
-// of tile groups, capped at the resident workgroups: persistent) times units
-// per wave, counting the units a wave pads with when KS does not divide the
-// row.  Ties go to the split with fewer padded units, then to the larger
+// busiest wave: rounds of tile groups per workgroup (persistent workgroups,
+// at most the resident ones) times units per wave, counting the units a wave
+// pads with when KS does not divide the row.  Ties go to the split with fewer padded units, then to the larger
 // split; every wave keeps at least one unit.
 template <typename T, bool FP8>
 int slots_mode(int mode, int ks, int R, int M, int NW) {
@@ -723,9 +722,14 @@ Plan plan(int64_t N, int M, int R, int NW) {
     if (NU < ks) continue;
     const int64_t ntg = (tiles + kWaves / ks - 1) / (kWaves / ks);
     const int64_t slots = slots_mode<T, FP8>(mode, ks, R, M, NW);
-    const int64_t grid = ntg < slots ? ntg : slots;
+    // rounds of tile groups on the resident workgroups, then as few
+    // workgroups as give every one the same number of rounds (one less for
+    // some): a last, partial round would run on few CUs, each held to its own
+    // memory rate, while the same bytes spread over all rounds keep HBM busy
+    const int64_t rounds = (ntg + slots - 1) / slots;
+    const int64_t grid = (ntg + rounds - 1) / rounds;
     const int nus = (NU + ks - 1) / ks;
-    const int64_t cost = (ntg + grid - 1) / grid * nus;
+    const int64_t cost = rounds * nus;
     const int pad = nus * ks - NU;
     if (best_cost < 0 || cost < best_cost || (cost == best_cost && pad < best_pad)) {
       best_cost = cost;
