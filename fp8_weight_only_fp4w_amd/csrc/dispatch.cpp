@@ -421,6 +421,14 @@ int fp4w_matmul_w4a4(const void* A, int64_t M, int64_t K, const uint8_t* B, int6
       overlaps(A_work, abytes, weight_scale, N * scale_cols) || overlaps(A_work, abytes, weight_scale_2, 4) ||
       overlaps(A_work, abytes, bias, N * 2))
     return FP4W_ERR_ALIAS;
+  if (mm_path == FP4W_PATH_FP4_GEMV && A_work != A && aligned(A, 16)) {
+    // Decode: the GEMV quantize-dequantizes its LDS copy of A itself (and
+    // writes it to A_work); 1 = the activations do not fit in LDS.
+    MatmulArgs f = a;
+    f.A = A;
+    const int rc = fp4w::launch_fp4_gemv_w4a4(f, A_work);
+    if (rc <= 0) return rc == 0 ? FP4W_OK : FP4W_ERR_LAUNCH;
+  }
   st = launch_nvfp4(q_path, q, false);
   if (st != FP4W_OK) return st;
   return launch_matmul(mm_path, a);

@@ -61,6 +61,7 @@
 
 #include "device.h"
 #include "launch.h"
+#include "nvfp4_block.h"
 
 namespace fp4w {
 namespace {
@@ -177,11 +178,13 @@ struct Pos {
 // LDS: [kWaves][D + 1] unit slots, [kWaves] scale slices (a wave's slice also
 // takes its part of the K-split reduction at the end of a tile), then the
 // activation rows (ACT_LDS) or [kWaves] activation staging areas (ACT_REG).
-template <typename T, int KS, bool FP8, bool ACT_LDS, int R, int D>
+template <typename T, int KS, bool FP8, bool ACT_LDS, int R, int D, bool QDQ>
 __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
     const T* __restrict__ A, const uint8_t* __restrict__ B, const void* __restrict__ scales,
     const float* __restrict__ ws2p, const T* __restrict__ bias, T* __restrict__ Y, int M, int N,
-    int K, int cols, FastDiv halves_per_block, FastDiv chunks_per_row, int num_tiles, int nus) {
+    int K, int cols, FastDiv halves_per_block, FastDiv chunks_per_row, int num_tiles, int nus,
+    T* __restrict__ a_work) {
+  static_assert(!QDQ || (!FP8 && ACT_LDS), "the W4A4 activation copy is an FP4, LDS-resident mode");
   constexpr bool ACT_REG = !ACT_LDS;
   constexpr int TPW = kWaves / KS;
   constexpr int S = D + 1;          // unit slots (LDS ring and registers)
@@ -379,6 +382,36 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_kernel(
     wait_vm<2 * D>();
     __builtin_amdgcn_s_barrier();
     __asm__ volatile("" ::: "memory");
+    if constexpr (QDQ) {
+      // W4A4: the copy becomes its NVFP4 quantize-dequantize, in place,
+      // block by block (16 k of one row; the row padding and the zero block
+      // are zeros and would stay zeros); the first workgroup also writes it
+      // to a_work.  The weight loads issued above stay in flight meanwhile.
+      typedef typename ActTraits<T>::vec8 V;
+      const uint32_t kbr = static_cast<uint32_t>(K) >> 4;  // blocks per row (K % 16 == 0)
+      const uint32_t nblk = static_cast<uint32_t>(M) * kbr;
+      for (uint32_t b = threadIdx.x; b < nblk; b += 64u * kWaves) {
+        const uint32_t m = b / kbr, kb = b - m * kbr;
+        unsigned char* p = a_lds + m * lds_pitch + 32u * kb;
+        const V x0 = *reinterpret_cast<const V*>(p), x1 = *reinterpret_cast<const V*>(p + 16);
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          v[i] = static_cast<float>(x0[i]);
+          v[8 + i] = static_cast<float>(x1[i]);
+        }
+        V r[2];
+        nvfp4_qdq_block<T>(v, r);
+        *reinterpret_cast<V*>(p) = r[0];
+        *reinterpret_cast<V*>(p + 16) = r[1];
+        if (blockIdx.x == 0) {
+          u32x4* q = reinterpret_cast<u32x4*>(a_work + static_cast<size_t>(m) * K + 16u * kb);
+          q[0] = __builtin_bit_cast(u32x4, r[0]);
+          q[1] = __builtin_bit_cast(u32x4, r[1]);
+        }
+      }
+      lds_barrier();
+    }
   } else {
     // FP4: the staging area's zero block (wave-private: no barrier)
     if constexpr (!FP8)
@@ -645,17 +678,17 @@ size_t lds_bytes(int mode, bool fp8, int M, int NW) {
   return ring + slices + act;
 }
 
-template <typename T, int KS, bool FP8, int MODE, int R>
+template <typename T, int KS, bool FP8, int MODE, int R, bool QDQ = false>
 constexpr auto kernel_ptr() {
-  return &gemv_kernel<T, KS, FP8, (MODE > 0), R, depth<FP8, MODE, R>()>;
+  return &gemv_kernel<T, KS, FP8, (MODE > 0), R, depth<FP8, MODE, R>(), QDQ>;
 }
 
 // Dynamic LDS above 64 KiB must be allowed per kernel, once per device.
-template <typename T, int KS, bool FP8, int MODE, int R>
+template <typename T, int KS, bool FP8, int MODE, int R, bool QDQ = false>
 void allow_lds() {
   static std::once_flag once[kMaxDevices];
   once_per_device(once, [] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel_ptr<T, KS, FP8, MODE, R>()),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel_ptr<T, KS, FP8, MODE, R, QDQ>()),
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kMaxLds));
   });
 }
@@ -773,15 +806,17 @@ Plan cached_plan(int64_t N, int M, int R, int NW) {
   return p;
 }
 
-template <typename T, int KS, bool FP8, int MODE>
-void launch_v(const MatmulArgs& a, const Plan& p, int R, size_t lds, FastDiv wpb, FastDiv cpr, int tiles) {
+template <typename T, int KS, bool FP8, int MODE, bool QDQ>
+void launch_v(const MatmulArgs& a, const Plan& p, int R, size_t lds, FastDiv wpb, FastDiv cpr, int tiles,
+              T* a_work) {
   hipStream_t s = static_cast<hipStream_t>(a.stream);
 #define FP4W_GEMV_LAUNCH(R_)                                                                            \
-  allow_lds<T, KS, FP8, MODE, R_>();                                                                    \
-  hipLaunchKernelGGL((kernel_ptr<T, KS, FP8, MODE, R_>()), dim3(p.grid), dim3(64 * kWaves), lds, s,     \
-                     static_cast<const T*>(a.A), a.B, a.scales, a.ws2, static_cast<const T*>(a.bias),   \
+  allow_lds<T, KS, FP8, MODE, R_, QDQ>();                                                               \
+  hipLaunchKernelGGL((kernel_ptr<T, KS, FP8, MODE, R_, QDQ>()), dim3(p.grid), dim3(64 * kWaves), lds,   \
+                     s, static_cast<const T*>(a.A), a.B, a.scales, a.ws2, static_cast<const T*>(a.bias), \
                      static_cast<T*>(a.Y), static_cast<int>(a.M), static_cast<int>(a.N),                \
-                     static_cast<int>(a.K), static_cast<int>(a.scale_cols), wpb, cpr, tiles, p.nus)
+                     static_cast<int>(a.K), static_cast<int>(a.scale_cols), wpb, cpr, tiles, p.nus,     \
+                     a_work)
   if (R == 1) {
     FP4W_GEMV_LAUNCH(1);
   } else if (R == 2) {
@@ -792,18 +827,22 @@ void launch_v(const MatmulArgs& a, const Plan& p, int R, size_t lds, FastDiv wpb
 #undef FP4W_GEMV_LAUNCH
 }
 
-template <typename T, bool FP8, int MODE>
-void launch_mode(const MatmulArgs& a, const Plan& p, int R, size_t lds, FastDiv wpb, FastDiv cpr, int tiles) {
+template <typename T, bool FP8, int MODE, bool QDQ>
+void launch_mode(const MatmulArgs& a, const Plan& p, int R, size_t lds, FastDiv wpb, FastDiv cpr, int tiles,
+                 T* a_work) {
   switch (p.KS) {
-    case 1: launch_v<T, 1, FP8, MODE>(a, p, R, lds, wpb, cpr, tiles); break;
-    case 2: launch_v<T, 2, FP8, MODE>(a, p, R, lds, wpb, cpr, tiles); break;
-    case 4: launch_v<T, 4, FP8, MODE>(a, p, R, lds, wpb, cpr, tiles); break;
-    default: launch_v<T, 8, FP8, MODE>(a, p, R, lds, wpb, cpr, tiles); break;
+    case 1: launch_v<T, 1, FP8, MODE, QDQ>(a, p, R, lds, wpb, cpr, tiles, a_work); break;
+    case 2: launch_v<T, 2, FP8, MODE, QDQ>(a, p, R, lds, wpb, cpr, tiles, a_work); break;
+    case 4: launch_v<T, 4, FP8, MODE, QDQ>(a, p, R, lds, wpb, cpr, tiles, a_work); break;
+    default: launch_v<T, 8, FP8, MODE, QDQ>(a, p, R, lds, wpb, cpr, tiles, a_work); break;
   }
 }
 
-template <typename T, bool FP8>
-int launch_t(const MatmulArgs& a) {
+// QDQ (W4A4, FP4 only): the activation copy in LDS is quantize-dequantized
+// in place and written to a_work; returns 1, launching nothing, when the
+// activations do not fit in LDS (the copy is not made).
+template <typename T, bool FP8, bool QDQ = false>
+int launch_t(const MatmulArgs& a, T* a_work = nullptr) {
   // buffer offsets are 32-bit: one 16-column tile and the activations must fit
   if (a.N > 0x7fffffff - 16 || a.K > (int64_t(1) << 26) || a.M * a.K * 2 >= (int64_t(1) << 31))
     return -1;
@@ -816,12 +855,19 @@ int launch_t(const MatmulArgs& a) {
   const size_t lds = lds_bytes(p.mode, FP8, M, NW);
   const FastDiv wpb = make_fastdiv(FP8 ? static_cast<uint32_t>(a.block_size / 64) : 1u);  // FP8: halves per block
   const FastDiv cpr = make_fastdiv(static_cast<uint32_t>(NW) * 16u + 1u);  // 16-byte chunks per LDS row
+  if constexpr (QDQ) {
+    // Every workgroup quantizes the whole of A again, so the fused form pays
+    // off only for small M x K: up to 3 blocks of 16 per thread it beat the
+    // separate QDQ launch (M = 4, K = 5120: 9.1 against 9.5 us), at 5 it lost
+    // (M = 8: 12.1 against 10.2 us).
+    if (p.mode == 0 || a.M * (a.K / 16) > 3 * 64 * kWaves) return 1;
+  }
   if (p.mode == 2)
-    launch_mode<T, FP8, 2>(a, p, R, lds, wpb, cpr, tiles);
+    launch_mode<T, FP8, 2, QDQ>(a, p, R, lds, wpb, cpr, tiles, a_work);
   else if (p.mode == 1)
-    launch_mode<T, FP8, 1>(a, p, R, lds, wpb, cpr, tiles);
-  else
-    launch_mode<T, FP8, 0>(a, p, R, lds, wpb, cpr, tiles);
+    launch_mode<T, FP8, 1, QDQ>(a, p, R, lds, wpb, cpr, tiles, a_work);
+  else if constexpr (!QDQ)
+    launch_mode<T, FP8, 0, false>(a, p, R, lds, wpb, cpr, tiles, a_work);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -829,6 +875,11 @@ int launch_t(const MatmulArgs& a) {
 
 int launch_fp4_gemv(const MatmulArgs& a) {
   return a.act == Act::BF16 ? launch_t<__bf16, false>(a) : launch_t<_Float16, false>(a);
+}
+
+int launch_fp4_gemv_w4a4(const MatmulArgs& a, void* a_work) {
+  return a.act == Act::BF16 ? launch_t<__bf16, false, true>(a, static_cast<__bf16*>(a_work))
+                            : launch_t<_Float16, false, true>(a, static_cast<_Float16*>(a_work));
 }
 
 int launch_fp8_gemv(const MatmulArgs& a) {

@@ -95,6 +95,11 @@ void once_per_device(std::once_flag (&flags)[kMaxDevices], F&& f) {
 // 1 <= M <= 8, block_size == 16, K % 32 == 0, scale_cols == K / 16,
 // A / B 16-byte aligned, scales 4-byte aligned, bias 2-byte aligned.
 int launch_fp4_gemv(const MatmulArgs& a);
+// The same GEMV with the W4A4 activation step fused: the LDS copy of A is
+// NVFP4 quantize-dequantized before use and also written to a_work (M x K,
+// 16-byte aligned, disjoint from A); K % 16 == 0.  Returns 1, launching
+// nothing, when A does not fit in LDS or M x K / 16 exceeds 1536 blocks.
+int launch_fp4_gemv_w4a4(const MatmulArgs& a, void* a_work);
 // M >= 1, block_size == 16, K % 64 == 0, scale_cols == K / 16,
 // A / B 16-byte aligned, scales 4-byte aligned.
 int launch_fp4_gemm(const MatmulArgs& a);

@@ -193,7 +193,10 @@ int fp4w_qdq_activation_ex(const void* A, int64_t M, int64_t K, void* out, int d
  * cannot apply E4M3 scales per 16 exactly, so this runs as A_work =
  * fp4w_qdq_activation(A) (exact in T), then fp4w_matmul(A_work, ...), whose
  * kernels fold the weight scales into exact BF16/FP16 MFMA operands.  Both
- * steps are enqueued on `stream`.  The pages' guards (block_size 16,
+ * steps are enqueued on `stream`.  For a decode GEMV (M <= 8) with
+ * M x K <= 24576, A and A_work distinct and A 16-byte aligned, the two are
+ * one launch: the GEMV quantize-dequantizes its own LDS copy of A (the same
+ * values, bit for bit) and writes it to A_work as well.  The pages' guards (block_size 16,
  * K % 32, N % 32, M > 8) choose this path inside their operator; called
  * directly it takes any arguments fp4w_matmul takes with K % 16 == 0.
  *

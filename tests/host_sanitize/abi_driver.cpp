@@ -13,6 +13,7 @@
 
 namespace fp4w {
 extern const char* g_last;
+extern int g_fused_rc;
 }
 
 static int failures = 0;
@@ -116,14 +117,20 @@ int main() {
   EXPECT(fp4w_qdq_activation(A, 4, 40, A, FP4W_F16, nullptr) == FP4W_ERR_SHAPE);
   EXPECT(fp4w_quantize_activation(A, big, big, C, C + 128, FP4W_BF16, nullptr) == FP4W_ERR_SHAPE);
   EXPECT(fp4w_matmul_w4a4(A, 4, 512, B, 300, S, 32, 16, ws2, nullptr, W, Y, FP4W_BF16, nullptr) == FP4W_OK);
+  EXPECT(strcmp(fp4w::g_last, "launch_fp4_gemv_w4a4") == 0);  // decode: the QDQ fused into the GEMV
+  fp4w::g_fused_rc = 1;  // A too large for the GEMV's LDS copy: separate QDQ, then the GEMV
+  EXPECT(fp4w_matmul_w4a4(A, 4, 512, B, 300, S, 32, 16, ws2, nullptr, W, Y, FP4W_BF16, nullptr) == FP4W_OK);
   EXPECT(strcmp(fp4w::g_last, "launch_fp4_gemv") == 0);
+  fp4w::g_fused_rc = 0;
+  EXPECT(fp4w_matmul_w4a4(A, 4, 512, B, 300, S, 32, 16, ws2, nullptr, A, Y, FP4W_BF16, nullptr) == FP4W_OK);
+  EXPECT(strcmp(fp4w::g_last, "launch_fp4_gemv") == 0);  // in place: separate QDQ, then the GEMV
   EXPECT(fp4w_matmul_w4a4(A, 4, 520, B, 300, S, 33, 16, ws2, nullptr, W, Y, FP4W_BF16, nullptr) ==
          FP4W_ERR_SHAPE);
   // the allocation-free variant: same dispatch, the library's scratch as the
   // workspace, sizes past the scratch rejected before anything is launched
   fp4w::g_last = "";
   EXPECT(fp4w_matmul_w4a4_noalloc(A, 4, 512, B, 300, S, 32, 16, ws2, nullptr, Y, FP4W_BF16, nullptr) == FP4W_OK);
-  EXPECT(strcmp(fp4w::g_last, "launch_fp4_gemv") == 0);
+  EXPECT(strcmp(fp4w::g_last, "launch_fp4_gemv_w4a4") == 0);
   fp4w::g_last = "";
   EXPECT(fp4w_matmul_w4a4_noalloc(A, 4096, 8192, B, 300, S, 512, 16, ws2, nullptr, Y, FP4W_BF16, nullptr) ==
          FP4W_ERR_SHAPE);  // 64 MiB of activation > FP4W_STATIC_SCRATCH_BYTES

@@ -30,6 +30,12 @@ STUB(launch_fp8_dequant_generic, Fp8DequantArgs)
 STUB(launch_qdq_vec, QdqArgs)
 STUB(launch_qdq_generic, QdqArgs)
 #undef STUB
+// what the fused W4A4 GEMV returns: 0 (launched) or 1 (A does not fit in LDS)
+int g_fused_rc = 0;
+int launch_fp4_gemv_w4a4(const MatmulArgs&, void*) {
+  if (g_fused_rc == 0) g_last = "launch_fp4_gemv_w4a4";
+  return g_fused_rc;
+}
 int launch_nvfp4_quantize(const Nvfp4Args&, bool vec) {
   g_last = vec ? "launch_nvfp4_quantize_vec" : "launch_nvfp4_quantize_generic";
   return 0;

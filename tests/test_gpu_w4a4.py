@@ -132,9 +132,19 @@ def test_qdq_in_place():
 
 
 W4A4_CASES = [
-    # M, N, K, dtype, bias: GEMV, skinny and GEMM paths of the matmul
+    # M, N, K, dtype, bias: GEMV, skinny and GEMM paths of the matmul; at
+    # M <= 8 and M * K <= 24576 the GEMV quantize-dequantizes its LDS copy of
+    # A itself (a last partial 128-k window at K = 480; M = 6, K = 4096 at
+    # that limit); M = 7, K = 5120 is past it, and at K = 17440 the
+    # activations do not fit in LDS: the separate QDQ runs first
     (1, 300, 256, "bf16", True),
     (4, 1000, 512, "fp16", False),
+    (2, 200, 480, "fp16", False),
+    (6, 300, 4096, "bf16", False),
+    (7, 260, 5120, "bf16", True),
+    (8, 1100, 1024, "fp16", True),
+    (4, 100, 17440, "bf16", False),
+    (8, 64, 17440, "fp16", True),
     (40, 777, 1024, "bf16", True),
     (300, 700, 640, "fp16", True),
     (513, 1024, 128, "bf16", False),
@@ -161,9 +171,10 @@ def test_w4a4_matmul_parity(M, N, K, dtype, bias):
     assert_bits_equal(dev_to_bits(work), dev_to_bits(q), "workspace holds the quantized activation")
 
 
-def test_w4a4_in_place_workspace():
+@pytest.mark.parametrize("M", [12, 3])  # skinny; GEMV (in place: the separate QDQ, then the GEMV)
+def test_w4a4_in_place_workspace(M):
     require_gpu()
-    p = workloads.make_fp4(12, 256, 512, 16, "bf16", seed=21, with_bias=True)
+    p = workloads.make_fp4(M, 256, 512, 16, "bf16", seed=21, with_bias=True)
     Y_ref, S = nvfp4.matmul_w4a4_reference(p.A, "bf16", p.B, p.weight_scale, 16, p.weight_scale_2, p.bias)
     d = fp4_device(p)
     Y = fw.fp4w_matmul_w4a4(d["A"], d["B"], d["ws"], d["ws2"], d["bias"], 16, workspace=d["A"])
