@@ -49,7 +49,8 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense BF16 / FP16 MFMA
 ROTATE_BYTES = 1 << 30          # rotate weight copies past the 256 MB MALL
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fp4_gemv_decode_traffic.json")
-GEMV_SOURCES = ["fp8_weight_only_fp4w_amd/csrc/gemv.hip", "fp8_weight_only_fp4w_amd/csrc/device.h"]
+GEMV_SOURCES = ["fp8_weight_only_fp4w_amd/csrc/gemv.hip", "fp8_weight_only_fp4w_amd/csrc/device.h",
+                "fp8_weight_only_fp4w_amd/csrc/nvfp4_block.h"]
 
 
 def log(*a):
