@@ -41,6 +41,11 @@ FP4_CASES = [
     # M = 5 .. 8 (row pairs) with streamed activations, one with a last window of 32 k
     (8, 300, 17440, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMV]),
     (6, 200, 12320, 16, "fp16", False, "ceil", [fw.PATH_FP4_GEMV]),
+    # streamed activations with several tile groups per workgroup (N = 5120:
+    # 320 tiles on 160 workgroups)
+    (4, 5120, 17408, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMV]),
+    (7, 4500, 9024, 16, "fp16", True, "ceil", [fw.PATH_FP4_GEMV]),
+    (3, 1000, 25600, 16, "bf16", False, "ceil", [fw.PATH_FP4_GEMV]),
     (8, 777, 1024, 16, "bf16", False, "ceil", [fw.PATH_FP4_GEMV, fw.PATH_FP4_GEMM]),
     (5, 65590, 128, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMV]),  # 2 tiles per wave, ragged N
     (9, 300, 128, 16, "bf16", True, "ceil", [fw.PATH_FP4_GEMM, fw.PATH_FP4_GENERIC]),
