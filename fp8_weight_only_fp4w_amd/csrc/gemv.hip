@@ -858,8 +858,8 @@ int launch_t(const MatmulArgs& a, T* a_work = nullptr) {
   if constexpr (QDQ) {
     // Every workgroup quantizes the whole of A again, so the fused form pays
     // off only for small M x K: up to 3 blocks of 16 per thread it beat the
-    // separate QDQ launch (M = 4, K = 5120: 9.1 against 9.5 us), at 5 it lost
-    // (M = 8: 12.1 against 10.2 us).
+    // separate QDQ launch (M = 4, K = 5120: 8.7 against 9.4 us), at 5 it lost
+    // (M = 8: about 11 against 10.1 us).
     if (p.mode == 0 || a.M * (a.K / 16) > 3 * 64 * kWaves) return 1;
   }
   if (p.mode == 2)

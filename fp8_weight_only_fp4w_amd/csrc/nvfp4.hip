@@ -7,7 +7,8 @@
 //
 // gfx950 mapping: one thread per block (32 bytes of T in, 9 bytes or 32 bytes
 // out, contiguous across the wave), a flat grid-stride loop; v_cvt_pk_fp8_f32
-// encodes the scale (round to nearest even), v_cvt_f32_fp8 decodes it.  The
+// encodes the scale (round to nearest even), v_cvt_f32_fp8 decodes it,
+// v_cvt_scalef32_pk_fp4_f32 / _pk_f32_fp4 encode and decode the codes.  The
 // decode GEMV's W4A4 form runs the same block QDQ on its LDS copy of A.
 //
 // [FP4 doc] = "MatMulBlockQuantizedFp4Weight - CUDA Operator Documentation"

@@ -10,15 +10,12 @@
 // saturating at 6 and keeping the sign.  Both quotients are IEEE FP32
 // divisions (the second one is decided without dividing, below).
 //
-// The element code needs no division.  The E2M1 rounding boundaries of a / s
-// are the midpoints t in {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5}; t * s is
-// exact in FP32 (at most 3 + 4 significand bits), so |a| against t * s
-// decides the exact quotient's side of each boundary, ties included.  The
-// rounded quotient RNE_f32(a / s) falls on the same side: a (at most 11
-// significand bits for FP16, 8 for BF16; t * s is at least 2^-11) either
-// equals t * s or differs from it by at least 2^-13 of its size, far more
-// than half an FP32 ulp, so rounding the quotient never moves it onto or
-// across a boundary.
+// The element code needs no division: the E2M1 rounding boundaries of a / s
+// are the midpoints t in {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5}, and the
+// rounded quotient RNE_f32(a / s) falls on the same side of each as the
+// exact one: a (at most 11 significand bits for FP16, 8 for BF16; t * s,
+// exact in FP32, is at least 2^-11) either equals t * s or differs from it
+// by at least 2^-13 of its size, far more than half an FP32 ulp.
 //
 // [FP4 doc] = "MatMulBlockQuantizedFp4Weight - CUDA Operator Documentation"
 #pragma once
@@ -27,85 +24,74 @@
 
 namespace fp4w {
 
-// E2M1 code of a / s from the boundaries t * s (thr, see above): the
-// magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 and their midpoints, each tie going
-// to the neighbour with the even code; saturating at 6; the sign of a kept
-__device__ __forceinline__ uint32_t nvfp4_e2m1_code(float a, const float (&thr)[7]) {
-  const float m = fabsf(a);
-  const uint32_t c = (m > thr[0]) + (m >= thr[1]) + (m > thr[2]) + (m >= thr[3]) + (m > thr[4]) +
-                     (m >= thr[5]) + (m > thr[6]);
-  return c | ((__float_as_uint(a) >> 28) & 8u);
+// The block's scale: its byte and FP32 value, NaN for a block with a NaN
+// (the largest magnitude, taken on the bits, is then above +inf's).
+__device__ __forceinline__ void nvfp4_block_scale(const float (&v)[16], uint32_t& sbyte, float& s) {
+  uint32_t mx = 0u;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) mx = max(mx, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+  if (mx > 0x7F800000u) {
+    sbyte = 0x7Fu;
+    s = __builtin_nanf("");
+  } else {
+    float r = __uint_as_float(mx) / 6.0f;
+    r = r > 448.0f ? 448.0f : r;  // E4M3 "fn" has no infinity: saturate
+    sbyte = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(r, 0.0f, 0, false)) & 0xFFu;
+    s = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(sbyte), 0);
+  }
+}
+
+// The block's 16 codes (element i in bits 4 (i % 8) of word i / 8), without
+// a division.  q' = a * rcp(s) is within 2^-22 of a / s (relative); rounded
+// to 20 significant bits (magnitude, half away from zero) it equals every
+// tie exactly (a boundary t of the E2M1 grid has at most 3 significant bits)
+// and stays on the same side of every boundary as a / s otherwise (those
+// quotients lie at least 2^-13 from every t, see above; the two roundings
+// move them by at most 2^-20).  v_cvt_scalef32_pk_fp4_f32 with scale 1 then
+// rounds it to the E2M1 grid: nearest, ties to the even code, saturating at
+// 6, the sign kept (also on a zero); the GPU tests check this on every FP16
+// and BF16 pattern.  A zero or NaN scale leaves every code 0.
+__device__ __forceinline__ void nvfp4_block_codes(const float (&v)[16], float s, uint32_t (&w)[2]) {
+  const bool live = s > 0.0f;
+  const float inv = __builtin_amdgcn_rcpf(s);
+  float q[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) q[i] = __uint_as_float((__float_as_uint(v[i] * inv) + 8u) & ~15u);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t x = 0u;
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, q[8 * h + 0], q[8 * h + 1], 1.0f, 0);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, q[8 * h + 2], q[8 * h + 3], 1.0f, 1);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, q[8 * h + 4], q[8 * h + 5], 1.0f, 2);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, q[8 * h + 6], q[8 * h + 7], 1.0f, 3);
+    w[h] = live ? x : 0u;
+  }
 }
 
 // one block: its 16 values -> scale byte, decoded scale and two words of
 // codes (element i in bits 4 (i % 8) of word i / 8)
 __device__ __forceinline__ void nvfp4_quant_block(const float (&v)[16], uint32_t& sbyte, float& s,
                                                   uint32_t (&w)[2]) {
-  float amax = 0.0f;
-  bool nan = false;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    nan |= v[i] != v[i];
-    amax = fmaxf(amax, fabsf(v[i]));
-  }
-  if (nan) {
-    sbyte = 0x7Fu;
-    s = __builtin_nanf("");
-  } else {
-    float r = amax / 6.0f;
-    r = r > 448.0f ? 448.0f : r;  // E4M3 "fn" has no infinity: saturate
-    sbyte = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(r, 0.0f, 0, false)) & 0xFFu;
-    s = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(sbyte), 0);
-  }
-  w[0] = 0u;
-  w[1] = 0u;
-  if (s > 0.0f) {  // a zero or NaN scale leaves every code 0
-    const float thr[7] = {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.0f * s};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) w[i >> 3] |= nvfp4_e2m1_code(v[i], thr) << (4 * (i & 7));
-  }
+  nvfp4_block_scale(v, sbyte, s);
+  nvfp4_block_codes(v, s, w);
 }
 
-// One block quantized and dequantized, without forming the codes.  The
-// value is sign(a) * e2m1(q) * s, q = |a| / s, and e2m1(q) is reached in
-// float arithmetic:
-//   * q' = |a| * rcp(s) is within 2^-22 of q (relative).  Rounding q' to 20
-//     significant bits gives every tie (q equal to a boundary t, at most 3
-//     significant bits) exactly, and moves no other quotient onto or across
-//     a boundary: those are at least 2^-13 (relative) away from every t (see
-//     above), far beyond the 2^-20 the two steps can move them.
-//   * adding and subtracting c = 2^(22 + floor(log2 clamp(q, 1, 8))) rounds q
-//     to the E2M1 step of its binade (0.5 below 2, then 1, then 2), ties to
-//     even, which is the E2M1 rounding: each tie goes to the even code;
-//     anything from 7 up reaches 8 or more, which saturates to 6.
-// e2m1 x e4m3 is exact in FP32 and in T (at most 6 significand bits,
-// magnitudes within [2^-10, 2688]).  A block with a zero scale (or NaN)
-// gives +0 (NaN) everywhere, as its codes are all 0.
+// one block quantized and dequantized: e2m1 x e4m3 is exact in FP32 and in
+// T (at most 6 significand bits, magnitudes within [2^-10, 2688]); a block
+// with a zero (NaN) scale gives +0 (NaN) everywhere
 template <typename T>
 __device__ __forceinline__ void nvfp4_qdq_block(const float (&v)[16], typename ActTraits<T>::vec8 (&r)[2]) {
-  uint32_t mx = 0u;  // largest magnitude, as bits: above +inf's means a NaN
-#pragma unroll
-  for (int i = 0; i < 16; ++i) mx = max(mx, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+  uint32_t sbyte, w[2];
   float s;
-  if (mx > 0x7F800000u) {
-    s = __builtin_nanf("");
-  } else {
-    float q = __uint_as_float(mx) / 6.0f;
-    q = q > 448.0f ? 448.0f : q;
-    s = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(__builtin_amdgcn_cvt_pk_fp8_f32(q, 0.0f, 0, false) & 0xFF), 0);
-  }
-  const bool live = s > 0.0f;
-  const float inv = live ? __builtin_amdgcn_rcpf(s) : 0.0f;
-  const uint32_t sign_mask = live ? 0x80000000u : 0u;
+  nvfp4_quant_block(v, sbyte, s, w);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float q = fabsf(v[i]) * inv;
-    q = __uint_as_float((__float_as_uint(q) + 8u) & ~15u);
-    const float c = __uint_as_float((__float_as_uint(__builtin_amdgcn_fmed3f(q, 1.0f, 8.0f)) & 0x7F800000u) +
-                                    (22u << 23));
-    const float e = fminf(f32_barrier(f32_barrier(q + c) - c), 6.0f);
-    const float o = __uint_as_float(__float_as_uint(e * s) | (__float_as_uint(v[i]) & sign_mask));
-    r[i >> 3][i & 7] = round_to<T>(o);
+  for (int h = 0; h < 2; ++h) {
+    const f32x2 p0 = e2m1x2_to_f32<0>(w[h]), p1 = e2m1x2_to_f32<1>(w[h]);
+    const f32x2 p2 = e2m1x2_to_f32<2>(w[h]), p3 = e2m1x2_to_f32<3>(w[h]);
+    r[h][0] = round_to<T>(p0.x * s); r[h][1] = round_to<T>(p0.y * s);
+    r[h][2] = round_to<T>(p1.x * s); r[h][3] = round_to<T>(p1.y * s);
+    r[h][4] = round_to<T>(p2.x * s); r[h][5] = round_to<T>(p2.y * s);
+    r[h][6] = round_to<T>(p3.x * s); r[h][7] = round_to<T>(p3.y * s);
   }
 }
 
